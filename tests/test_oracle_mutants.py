@@ -1,0 +1,77 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each mutant below is a copy of the oracle's three-loop algorithm with one
+planted mistake (on the CPU, in Python).  The same pin checks used on the real
+oracle - the printed worked example, exact brute force on tiny shapes and the
+identity closed form - must reject every mutant and accept the unmutated
+copy.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import exact
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_values.json")))
+
+
+def three_loop(A, B, mutant=None):
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    M, K = A.shape
+    N = B.shape[1]
+    C = np.zeros((M, N))
+    for i in range(M):
+        for k in range(K):
+            if mutant == "drop_last_k" and k == K - 1:
+                continue
+            if mutant == "reset_each_k_step" and k % 2 == 0:
+                C[i, :] = 0.0                       # accumulator cleared per BK=2 step
+            a = A[(i + 1) % M if mutant == "wrong_row" else i, k]
+            for j in range(N):
+                if mutant == "transposed_b":
+                    b = B[j % K, k % N]
+                elif mutant == "wrong_k_in_b":
+                    b = B[(k + 1) % K, j]
+                else:
+                    b = B[k, j]
+                term = a * b
+                if mutant == "wrong_sign" and k == 1:
+                    term = -term
+                C[i, j] += term
+    if mutant == "swapped_output":
+        C = C[::-1, :].copy()
+    return C
+
+
+def pins_pass(fn) -> bool:
+    g = GOLD["worked_example"]
+    try:
+        if fn(g["A"], g["B"]).tolist() != g["C"]:
+            return False
+        rng = np.random.default_rng(0)
+        for M, N, K in [(2, 3, 4), (3, 2, 5), (4, 4, 3), (1, 5, 2)]:
+            A = rng.integers(-4, 5, (M, K))
+            B = rng.integers(-4, 5, (K, N))
+            want = np.array(exact.exact_gemm(A.tolist(), B.tolist()), dtype=np.float64)
+            if not np.array_equal(fn(A, B), want):
+                return False
+        B = rng.integers(-4, 5, (5, 5))
+        if not np.array_equal(fn(np.eye(5), B), B.astype(np.float64)):
+            return False
+    except IndexError:
+        return False
+    return True
+
+
+def test_unmutated_copy_passes():
+    assert pins_pass(lambda A, B: three_loop(A, B))
+
+
+@pytest.mark.parametrize("mutant", ["drop_last_k", "reset_each_k_step", "wrong_row",
+                                    "transposed_b", "wrong_k_in_b", "wrong_sign",
+                                    "swapped_output"])
+def test_mutant_is_caught(mutant):
+    assert not pins_pass(lambda A, B: three_loop(A, B, mutant))
