@@ -1,0 +1,185 @@
+"""Throughput of C = A·B on one MI355X through the library's C ABI.
+
+One step = one gemm_run of the whole workload (default: the square fp16
+4096^3 product, A and B ~ N(0,1)/sqrt(K), fp32 accumulation, fp16 output),
+with inputs already resident in HBM.  W untimed warm-up steps, then exactly K
+timed steps bracketed by a device synchronisation on both sides; the kernel
+time is taken with HIP events recorded on the stream the kernels run on.
+
+Prints one JSON line (stdout):
+  metric/value/unit   GEMM TFLOP/s = 2MNK / time per step
+  roofline            achieved FLOP rate of the GEMM kernel against the MI355X
+                      dense fp16/bf16 MFMA peak (2516.6 TFLOP/s); ``traffic``
+                      is the HBM bytes per launch from the committed rocprofv3
+                      counter summary when it was taken on the current kernel
+                      source, else null
+  cpu_baseline        the CPU oracle (fp64 three loops) timed on a bounded
+                      block of rows of the same product on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ fp16/bf16 on 1 GPU; % of MFMA dense peak"
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}   # MI355X dense, published
+HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "f16_4096x4096x4096"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_run_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_cfg: str, workload: str):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE/WRITE_SIZE runs,
+    or None when missing or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_cfg}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
+    """Time the oracle on a block of leading rows of the same product."""
+    import numpy as np
+    import torch
+    from oracle import gemm64
+    M, K = A.shape
+    N = B.shape[1]
+    threads = gemm64.default_threads()
+    A64 = np.ascontiguousarray(A.to(torch.float64).numpy())
+    B64 = np.ascontiguousarray(B.to(torch.float64).numpy())
+    probe_rows = max(1, min(M, threads))
+    t_probe, _ = gemm64.time_rows_f64(A64, B64, 0, probe_rows, threads)
+    rows = int(min(M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
+    rows = max(threads, rows - rows % threads) if rows >= threads else rows
+    t, _ = gemm64.time_rows_f64(A64, B64, 0, rows, threads)
+    flops = 2.0 * rows * N * K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product ({rows / M:.4f} of the "
+                      f"work), fp64 three-loop oracle, {t:.2f} s on {threads} threads"}
+
+
+def main(argv=None) -> int:
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="also run one device copy of this many MiB (for scaling HBM counters)")
+    args = p.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the product shards by output rows or columns with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import dense_gemm_run_amd as dg
+    from dense_gemm_run_amd.inputs import WORKLOADS, workload_operands
+
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name} M={w.M} N={w.N} K={w.K} {w.dtype}")
+    A, B = workload_operands(w.name)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    a = A.to(dev)
+    b = B.to(dev)
+    c = torch.empty((w.M, w.N), dtype=a.dtype, device=dev)
+    code = dg.dtype_code(a.dtype)
+    h = dg.gemm_create()
+    cid = args.config if args.config is not None else dg.gemm_select_config(
+        a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code)
+    cfg = dg.gemm_config_info(cid)
+    log(f"[bench] kernel configuration {cid} {cfg['name']}")
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        dg.gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
+                           cid, stream.cuda_stream)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warm-up steps done")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms * 1e3:.1f} us/step (events), wall {wall:.3f} s")
+
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = traffic_from_profiles(cfg["name"], w.name)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "distribution": w.dist, "seed": w.seed,
+                   "kernel_config": cfg["name"], "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu",
+                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    dg.gemm_destroy(h)
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a block of rows")
+        out["cpu_baseline"] = cpu_baseline(A, B)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

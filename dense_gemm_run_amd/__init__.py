@@ -1,1 +1,89 @@
-"""MI355X (gfx950) dense matrix product C = A·B behind a small C ABI."""
+"""MI355X (gfx950) dense matrix product C = A·B behind a small C ABI.
+
+``gemm(a, b)`` takes two row-major CUDA/ROCm tensors of one dtype (fp32, fp16
+or bf16) and returns C = a @ b of that dtype, computed by the library's HIP
+kernels on the current stream (fp32 accumulation, round-to-nearest-even
+output).  The C-ABI functions are re-exported under their C names.
+PyTorch supplies device memory and the stream; nothing else.
+"""
+from __future__ import annotations
+
+from ._lib import (GEMM_BF16, GEMM_F16, GEMM_F32, GemmError, gemm_check_args,
+                   gemm_config_count, gemm_config_info, gemm_create, gemm_destroy,
+                   gemm_run, gemm_run_config, gemm_select_config, gemm_tile_of_block,
+                   status_string)
+
+__all__ = ["gemm", "Gemm", "gemm_create", "gemm_run", "gemm_run_config", "gemm_destroy",
+           "gemm_check_args", "gemm_config_count", "gemm_config_info",
+           "gemm_select_config", "gemm_tile_of_block", "status_string", "GemmError",
+           "GEMM_F32", "GEMM_F16", "GEMM_BF16", "dtype_code"]
+
+
+def dtype_code(dt) -> int:
+    import torch
+    codes = {torch.float32: GEMM_F32, torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16}
+    if dt not in codes:
+        raise TypeError(f"dtype must be float32, float16 or bfloat16, got {dt}")
+    return codes[dt]
+
+
+class Gemm:
+    """A handle bound to one device, plus the tensor-level call."""
+
+    def __init__(self, device=None):
+        import torch
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None
+                                   else torch.device(device).index or 0)
+        with torch.cuda.device(self.device):
+            self.handle = gemm_create()
+
+    def close(self):
+        if getattr(self, "handle", None):
+            gemm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __call__(self, a, b, out=None, config: int | None = None):
+        import torch
+        if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+            raise ValueError("gemm expects [M, K] @ [K, N]")
+        if a.dtype != b.dtype:
+            raise TypeError(f"a and b must share a dtype ({a.dtype} vs {b.dtype})")
+        code = dtype_code(a.dtype)
+        if a.device != self.device or b.device != self.device:
+            raise ValueError(f"inputs must be on {self.device}")
+        if not (a.is_contiguous() and b.is_contiguous()):
+            raise ValueError("inputs must be contiguous row-major (no implicit copies)")
+        M, K = a.shape
+        N = b.shape[1]
+        if out is None:
+            out = torch.empty((M, N), device=self.device, dtype=a.dtype)
+        elif (out.shape != (M, N) or out.dtype != a.dtype or out.device != self.device
+              or not out.is_contiguous()):
+            raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        with torch.cuda.device(self.device):
+            if config is None:
+                gemm_run(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                         code, stream)
+            else:
+                gemm_run_config(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                M, N, K, code, config, stream)
+        return out
+
+
+_default: dict[int, Gemm] = {}
+
+
+def gemm(a, b, out=None, config: int | None = None):
+    """C = a @ b on a's device and the current stream (see module docstring)."""
+    idx = a.device.index if a.device.index is not None else 0
+    g = _default.get(idx)
+    if g is None:
+        g = _default[idx] = Gemm(idx)
+    return g(a, b, out=out, config=config)

@@ -1,0 +1,73 @@
+// Internal declarations shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dgr {
+
+// MI355X hands consecutive workgroup ids to its 8 XCDs in turn (id % 8 picks
+// the XCD); each XCD has its own L2.
+constexpr int kNumXcd = 8;
+
+__host__ __device__ inline int cdiv_i(int a, int b) { return (a + b - 1) / b; }
+
+// Output tile owned by workgroup `bid`.
+//
+// Step 1 (optional, xcd_remap): turn the hardware id into a logical id so
+// that the workgroups one XCD runs get consecutive logical ids.  Of the
+// first 8*q ids (q = total/8), XCD x runs ids x, x+8, x+16, ...; those become
+// logical ids x*q, x*q+1, ...  The last total%8 ids keep their value.
+//
+// Step 2: the grouped order of the pages (kernels-book chapter "Matrix
+// Multiplication", section "The naive version"; lesson "Matrix
+// multiplication", section "Connect to the real implementation"): logical
+// ids fill a band of group_m tile-rows going down the band first, then one
+// tile-column to the right, so the workgroups that run together share B
+// tiles (and A tiles) in L2.  The last band holds the remaining tile-rows.
+__host__ __device__ inline void tile_of_block(int bid, int tiles_m, int tiles_n, int group_m,
+                                              bool xcd_remap, int& tm, int& tn)
+{
+    int p = bid;
+    if (xcd_remap) {
+        const int total = tiles_m * tiles_n;
+        const int q = total / kNumXcd;
+        if (bid < q * kNumXcd) p = (bid % kNumXcd) * q + bid / kNumXcd;
+    }
+    const int band_size = group_m * tiles_n;
+    const int band = p / band_size;
+    const int within = p - band * band_size;
+    const int top = band * group_m;
+    const int rows_left = tiles_m - top;
+    const int height = rows_left < group_m ? rows_left : group_m;
+    tn = within / height;
+    tm = top + (within - tn * height);
+}
+
+enum Dtype : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct Config {
+    int32_t id;
+    int32_t bm, bn, bk;
+    int32_t group_m;
+    int32_t threads;
+    int32_t dtype_mask;
+    int32_t needs_vec_align;
+    int32_t xcd_remap;
+    const char* name;
+};
+
+struct LaunchArgs {
+    const void* A;
+    const void* B;
+    void* C;
+    int M, N, K;
+    int dtype;
+    hipStream_t stream;
+};
+
+// Kernel launchers; each returns the hipError_t of the launch.
+hipError_t launch_generic(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_mfma16(const Config& cfg, const LaunchArgs& a);
+
+}  // namespace dgr

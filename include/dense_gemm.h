@@ -1,0 +1,150 @@
+/*
+ * dense_gemm.h - dense matrix product C = A·B on an AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The operation (lesson "Matrix multiplication: reuse the inputs",
+ * triton-cuda-lab, section "The three dimensions have different jobs"):
+ * A has shape [M,K], B has shape [K,N], C has shape [M,N] and
+ *     C[row,col] = sum over inner of A[row,inner] * B[inner,col].
+ * A's column count must equal B's row count; that is why K is passed once.
+ *
+ * Layout: all three matrices are dense and row-major with no padding between
+ * rows: element (r,c) of A is at A + r*K + c, of B at B + r*N + c, of C at
+ * C + r*N + c (same lesson, "Connect to the real implementation").
+ *
+ * Types: A, B and C share one element type, fp32, fp16 or bf16 (the output
+ * has the input's type, as in chapter "Fast matrix multiplication", the
+ * Triton wrapper).  Products are summed in fp32 whatever the input type
+ * (notebook "Triton tiled matmul", section "What"), and the fp32 sum is
+ * rounded to the output type with round-to-nearest-even.  fp32 inputs are
+ * multiplied at full fp32 precision (no reduced-precision input mode).
+ *
+ * Edges: M, N and K need not be multiples of any tile size.  Out-of-range
+ * input elements read as zero (zero padding is neutral for the sum) and only
+ * rows < M and columns < N of C are written (chapter "Fast matrix
+ * multiplication", section "The CUDA kernel", the zero-padded edges).
+ * Alignment of A, B and C never affects results, only which kernel runs.
+ *
+ * Ownership: the caller allocates A, B and C in device memory of the device
+ * the handle was created on and keeps them alive until the stream has
+ * finished the call.  The library allocates no device memory and never
+ * synchronises: gemm_run only enqueues work on the given stream and returns.
+ *
+ * Errors: every argument check happens on the host before anything is
+ * enqueued; on an error status nothing has been launched and C is untouched.
+ * A fault inside a kernel would surface at the caller's next synchronisation,
+ * like any asynchronous HIP work.
+ */
+#ifndef DENSE_GEMM_H
+#define DENSE_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of A, B and C. */
+typedef enum gemm_dtype {
+    GEMM_F32 = 0,   /* IEEE binary32 */
+    GEMM_F16 = 1,   /* IEEE binary16 */
+    GEMM_BF16 = 2   /* bfloat16: fp32's exponent, 8-bit significand */
+} gemm_dtype_t;
+
+typedef enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1,      /* negative size, null pointer with data, null handle, wrong device, bad config id */
+    GEMM_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype is not one of gemm_dtype_t */
+    GEMM_ERR_UNSUPPORTED_DEVICE = 3, /* no GPU, or the current device is not gfx950 */
+    GEMM_ERR_TOO_LARGE = 4,          /* a dimension > 2^31-1 or a matrix of 2^31 bytes or more */
+    GEMM_ERR_ALIASING = 5,           /* C's bytes overlap A's or B's */
+    GEMM_ERR_HIP = 6,                /* a HIP runtime call failed */
+    GEMM_ERR_CONFIG_MISMATCH = 7     /* forced kernel configuration cannot run these arguments */
+} gemm_status_t;
+
+/* Opaque, immutable after creation; safe to share between host threads and
+ * to use for concurrent calls on different streams. */
+typedef struct gemm_ctx* gemm_handle_t;
+
+/* Bind a handle to the device that is current on the calling thread.
+ * *out receives the handle (NULL on error).  Fails with
+ * GEMM_ERR_UNSUPPORTED_DEVICE when there is no GPU or it is not gfx950, and
+ * with GEMM_ERR_INVALID_VALUE when out is NULL. */
+gemm_status_t gemm_create(gemm_handle_t* out);
+
+/* Enqueue C = A·B on `stream`.
+ *   A      device pointer to M*K elements, row-major [M,K]    (read only)
+ *   B      device pointer to K*N elements, row-major [K,N]    (read only)
+ *   C      device pointer to M*N elements, row-major [M,N]    (written)
+ *   M,N,K  sizes, each >= 0.  M == 0 or N == 0: nothing is written.
+ *          K == 0: C is filled with zeros (an empty sum).
+ *   dtype  a gemm_dtype_t value, the type of all three matrices.
+ *   stream a hipStream_t, or NULL for the null stream.
+ * A pointer may be NULL only when its matrix has no elements.  C may not
+ * overlap A or B.  The device current on the calling thread must be the
+ * handle's device.  Returns GEMM_OK once the work is enqueued. */
+gemm_status_t gemm_run(gemm_handle_t h, const void* A, const void* B, void* C,
+                       int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream);
+
+/* Release a handle.  NULL is accepted and ignored.  No work may still be
+ * using the handle (enqueued work does not refer to it). */
+gemm_status_t gemm_destroy(gemm_handle_t h);
+
+/* Static English text for a status code (never NULL). */
+const char* gemm_status_string(int32_t status);
+
+/* ---------------------------------------------------------------------------
+ * Introspection.  These touch no device and are safe without a GPU.
+ * ------------------------------------------------------------------------- */
+
+/* The status gemm_run would return for these arguments before launching
+ * (handle and device checks excluded).  Pointers are only compared, never
+ * dereferenced. */
+gemm_status_t gemm_check_args(const void* A, const void* B, const void* C,
+                              int64_t M, int64_t N, int64_t K, int32_t dtype);
+
+/* Kernel configurations.  A configuration fixes the output tile BM x BN, the
+ * K-step BK, the band height GROUP_M of the tile order, the workgroup size,
+ * and which element types and alignments it accepts. */
+typedef struct gemm_config_info {
+    int32_t id;
+    int32_t bm, bn, bk;        /* output tile and K-step */
+    int32_t group_m;           /* tile-rows walked before moving right */
+    int32_t threads;           /* workgroup size */
+    int32_t dtype_mask;        /* bit d set: accepts gemm_dtype_t d */
+    int32_t needs_vec_align;   /* 1: needs 16-byte aligned A, B, C and K, N multiples of 16 bytes / element size */
+    int32_t xcd_remap;         /* 1: workgroup ids are remapped so each XCD gets a compact block of tiles */
+    char name[40];
+} gemm_config_info_t;
+
+/* Number of configurations; ids run from 0 to count-1. */
+int32_t gemm_config_count(void);
+
+/* Describe configuration `id`.  GEMM_ERR_INVALID_VALUE for a bad id or NULL. */
+gemm_status_t gemm_config_info(int32_t id, gemm_config_info_t* out);
+
+/* The configuration gemm_run picks for these arguments (alignment is read
+ * from the pointer values), or -1 when gemm_check_args would fail. */
+int32_t gemm_select_config(const void* A, const void* B, const void* C,
+                           int64_t M, int64_t N, int64_t K, int32_t dtype);
+
+/* Output tile (tile_m, tile_n) computed by workgroup `block` of
+ * configuration `id` for an M x N output, evaluated on the host with the
+ * same function the kernels use.  Used to test the tile order. */
+gemm_status_t gemm_tile_of_block(int32_t id, int64_t M, int64_t N, int64_t block,
+                                 int64_t* tile_m, int64_t* tile_n);
+
+/* ---------------------------------------------------------------------------
+ * gemm_run with a forced configuration, for measuring the alternatives.
+ * GEMM_ERR_CONFIG_MISMATCH when that configuration does not accept the
+ * dtype or the alignment of these arguments; otherwise as gemm_run.
+ * ------------------------------------------------------------------------- */
+gemm_status_t gemm_run_config(gemm_handle_t h, const void* A, const void* B, void* C,
+                              int64_t M, int64_t N, int64_t K, int32_t dtype,
+                              int32_t config_id, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_H */

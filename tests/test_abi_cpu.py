@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/dense_gemm.h declares, and its argument checks, status
+codes, configuration table and tile order behave as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_run_amd as dg
+from dense_gemm_run_amd import _lib
+from oracle import exact
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dense_gemm.h")
+
+OK, INVALID, BADTYPE, NODEV, TOOBIG, ALIAS, HIPERR, MISMATCH = range(8)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(_lib.LIB_PATH):
+        from dense_gemm_run_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    for name, code in _lib.STATUS_CODE.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+    for s in range(8):
+        assert dg.status_string(s) and dg.status_string(s) != "unknown status"
+    assert dg.status_string(99) == "unknown status"
+
+
+A, B, C = 0x10000, 0x200000, 0x4000000   # fake, never dereferenced
+
+
+@pytest.mark.parametrize("args,want", [
+    ((A, B, C, 4, 5, 6, 1), OK),
+    ((A, B, C, -1, 5, 6, 1), INVALID),
+    ((A, B, C, 4, -5, 6, 1), INVALID),
+    ((A, B, C, 4, 5, -6, 1), INVALID),
+    ((A, B, C, 4, 5, 6, 3), BADTYPE),
+    ((A, B, C, 4, 5, 6, -1), BADTYPE),
+    ((0, B, C, 4, 5, 6, 1), INVALID),
+    ((A, 0, C, 4, 5, 6, 1), INVALID),
+    ((A, B, 0, 4, 5, 6, 1), INVALID),
+    ((0, 0, C, 4, 5, 0, 1), OK),          # K = 0: A and B hold nothing
+    ((0, B, 0, 0, 5, 6, 1), OK),          # M = 0
+    ((A, 0, 0, 4, 0, 6, 1), OK),          # N = 0
+    ((A, B, C, 2 ** 31, 1, 1, 1), TOOBIG),
+    ((A, B, C, 1 << 16, 1 << 14, 1, 1), TOOBIG),   # C = 2^30 fp16 elements = 2^31 bytes
+    ((A, B, C, (1 << 16) - 1, 1 << 14, 1, 1), OK),
+    ((A, B, C, 1 << 15, 1 << 14, 1, 0), TOOBIG),   # fp32: 2^29 elements = 2^31 bytes
+    ((A, B, A + 4, 4, 5, 6, 1), ALIAS),   # C starts inside A
+    ((A, B, B - 10, 4, 5, 6, 1), ALIAS),  # C ends inside B
+    ((A, B, A + 48, 4, 5, 6, 1), OK),     # A holds 24 fp16 = 48 bytes: adjacent, no overlap
+])
+def test_check_args(args, want):
+    assert dg.gemm_check_args(*args) == want
+
+
+def test_run_without_handle_is_rejected_before_any_launch():
+    assert _lib.lib().gemm_run(None, A, B, C, 4, 5, 6, 1, None) == INVALID
+    assert _lib.lib().gemm_run(None, A, B, C, 4, 5, 6, 7, None) == BADTYPE
+    assert _lib.lib().gemm_run_config(None, A, B, C, 4, 5, 6, 1, 999, None) == INVALID
+
+
+def test_create_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(dg.GemmError) as e:
+        dg.gemm_create()
+    assert e.value.status == NODEV
+    assert _lib.lib().gemm_create(None) == INVALID
+    assert _lib.lib().gemm_destroy(None) == OK
+
+
+def test_config_table():
+    n = dg.gemm_config_count()
+    assert n >= 1
+    names = set()
+    for i in range(n):
+        info = dg.gemm_config_info(i)
+        assert info["id"] == i
+        assert info["bm"] > 0 and info["bn"] > 0 and info["bk"] > 0 and info["group_m"] > 0
+        assert info["threads"] % 64 == 0
+        names.add(info["name"])
+    assert len(names) == n
+    assert dg.gemm_config_info(0)["dtype_mask"] == 0x7 and dg.gemm_config_info(0)["needs_vec_align"] == 0
+    with pytest.raises(dg.GemmError):
+        dg.gemm_config_info(n)
+
+
+def test_selection_rules():
+    # the generic configuration takes anything small, ragged or unaligned
+    assert dg.gemm_select_config(A, B, C, 64, 64, 64, 0) == 0
+    assert dg.gemm_select_config(A, B, C, 127, 255, 65, 1) == 0
+    assert dg.gemm_select_config(A + 2, B, C, 4096, 4096, 4096, 1) == 0   # misaligned A
+    assert dg.gemm_select_config(A, B, C, 4096, 4096, 4094, 1) in (0,)   # K not a multiple of 8
+    assert dg.gemm_select_config(A, B, C, -1, 4, 4, 1) == -1
+    for M, N, K, dt in [(4096, 4096, 4096, 1), (8192, 8192, 8192, 2), (8192, 12288, 4096, 2),
+                        (8192, 4096, 14336, 2), (1000, 1000, 1000, 1)]:
+        Cb = C + (1 << 32)
+        cid = dg.gemm_select_config(A, A + (M * K * 2 + 4096) // 16 * 16, Cb, M, N, K, dt)
+        assert 0 <= cid < dg.gemm_config_count()
+        info = dg.gemm_config_info(cid)
+        assert (info["dtype_mask"] >> dt) & 1
+
+
+@pytest.mark.parametrize("cid", range(8))
+def test_tile_order_is_a_bijection(cid):
+    if cid >= dg.gemm_config_count():
+        pytest.skip("no such configuration")
+    info = dg.gemm_config_info(cid)
+    for M, N in [(1, 1), (127, 255), (4096, 4096), (8192, 12288), (300, 5000), (8192, 4096)]:
+        tm_n = -(-M // info["bm"])
+        tn_n = -(-N // info["bn"])
+        total = tm_n * tn_n
+        if total > 2000:
+            continue
+        seen = [dg.gemm_tile_of_block(cid, M, N, b) for b in range(total)]
+        assert sorted(seen) == [(r, c) for r in range(tm_n) for c in range(tn_n)]
+        if not info["xcd_remap"]:
+            # without the XCD remap the order is exactly the pages' grouped order
+            assert seen == [exact.grouped_tile(b, tm_n, tn_n, info["group_m"]) for b in range(total)]
+        with pytest.raises(dg.GemmError):
+            dg.gemm_tile_of_block(cid, M, N, total)
+
+
+def test_xcd_remap_gives_each_xcd_a_compact_block():
+    remapped = [i for i in range(dg.gemm_config_count()) if dg.gemm_config_info(i)["xcd_remap"]]
+    if not remapped:
+        pytest.skip("no configuration remaps workgroups")
+    cid = remapped[0]
+    info = dg.gemm_config_info(cid)
+    M = N = 16 * info["bm"] if info["bm"] == info["bn"] else 4096
+    tm_n, tn_n = -(-M // info["bm"]), -(-N // info["bn"])
+    total = tm_n * tn_n
+    for x in range(8):
+        tiles = [dg.gemm_tile_of_block(cid, M, N, b) for b in range(x, total, 8)]
+        rows = {t[0] for t in tiles}
+        cols = {t[1] for t in tiles}
+        # a compact block touches far fewer rows+columns than a scattered one
+        assert len(rows) * len(cols) <= 2 * len(tiles), (x, len(rows), len(cols))
