@@ -34,6 +34,9 @@ struct Entry {
 // outside a row).
 const Entry kTable[] = {
     {{0, 64, 64, 32, 8, 256, 0x7, 0, 0, "generic_64x64"}, kGeneric},
+    {{1, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma16_256x256x64"}, kMfma16},
+    {{2, 256, 128, 64, 4, 256, 0x6, 1, 1, "mfma16_256x128x64"}, kMfma16},
+    {{3, 128, 128, 64, 4, 256, 0x6, 1, 1, "mfma16_128x128x64"}, kMfma16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -89,8 +92,15 @@ int select(const void* A, const void* B, const void* C, int64_t M, int64_t N, in
            int32_t dtype)
 {
     if (M == 0 || N == 0 || K == 0) return 0;
-    (void)A; (void)B; (void)C; (void)K; (void)dtype;
-    return 0;
+    if (dtype == kF32) return 0;
+    if (!accepts(kTable[1], A, B, C, N, K, dtype)) return 0;
+    if (M * N * K < (int64_t)128 * 128 * 128) return 0;
+    // largest tile that still leaves at least one tile per CU (256 CUs)
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    if (t256 >= 256) return 1;
+    const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+    if (t128 >= 256) return 2;
+    return 3;
 }
 
 gemm_status_t launch(const Entry& e, gemm_handle_t h, const void* A, const void* B, void* C,

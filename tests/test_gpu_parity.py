@@ -151,7 +151,8 @@ def test_k_zero_gives_zeros_and_empty_outputs_write_nothing():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("shape", [(127, 255, 65), (1, 1, 1), (65, 129, 8), (300, 260, 64)])
+@pytest.mark.parametrize("shape", [(127, 255, 65), (1, 1, 1), (65, 129, 8), (300, 260, 64),
+                                   (264, 392, 136), (520, 776, 264)])
 def test_masked_store_leaves_guards_untouched(dtype, shape):
     M, N, K = shape
     A, B = make_operands(M, N, K, dtype, "normal", 5)
@@ -192,18 +193,27 @@ def test_repeat_runs_are_bitwise_identical():
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
 
 
-def test_every_configuration_that_accepts_the_arguments():
-    A, B = make_operands(520, 776, 264, "f16", "normal", 4)
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("shape", [(520, 776, 264), (256, 256, 64), (8, 8, 8), (1, 8, 4096),
+                                   (777, 8, 72), (300, 1000, 8)])
+def test_every_configuration_that_accepts_the_arguments(dtype, shape):
+    M, N, K = shape
+    A, B = make_operands(M, N, K, dtype, "normal", 4 + M)
     a, b = A.cuda(), B.cuda()
-    ref = None
     for cid in range(dg.gemm_config_count()):
         info = dg.gemm_config_info(cid)
-        if not (info["dtype_mask"] >> 1) & 1:
+        if not (info["dtype_mask"] >> DT_CODE[dtype]) & 1:
             continue
-        note(f"[parity] config {cid} {info['name']}")
+        note(f"[parity] config {cid} {info['name']} {dtype} {shape}")
         c = dg.gemm(a, b, config=cid)
         torch.cuda.synchronize()
-        check_full(A, B, "f16", c)
+        check_full(A, B, dtype, c)
+        # the same configuration on integer inputs must be bit-exact
+        Ai, Bi = make_operands(M, N, K, dtype, "integers", 5 + M)
+        ci = dg.gemm(Ai.cuda(), Bi.cuda(), config=cid)
+        torch.cuda.synchronize()
+        ref, _ = gemm64.reference(Ai, Bi, dtype)
+        assert np.array_equal(ci.to("cpu", torch.float64).numpy(), ref)
 
 
 def test_api_errors_on_gpu():
