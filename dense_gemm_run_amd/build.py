@@ -49,6 +49,10 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
+    # a library with unresolved symbols (e.g. a kernel whose host stub was not
+    # emitted) must fail here, not at first use
+    import ctypes
+    ctypes.CDLL(tmp)
     os.replace(tmp, LIB)
     return LIB
 

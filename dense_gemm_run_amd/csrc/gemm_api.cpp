@@ -34,9 +34,9 @@ struct Entry {
 // outside a row).
 const Entry kTable[] = {
     {{0, 64, 64, 32, 8, 256, 0x7, 0, 0, "generic_64x64"}, kGeneric},
-    {{1, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma16_256x256x64"}, kMfma16},
-    {{2, 256, 128, 64, 4, 256, 0x6, 1, 1, "mfma16_256x128x64"}, kMfma16},
-    {{3, 128, 128, 64, 4, 256, 0x6, 1, 1, "mfma16_128x128x64"}, kMfma16},
+    {{1, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16_256x256x32"}, kMfma16},
+    {{2, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma16_256x128x32"}, kMfma16},
+    {{3, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16_128x128x32"}, kMfma16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

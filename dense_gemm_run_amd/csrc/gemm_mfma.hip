@@ -7,28 +7,34 @@
 //
 //  * Tile order: 1-D grid, XCD-aware remap + grouped band order
 //    (tile_of_block in gemm_internal.h).
-//  * Staging: the BM x 64 A tile and 64 x BN B tile of K-step i+1 are copied
-//    global -> LDS by buffer loads that write LDS directly (16 bytes per lane,
-//    no VGPR round trip) while K-step i is being multiplied; two LDS stages.
-//    Out-of-range 16-byte pieces (rows >= M, columns >= N, K positions >= K)
-//    are given an offset past the buffer's end, which the buffer unit
-//    returns as zeros: the zero padding of the pages' tensor descriptors
-//    (chapter "Matrix Multiplication", section "The real tiled loop").
-//  * LDS layout: A tile [BM][64] and B tile [64][BN], both with their 16-byte
-//    pieces XOR-swizzled by row so the MFMA operand reads spread over the
-//    banks (the pages pad rows for the same purpose; chapter "Fast matrix
-//    multiplication", section "Shared-memory bank conflicts").
+//  * Staging: K is walked in steps of 32.  Four LDS stages form a ring; the
+//    BM x 32 A tile and 32 x BN B tile of K-step it+3 are copied global -> LDS
+//    while K-step it is multiplied, by buffer loads that write LDS directly
+//    (16 bytes per lane, no VGPR round trip), spread over the step so the
+//    load path is never flooded.  Out-of-range 16-byte pieces (rows >= M,
+//    columns >= N, K positions >= K) get an offset past the buffer's end,
+//    which the buffer unit returns as zeros: the zero padding of the pages'
+//    tensor descriptors (chapter "Matrix Multiplication", section "The real
+//    tiled loop").
+//  * LDS layout: A tile [BM][32] and B tile [32][BN], both with their 16-byte
+//    pieces XOR-swizzled by row so the MFMA operand reads hit every bank
+//    once per cycle (the pages pad rows for the same purpose; chapter "Fast
+//    matrix multiplication", section "Shared-memory bank conflicts").
 //  * Math: 4 wavefronts in a 2x2 grid, each owning a (BM/2) x (BN/2) block
 //    of 32x32 MFMA tiles (v_mfma_f32_32x32x16_{f16,bf16}) whose fp32
 //    accumulators stay in registers for the whole K walk.  A operands are
 //    read with 16-byte LDS reads; B is stored N-contiguous (as it is in
 //    memory) and read with the gfx950 LDS transpose read, which hands each
-//    lane 4 consecutive K values of one column.
+//    lane 4 consecutive K values of one column.  Operands of the next
+//    16-wide K-slice are read while the current one multiplies; one barrier
+//    per K-step, placed inside the step's second slice, publishes the next
+//    stage and retires the oldest one.
 //  * The MFMA is issued with its operands swapped (B fragment first), which
-//    computes the transposed 32x32 block; each lane then holds 4 consecutive
-//    columns of one row and the epilogue writes 8-byte pieces, rounding the
-//    fp32 sums to the output type (round to nearest even) and skipping rows
-//    >= M and columns >= N.
+//    computes the transposed 32x32 block: each lane holds 4 consecutive
+//    columns of one row.  The epilogue rounds the fp32 sums to the output
+//    type (round to nearest even), stages the wavefront's block through LDS
+//    and writes C with 16-byte stores covering whole row segments, skipping
+//    rows >= M and columns >= N.
 #include "gemm_internal.h"
 
 namespace dgr {
@@ -39,10 +45,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
-constexpr int kBK = 64;            // K-step (elements)
-constexpr int kRowBytesA = kBK * 2; // one A tile row: 128 bytes = 8 pieces of 16 bytes
+constexpr int kBK = 32;              // K-step (elements)
+constexpr int kStages = 2;           // LDS stages (one being read, one being filled)
+constexpr int kLead = 4;             // K-steps of global loads in flight (register slots)
+constexpr int kRowBytesA = kBK * 2;  // one A tile row: 64 bytes = 4 pieces of 16 bytes
 constexpr int kThreads = 256;
 constexpr unsigned kOOB = 0x80000000u;   // byte offset past any buffer (< 2^31 bytes)
 
@@ -53,6 +63,13 @@ template <> struct Op<_Float16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
+    // two fp32 -> two fp16 (round to nearest even), packed
+    static __device__ inline unsigned pack2(float a, float b)
+    {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        h2 v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(unsigned, v);
+    }
 };
 template <> struct Op<__bf16> {
     typedef bf16x8 V8;
@@ -60,14 +77,33 @@ template <> struct Op<__bf16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ inline unsigned pack2(float a, float b)
+    {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        b2 v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(unsigned, v);
+    }
 };
 
-// 16-byte piece swizzles.  A rows hold 8 pieces; B rows hold BN/8 pieces and
-// the B swizzle moves whole 64-byte groups so an LDS transpose read (which
-// covers 64 contiguous bytes of 4 rows per half-wavefront) hits 4 different
-// bank groups.
-__device__ __forceinline__ int swz_a(int row) { return row & 7; }
+// 16-byte piece swizzles (LDS: 64 banks of 4 bytes, 256 bytes per cycle).
+// A rows are 64 bytes, so four rows share one 256-byte bank window; a
+// 16-byte read by 16 lanes covers 16 consecutive rows at one logical piece,
+// and XOR-ing the piece with (row/4)%4 puts each of those rows on its own 4
+// banks.  B rows hold BN/8 pieces; the B swizzle moves whole 64-byte groups
+// so a transpose read (64 contiguous bytes of 4 rows per 32 lanes) hits 4
+// different bank groups.
+__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
 template <int BN> __device__ __forceinline__ int swz_b(int k) { return ((k & 7) << 2) & (BN / 8 - 1); }
+
+// s_waitcnt immediate that waits until at most n vector-memory loads of this
+// wavefront are outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt and lgkmcnt left at their maximum, i.e. not waited for).
+constexpr unsigned waitcnt_vm(unsigned n)
+{
+    return (n & 15u) | (7u << 4) | (15u << 8) | ((n >> 4) << 14);
+}
+// ... and the one that waits for all of this wavefront's LDS operations.
+constexpr unsigned kWaitLgkm0 = 15u | (7u << 4) | (0u << 8) | (3u << 14);
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsigned bytes)
 {
@@ -86,10 +122,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma16_kernel(
     constexpr int ROW_B = BN * 2;             // bytes in one B tile row
     constexpr int B_BYTES = kBK * ROW_B;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 1 KB direct-to-LDS loads per wavefront
+    constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 16-byte-per-lane loads per wavefront
     constexpr int B_LOADS = B_BYTES / 1024 / 4;
+    constexpr int LOADS = A_LOADS + B_LOADS;      // per wavefront per K-step
+    constexpr int C_BYTES = WM * WN * 2;          // one wavefront's C block in LDS
+    constexpr int SMEM = kStages * STAGE > 4 * C_BYTES ? kStages * STAGE : 4 * C_BYTES;
     static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int tm, tn;
@@ -101,69 +140,124 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma16_kernel(
     const int wm = wave >> 1, wn = wave & 1;
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * 2u);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (unsigned)K * (unsigned)N * 2u);
 
     // ---- per-lane load geometry (fixed across K-steps)
-    // A: load j of this wavefront fills tile rows 8*(wave*A_LOADS + j) .. +8;
-    //    lane -> row +lane/8, physical piece lane%8, logical piece p ^ swz.
-    // Rows >= M get a base offset of kOOB, so every piece of theirs reads zero.
-    unsigned a_row_off[A_LOADS];
-    int a_kpiece[A_LOADS];
+    // A: load j of this wavefront fills tile rows 16*(wave*A_LOADS + j) .. +16;
+    //    lane -> row +lane/4, physical piece lane%4, logical piece p ^ swz.
+    //    voffset = (row*K + piece*8)*2 (kOOB for rows >= M); the K-step's
+    //    k0*2 goes in the scalar offset.  A piece whose K range starts at or
+    //    past K is switched to kOOB per K-step.
+    unsigned a_voff[A_LOADS];
+    int a_kp[A_LOADS];
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-        const int row = 8 * (wave * A_LOADS + j) + (lane >> 3);
-        const int piece = (lane & 7) ^ swz_a(row);
-        a_row_off[j] = (m0 + row) < M ? (unsigned)(m0 + row) * (unsigned)K * 2u : kOOB;
-        a_kpiece[j] = piece * 8;
+        const int row = 16 * (wave * A_LOADS + j) + (lane >> 2);
+        const int piece = (lane & 3) ^ swz_a(row);
+        a_voff[j] = (m0 + row) < M ? ((unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 8u) * 2u : kOOB;
+        a_kp[j] = piece * 8;
     }
-    // B: 1 KB covers 1024/ROW_B rows of the B tile.
+    // B: 1 KB covers 1024/ROW_B rows of the B tile.  voffset = (krow*N +
+    //    col)*2 (kOOB for columns >= N) relative to a buffer that starts at
+    //    row k0 and ends at row min(K, k0 + 32), so rows >= K read zero.
     constexpr int B_ROWS_PER_LOAD = 1024 / ROW_B;
-    // Columns >= N get a base offset of kOOB (k*N*2 < 2^31 keeps the sum in range).
-    int b_krow[B_LOADS];
-    unsigned b_col_off[B_LOADS];
+    unsigned b_voff[B_LOADS];
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) {
         const int byte = lane * 16;
         const int krow = B_ROWS_PER_LOAD * (wave * B_LOADS + j) + byte / ROW_B;
         const int piece = ((byte % ROW_B) / 16) ^ swz_b<BN>(krow);
         const int col = n0 + piece * 8;
-        b_krow[j] = krow;
-        b_col_off[j] = col < N ? (unsigned)col * 2u : kOOB;
+        b_voff[j] = col < N ? ((unsigned)krow * (unsigned)N + (unsigned)col) * 2u : kOOB;
     }
 
-    auto issue_loads = [&](int stage, int k0) {
-        lds_byte* base = (lds_byte*)smem + stage * STAGE;
+    // Global loads of the K-step starting at k0 into register slot `slot`
+    // (16 bytes per lane per load).  Loads past the end of K read zeros, so
+    // the last K-step may be ragged or entirely empty.
+    u32x4 stg[kLead][LOADS];
+    auto load_regs = [&](int slot, int k0_in) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);   // uniform: keep it scalar
+        const int krem = K - k0;
 #pragma unroll
         for (int j = 0; j < A_LOADS; ++j) {
-            const int k = k0 + a_kpiece[j];
-            const unsigned in_row = a_row_off[j] + (unsigned)k * 2u;
-            const unsigned off = k < K ? in_row : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (void __attribute__((address_space(3)))*)(base + (wave * A_LOADS + j) * 1024),
-                                                     16, off, 0, 0, 0);
+            const unsigned off = a_kp[j] < krem ? a_voff[j] : kOOB;
+            stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0 * 2, 0));
         }
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > kBK ? kBK : krem));
+        const __amdgpu_buffer_rsrc_t rbk =
+            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
 #pragma unroll
         for (int j = 0; j < B_LOADS; ++j) {
-            const int k = k0 + b_krow[j];
-            const unsigned in_col = (unsigned)k * (unsigned)N * 2u + b_col_off[j];
-            const unsigned off = k < K ? in_col : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (void __attribute__((address_space(3)))*)(base + A_BYTES + (wave * B_LOADS + j) * 1024),
-                                                     16, off, 0, 0, 0);
+            // (copied to a local: clang's host pass drops the kernel stub when a
+            // captured array element is passed straight to this builtin)
+            const unsigned off = b_voff[j];
+            stg[slot][A_LOADS + j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rbk, off, 0, 0));
         }
     };
-
-    // ---- per-lane LDS read geometry
-    // A fragment (tile bi, K-slice s): row wm*WM + 32*bi + lane%32, logical piece 2s + lane/32.
-    int a_rd[FM];
+    // Write register slot `slot` into LDS stage `stage`: load j of this
+    // wavefront covers 1 KB of the stage, lane l its bytes 16l..16l+15, so
+    // every 16-byte write of a wavefront is one contiguous, conflict-free KB.
+    auto store_stage = [&](int stage, int slot) {
+        lds_byte* base = (lds_byte*)smem + stage * STAGE + lane * 16;
 #pragma unroll
-    for (int bi = 0; bi < FM; ++bi) a_rd[bi] = (wm * WM + 32 * bi + (lane & 31)) * kRowBytesA;
-    const int a_sel = lane >> 5;
+        for (int j = 0; j < A_LOADS; ++j)
+            *(u32x4 __attribute__((address_space(3)))*)(base + (wave * A_LOADS + j) * 1024) = stg[slot][j];
+#pragma unroll
+        for (int j = 0; j < B_LOADS; ++j)
+            *(u32x4 __attribute__((address_space(3)))*)(base + A_BYTES + (wave * B_LOADS + j) * 1024) = stg[slot][A_LOADS + j];
+    };
+
+    // ---- per-lane LDS read addresses.  The stage, the K-slice and the tile
+    // index are compile-time constants in the instruction's 16-bit offset.
+    // A fragment (tile bi, K-slice s): row wm*WM + 32*bi + lane%32, logical
+    // piece 2s + lane/32; the row swizzle only depends on lane%32.
+    const int a_sw = ((lane & 31) >> 2) & 3;
+    constexpr int NSETS = (kStages + 1) / 2;
+    int a_addr[NSETS][2];
+#pragma unroll
+    for (int p = 0; p < NSETS; ++p)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+            a_addr[p][sl] = 2 * p * STAGE + (wm * WM + (lane & 31)) * kRowBytesA +
+                            (((2 * sl + (lane >> 5)) ^ a_sw) * 16);
     // B fragment via transpose reads: within each 16-lane group, lane 4r+q
     // points at row r, columns 4q..4q+3 of a 4 x 16 block; the read returns
     // to lane i the 4 rows of column i.  Lanes 0-31 cover K rows 0..7 of the
     // slice, lanes 32-63 rows 8..15; lanes 16-31 / 48-63 the upper 16 columns.
+    // The B swizzle depends on k%8, which does not change with the slice.
     const int g16 = lane & 15;
-    const int b_kr = 8 * (lane >> 5) + (g16 >> 2);          // + 16*s + 4*h
-    const int b_cn = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3); // + wn*WN + 32*bj
+    const int b_kr = 8 * (lane >> 5) + (g16 >> 2);
+    const int b_cn = 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+    int b_addr[NSETS][FN][2];
+#pragma unroll
+    for (int p = 0; p < NSETS; ++p)
+#pragma unroll
+        for (int bj = 0; bj < FN; ++bj)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int k = 4 * hh + b_kr;
+                const int n = wn * WN + 32 * bj + b_cn;
+                const int piece = (n >> 3) ^ swz_b<BN>(k);
+                b_addr[p][bj][hh] = 2 * p * STAGE + A_BYTES + k * ROW_B + piece * 16 + (n & 7) * 2;
+            }
+
+    const lds_byte* lds0 = (const lds_byte*)smem;
+    // Fragments of K-slice sl of stage st.
+    auto read_frags = [&](int st, int sl, V8* af, V8* bf) {
+        const int p = st >> 1, so = (st & 1) * STAGE;
+#pragma unroll
+        for (int bi = 0; bi < FM; ++bi)
+            af[bi] = *(const V8*)(lds0 + a_addr[p][sl] + so + bi * 32 * kRowBytesA);
+#pragma unroll
+        for (int bj = 0; bj < FN; ++bj) {
+            s16x4 h[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (s16x4 __attribute__((address_space(3)))*)(lds0 + b_addr[p][bj][hh] + so + 16 * sl * ROW_B));
+            const s16x8 v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            bf[bj] = __builtin_bit_cast(V8, v);
+        }
+    };
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -173,68 +267,120 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = cdiv_i(K, kBK);
-    if (nk > 0) issue_loads(0, 0);
+    // MFMAs [lo, hi) of one K-slice, tile index = bi*FN + bj.
+    auto mfmas = [&](const V8* af, const V8* bf, int lo, int hi) {
+#pragma unroll
+        for (int x = lo; x < hi; ++x)
+            acc[x / FN][x % FN] = Op<T>::mfma(bf[x % FN], af[x / FN], acc[x / FN][x % FN]);
+    };
 
-    for (int it = 0; it < nk; ++it) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                       // stage it%2 complete; stage (it+1)%2 free
-        if (it + 1 < nk) issue_loads((it + 1) & 1, (it + 1) * kBK);
-        const lds_byte* sa = (const lds_byte*)smem + (it & 1) * STAGE;
-        const lds_byte* sb = sa + A_BYTES;
+    constexpr int NT = FM * FN;                  // MFMAs per wavefront per K-slice
+    constexpr int NR = FM + 2 * FN;              // LDS reads per wavefront per K-slice
+    // K-steps, rounded up to the 4-step unroll (register slots cycle with
+    // period kLead = 4 and LDS stages with period 2): the extra steps, at
+    // most 3, multiply the zeros their loads brought in.
+    const int nk = (cdiv_i(K, kBK) + kLead - 1) / kLead * kLead;
+
+    // Software pipeline.  K-step j's data travels global -> register slot
+    // j%4 (loaded during K-step j-4) -> LDS stage j%2 (written during K-step
+    // j-1) -> operand registers.
+    //  slice 0 of K-step it: read slice-1 operands of stage it%2; write
+    //    K-step it+1 (loaded three steps ago) from slot (it+1)%4 into stage
+    //    (it+1)%2, which every wavefront finished reading before the barrier
+    //    of K-step it-1; load K-step it+4 into slot it%4 (its previous
+    //    content, K-step it, went to LDS one step ago); multiply slice 0.
+    //  slice 1: multiply half of slice 1; pass the barrier (everyone's
+    //    K-step it+1 now in LDS); read slice-0 operands of stage (it+1)%2;
+    //    multiply the other half.
+    V8 fa[2][FM], fb[2][FN];
 #pragma unroll
-        for (int s = 0; s < kBK / 16; ++s) {
-            V8 af[FM], bf[FN];
+    for (int q = 0; q < kLead; ++q) load_regs(q, q * kBK);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kLead - 1) * LOADS));   // K-step 0 loaded
+    store_stage(0, 0);
+    __syncthreads();
+    read_frags(0, 0, fa[0], fb[0]);
+
+    // q = it % 4 is always passed as a literal, so after inlining every
+    // register slot and LDS address is fixed at compile time.
+    auto kstep = [&](const int q, int it) {
+        const int ST = q & 1;
+        // slice 0
+        read_frags(ST, 1, fa[1], fb[1]);
+        store_stage(ST ^ 1, (q + 1) % kLead);
+        load_regs(q, (it + kLead) * kBK);
+        mfmas(fa[0], fb[0], 0, NT);
+        // one MFMA, then an LDS read, an LDS write or a global load, until
+        // they run out
 #pragma unroll
-            for (int bi = 0; bi < FM; ++bi) {
-                const int row = wm * WM + 32 * bi + (lane & 31);
-                const int piece = (2 * s + a_sel) ^ swz_a(row);
-                af[bi] = *(const V8*)(sa + a_rd[bi] + piece * 16);
-            }
-#pragma unroll
-            for (int bj = 0; bj < FN; ++bj) {
-                s16x4 h[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int k = 16 * s + 4 * hh + b_kr;
-                    const int n = wn * WN + 32 * bj + b_cn;
-                    const int piece = (n >> 3) ^ swz_b<BN>(k);
-                    const lds_byte* p = sb + k * ROW_B + piece * 16 + (n & 7) * 2;
-                    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
-                }
-                const s16x8 v = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                bf[bj] = __builtin_bit_cast(V8, v);
-            }
-#pragma unroll
-            for (int bi = 0; bi < FM; ++bi)
-#pragma unroll
-                for (int bj = 0; bj < FN; ++bj)
-                    acc[bi][bj] = Op<T>::mfma(bf[bj], af[bi], acc[bi][bj]);
+        for (int i = 0; i < NT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i % 2 == 0 && i / 2 < LOADS) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+            if (i % 2 == 1 && i / 2 < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // slice 1
+        mfmas(fa[1], fb[1], 0, NT / 2);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();                       // everyone's K-step it+1 in LDS
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(ST ^ 1, 0, fa[0], fb[0]);
+        mfmas(fa[1], fb[1], NT / 2, NT);
+#pragma unroll
+        for (int i = 0; i < NT / 2; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, (NR + NT / 2 - 1) / (NT / 2), 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int it = 0; it < nk; it += kLead) {
+#pragma unroll
+        for (int q = 0; q < kLead; ++q) kstep(q, it + q);
     }
 
-    // ---- epilogue: lane holds C[row][col .. col+3] for 4 groups per tile
+    // ---- epilogue
+    // All loads (including the zero-fills past K) have landed and every
+    // wavefront is done with the stages before they are reused for C.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+
+    // Each wavefront writes its WM x WN block of C (output type) into its own
+    // LDS region, row-major with 16-byte pieces swizzled: piece p of row r
+    // sits at p ^ (r % PR) and its two 8-byte halves are swapped when
+    // (r / PR) is odd, so the 8-byte writes of 32 lanes (32 rows, one
+    // piece-half each) land on distinct banks.
+    constexpr int PR = WN / 8;                    // 16-byte pieces per C row
+    lds_byte* cw = (lds_byte*)smem + wave * C_BYTES;
 #pragma unroll
     for (int bi = 0; bi < FM; ++bi) {
-        const int row = m0 + wm * WM + 32 * bi + (lane & 31);
-        if (row >= M) continue;
-        T* crow = C + (size_t)row * N;
+        const int r = 32 * bi + (lane & 31);
 #pragma unroll
         for (int bj = 0; bj < FN; ++bj) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * WN + 32 * bj + 8 * g + 4 * (lane >> 5);
-                if (col < N) {
-                    typedef T T4 __attribute__((ext_vector_type(4)));
-                    T4 v;
-                    v[0] = (T)acc[bi][bj][4 * g + 0];
-                    v[1] = (T)acc[bi][bj][4 * g + 1];
-                    v[2] = (T)acc[bi][bj][4 * g + 2];
-                    v[3] = (T)acc[bi][bj][4 * g + 3];
-                    *(T4*)(crow + col) = v;
-                }
+                const int p = (4 * bj + g) ^ (r & (PR - 1));
+                const int h = (lane >> 5) ^ ((r / PR) & 1);
+                u32x2 v;
+                v[0] = Op<T>::pack2(acc[bi][bj][4 * g + 0], acc[bi][bj][4 * g + 1]);
+                v[1] = Op<T>::pack2(acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]);
+                *(u32x2 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16 + h * 8) = v;
             }
         }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's LDS writes done
+    // Read back whole row segments: lane -> row it*(64/PR) + lane/PR, piece lane%PR.
+    const int row_base = m0 + wm * WM;
+    const int q = lane % PR;
+    const int col = n0 + wn * WN + q * 8;
+#pragma unroll 4
+    for (int it = 0; it < WM * PR / 64; ++it) {
+        const int r = it * (64 / PR) + lane / PR;
+        const int p = q ^ (r & (PR - 1));
+        u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
+        if ((r / PR) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
+        const int row = row_base + r;
+        if (row < M && col < N) *(u32x4*)(C + (size_t)row * N + col) = v;
     }
 }
 
