@@ -21,7 +21,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma16 = 1 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2 };
 
 struct Entry {
     Config cfg;
@@ -34,11 +34,13 @@ struct Entry {
 // outside a row).
 const Entry kTable[] = {
     {{0, 64, 64, 32, 8, 256, 0x7, 0, 0, "generic_64x64"}, kGeneric},
-    {{1, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16_256x256x32"}, kMfma16},
-    {{2, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma16_256x128x32"}, kMfma16},
-    {{3, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16_128x128x32"}, kMfma16},
-    {{4, 256, 256, 32, 4, 512, 0x6, 1, 1, "mfma16_256x256x32_w8"}, kMfma16},
-    {{5, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma16_256x256x64"}, kMfma16},
+    {{1, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma32x32_256x256x32"}, kMfma32x32},
+    {{2, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma32x32_256x128x32"}, kMfma32x32},
+    {{3, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma32x32_128x128x32"}, kMfma32x32},
+    {{4, 256, 256, 32, 4, 512, 0x6, 1, 1, "mfma32x32_256x256x32_w8"}, kMfma32x32},
+    {{5, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma32x32_256x256x64"}, kMfma32x32},
+    {{6, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x32"}, kMfma16x16},
+    {{7, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x128x32"}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -119,7 +121,8 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const void* A, const void*
     hipError_t err = hipSuccess;
     switch (e.kind) {
     case kGeneric: err = launch_generic(e.cfg, la); break;
-    case kMfma16: err = launch_mfma16(e.cfg, la); break;
+    case kMfma32x32: err = launch_mfma32x32(e.cfg, la); break;
+    case kMfma16x16: err = launch_mfma16x16(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -68,6 +68,7 @@ struct LaunchArgs {
 
 // Kernel launchers; each returns the hipError_t of the launch.
 hipError_t launch_generic(const Config& cfg, const LaunchArgs& a);
-hipError_t launch_mfma16(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_mfma32x32(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_mfma16x16(const Config& cfg, const LaunchArgs& a);
 
 }  // namespace dgr

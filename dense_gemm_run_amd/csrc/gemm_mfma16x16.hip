@@ -1,0 +1,412 @@
+// MFMA kernel built on v_mfma_f32_16x16x32_{f16,bf16}, for fp16/bf16
+// problems whose rows are 16-byte aligned (K and N multiples of 8 elements,
+// A, B, C 16-byte aligned).
+//
+// Same tiled loop as the 32x32 kernel (kernels-book chapter "Matrix
+// Multiplication", section "Tiles": one program per BM x BN output tile, an
+// fp32 accumulator per output element that lives across the whole K walk),
+// with these differences:
+//
+//  * Math: 4 wavefronts in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs
+//    as 16x16 MFMA tiles.  Per unit of work the 16x16x32 instruction moves
+//    half the accumulator data of the 32x32x16 one; under MI355X's power
+//    limit this runs at a higher clock for the same issue rate.
+//  * The MFMAs are written as inline assembly with the accumulator operand
+//    tied to the destination ("+a"): the compiler's own selection for this
+//    instruction rotates accumulators through copies every K-step.  Being
+//    volatile, the statements also fix the order of every MFMA against the
+//    LDS and global-memory instructions around them, so the interleave below
+//    is exactly the issue order.  The compiler does not see the MFMA
+//    latency through inline assembly; the kernel covers the two places where
+//    it matters: the first K-step writes the accumulators without reading
+//    them (source C = 0, no zero-fill before it) and the epilogue waits out
+//    the last MFMAs before it reads accumulators.
+//  * Staging: K is walked in steps of 32 (one MFMA K-slice).  A goes through
+//    registers (LEAD register slots; K-step it+LEAD is loaded during K-step
+//    it and written to LDS during K-step it+LEAD-1, into one of two A
+//    stages).  B goes global -> LDS directly (buffer loads with the LDS
+//    destination) into a ring of SB stages, K-step it+SB-1 during K-step
+//    it.  Out-of-range 16-byte pieces read zeros, as in the 32x32 kernel (the
+//    zero padding of chapter "Matrix Multiplication", section "The real
+//    tiled loop").
+//  * LDS layout: A [BM][32] with 16-byte pieces XOR-swizzled by (row/4)%4,
+//    so the 16 rows one 16-lane group reads land on 16 different 16-byte
+//    bank groups; B [32][BN] with 16-byte pieces XOR-swizzled by an even
+//    value taken from bits 0, 1 and 3 of the row, so the 8 rows that one
+//    half-wavefront's transpose read touches (k = r, r+8 for r in a group of
+//    4) cover all 64 banks (chapter "Fast matrix multiplication", section
+//    "Shared-memory bank conflicts", pads rows for the same purpose).
+//  * One barrier per K-step, a quarter of the way into its MFMAs: it
+//    publishes K-step it+1 (A written by every wavefront, B landed), after
+//    which the operands of K-step it+1 are read into the second register set
+//    while the rest of K-step it multiplies.
+//  * The MFMA takes the B fragment first, which computes the transposed
+//    16x16 block: lane l holds row l%16 of the tile, columns 4*(l/16)..+3.
+//    The epilogue rounds to the output type (round to nearest even), stages
+//    the wavefront's block through LDS and writes whole row segments with
+//    16-byte stores, skipping rows >= M and columns >= N.
+#include "gemm_internal.h"
+#include "gemm_device.h"
+
+namespace dgr {
+namespace {
+
+constexpr int kBK = 32;   // K-step = one MFMA K-slice
+
+template <typename T> struct Mfma16x16;
+template <> struct Mfma16x16<_Float16> {
+    // c += b-fragment x a-fragment (16x16x32)
+    static __device__ __forceinline__ void acc(f32x4& c, const u32x4& b, const u32x4& a)
+    {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+    }
+    // c = b-fragment x a-fragment (source C is the constant 0)
+    static __device__ __forceinline__ void first(f32x4& c, const u32x4& b, const u32x4& a)
+    {
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(b), "v"(a));
+    }
+};
+template <> struct Mfma16x16<__bf16> {
+    static __device__ __forceinline__ void acc(f32x4& c, const u32x4& b, const u32x4& a)
+    {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+    }
+    static __device__ __forceinline__ void first(f32x4& c, const u32x4& b, const u32x4& a)
+    {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(b), "v"(a));
+    }
+};
+
+// A row of the A tile is 64 bytes (4 pieces of 16 bytes); 4 rows share one
+// 256-byte bank window.
+__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
+// B rows are BN*2 bytes (a multiple of 256): every row starts at bank 0.
+template <int BN> __device__ __forceinline__ int swz_b(int k)
+{
+    return (2 * ((k & 3) | ((k >> 1) & 4))) & (BN / 8 - 1);
+}
+
+// Epilogue: one wavefront's WM x WN block of fp32 accumulators (tile (bi,
+// bj): lane l holds row 16*bi + l%16, columns 16*bj + 4*(l/16) .. +3) is
+// rounded to the output type and written to C at (row0, col0) through the
+// wavefront's own LDS region `cw` of CW_BYTES: RP rows at a time are staged
+// there and read back as whole row segments for 16-byte stores, skipping
+// rows >= M and columns >= N.
+template <typename T, int WM, int WN, int CW_BYTES>
+__device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 16], lds_byte* cw,
+                                              int lane, int row0, int col0, int M, int N, T* C)
+{
+    constexpr int FN = WN / 16;
+    constexpr int PR = WN / 8;           // 16-byte pieces per C row
+    constexpr int W = 128 / WN;          // C rows per 256-byte bank window
+    constexpr int RP = CW_BYTES / (WN * 2);   // rows per pass
+    static_assert(W >= 1 && PR <= 16, "wavefront block too wide");
+    static_assert(RP % 16 == 0 && WM % RP == 0, "passes must hold whole tile rows");
+    // piece p of row r sits at p ^ ((r / W) % PR): the 16 rows one
+    // half-wavefront writes (8 bytes per lane, two lanes per piece) and the
+    // rows one 16-lane group reads back each cover 16 different bank groups.
+    const int q = lane % PR;
+    const int col = col0 + q * 8;
+#pragma unroll
+    for (int pass = 0; pass < WM / RP; ++pass) {
+        if (pass) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // previous pass read back
+#pragma unroll
+        for (int bi = pass * RP / 16; bi < (pass + 1) * RP / 16; ++bi) {
+            const int r = 16 * bi + (lane & 15) - pass * RP;
+            const int sw = (r / W) & (PR - 1);
+#pragma unroll
+            for (int bj = 0; bj < FN; ++bj) {
+                const int p = (2 * bj + (lane >> 5)) ^ sw;
+                const int h = (lane >> 4) & 1;
+                u32x2 v;
+                v[0] = pack2<T>(acc[bi][bj][0], acc[bi][bj][1]);
+                v[1] = pack2<T>(acc[bi][bj][2], acc[bi][bj][3]);
+                *(u32x2 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16 + h * 8) = v;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's LDS writes done
+#pragma unroll 4
+        for (int it = 0; it < RP * PR / 64; ++it) {
+            const int r = it * (64 / PR) + lane / PR;
+            const int p = q ^ ((r / W) & (PR - 1));
+            const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
+            const int row = row0 + pass * RP + r;
+            if (row < M && col < N) *(u32x4*)(C + (size_t)row * N + col) = v;
+        }
+    }
+}
+
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
+    const T* A, const T* B, T* C,
+    int M, int N, int K, int group_m)
+{
+    constexpr int NW = 4;                        // wavefronts, 2 x 2
+    constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
+    constexpr int FM = WM / 16, FN = WN / 16;    // 16x16 tiles per wavefront
+    constexpr int NT = FM * FN;                  // MFMAs per wavefront per K-step
+    constexpr int LEAD = 4;                      // A register slots
+    constexpr int SB = 4;                        // B stages in the ring
+    constexpr int ROW_A = kBK * 2;               // 64 bytes
+    constexpr int A_BYTES = BM * ROW_A;
+    constexpr int ROW_B = BN * 2;
+    constexpr int B_BYTES = kBK * ROW_B;
+    constexpr int A_LOADS = A_BYTES / 1024 / NW; // 16-byte-per-lane loads per wavefront
+    constexpr int B_LOADS = B_BYTES / 1024 / NW;
+    constexpr int LOADS = A_LOADS + B_LOADS;     // vector-memory instructions per K-step
+    constexpr int BAR = NT / 4;                  // MFMAs of a K-step before its barrier
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
+    static_assert(ROW_B % 256 == 0, "B rows must be whole bank windows");
+    // Every stage is an LDS object of its own: the compiler tracks the
+    // direct-to-LDS loads per object, so reading one B stage does not wait
+    // for the loads still landing in the others.
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES], sb2[B_BYTES],
+        sb3[B_BYTES];
+    auto a_stage = [&](int st) { return (lds_byte*)(st == 0 ? sa0 : sa1); };
+    auto b_stage = [&](int st) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+
+    const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, true, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * 2u);
+
+    // ---- global load geometry
+    // A: load j of this wavefront fills 1 KB = 16 tile rows; lane -> row
+    //    +lane/4, physical piece lane%4 holding logical piece p ^ swz_a(row).
+    //    voffset = (row*K + piece*8)*2 (kOOB for rows >= M); the K-step's
+    //    k0*2 goes in the scalar offset.  Pieces starting at or past K read
+    //    zeros (checked per K-step).
+    unsigned a_voff[A_LOADS];
+    int a_kp[A_LOADS];
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+        const int row = 16 * (wave * A_LOADS + j) + (lane >> 2);
+        const int piece = (lane & 3) ^ swz_a(row);
+        a_voff[j] = (m0 + row) < M ? ((unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 8u) * 2u : kOOB;
+        a_kp[j] = piece * 8;
+    }
+    // B: load j fills 1 KB = 1024/ROW_B tile rows; lane -> byte 16*lane of
+    //    it, physical piece (16*lane % ROW_B)/16 holding logical piece
+    //    p ^ swz_b(k).  voffset = (k*N + col)*2 (kOOB for columns >= N)
+    //    relative to a buffer that starts at row k0 and ends at row
+    //    min(K, k0 + 32), so rows >= K read zero.
+    unsigned b_voff[B_LOADS];
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+        const int byte = 1024 * (wave * B_LOADS + j) + lane * 16;
+        const int k = byte / ROW_B;
+        const int piece = ((byte % ROW_B) / 16) ^ swz_b<BN>(k);
+        const int col = n0 + piece * 8;
+        b_voff[j] = col < N ? ((unsigned)k * (unsigned)N + (unsigned)col) * 2u : kOOB;
+    }
+
+    u32x4 stg[LEAD][A_LOADS];
+    // A rows of the K-step at k0 -> register slot `slot`, load j.
+    auto load_a = [&](int slot, int k0_in, int j) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0 * 2, 0));
+    };
+    // Register slot `slot`, load j -> A stage `st`.
+    auto store_a = [&](int st, int slot, int j) {
+        lds_byte* p = a_stage(st) + (wave * A_LOADS + j) * 1024 + lane * 16;
+        *(u32x4 __attribute__((address_space(3)))*)p = stg[slot][j];
+    };
+    // B rows of the K-step at k0, load j -> B stage `st` (direct to LDS).
+    auto load_b = [&](int st, int k0_in, int j) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const int krem = K - k0;
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > kBK ? kBK : krem));
+        const __amdgpu_buffer_rsrc_t rbk =
+            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
+        // (copied to a local: clang's host pass drops the kernel stub when a
+        // captured array element is passed straight to a buffer builtin)
+        const unsigned off = b_voff[j];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rbk, (void __attribute__((address_space(3)))*)(b_stage(st) + (wave * B_LOADS + j) * 1024), 16,
+            off, 0, 0, 0);
+    };
+
+    // ---- operand read addresses (within a stage); the stage, the tile and
+    // the half of a transpose read are constants.
+    // A fragment (tile bi): row wm*WM + 16*bi + lane%16, logical piece
+    // lane/16 (K 8*(lane/16) .. +7); the swizzle depends only on lane%16.
+    const int a_rd = (wm * WM + (lane & 15)) * ROW_A + (((lane >> 4) ^ swz_a(lane & 15)) * 16);
+    // B fragment (tile bj) via two transpose reads: within each 16-lane group
+    // g = lane/16, lane 4r+q points at K row 8g + r (+4 for the second read),
+    // columns 4q..4q+3 of the tile; lane i of the group receives column i.
+    // The swizzle is the same for rows k and k+4.
+    int b_rd[FN];
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) {
+        const int g16 = lane & 15;
+        const int k = 8 * (lane >> 4) + (g16 >> 2);
+        const int n = wn * WN + 16 * bj + 4 * (g16 & 3);
+        const int piece = (n >> 3) ^ swz_b<BN>(k);
+        b_rd[bj] = k * ROW_B + piece * 16 + (n & 7) * 2;
+    }
+    auto read_a = [&](int st, int bi) -> u32x4 {
+        return *(const u32x4 __attribute__((address_space(3)))*)(a_stage(st) + a_rd + bi * 16 * ROW_A);
+    };
+    auto read_b = [&](int st, int bj) -> u32x4 {
+        const lds_byte* p = b_stage(st) + b_rd[bj];
+        const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
+        const s16x4 h1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p + 4 * ROW_B));
+        return __builtin_bit_cast(u32x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x4 acc[FM][FN];
+    u32x4 fa[2][FM], fb[2][FN];
+
+    // ---- software pipeline.  Vector-memory instructions are issued in
+    // groups, one per K-step: group it = [A loads of K-step it+LEAD, B loads
+    // of K-step it+SB-1].  The prologue issues groups -LEAD .. -1 (the parts
+    // that exist), so when K-step it waits for its B loads of K-step it+1
+    // (group it+2-SB), exactly SB-2 full groups were issued after them.
+#pragma unroll
+    for (int g = -LEAD; g < 0; ++g) {
+        if (g + LEAD >= 0)
+#pragma unroll
+            for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * kBK, j);
+        if (g + SB - 1 >= 0)
+#pragma unroll
+            for (int j = 0; j < B_LOADS; ++j) load_b(g + SB - 1, (g + SB - 1) * kBK, j);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS));   // group -SB+1 (B of K-step 0) landed
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) fb[0][bj] = read_b(0, bj);
+#pragma unroll
+    for (int bi = 0; bi < FM; ++bi) fa[0][bi] = read_a(0, bi);
+
+    // One K-step; q = it % LEAD is a literal, so every slot, stage and
+    // register set below is fixed at compile time.
+    //   MFMAs 0 .. BAR-1, interleaved with: A writes of K-step it+1 (slot
+    //     (q+1)%LEAD -> A stage (q+1)%2), A loads of K-step it+LEAD (-> slot
+    //     q, which K-step it left one step ago), B loads of K-step it+SB-1
+    //     (-> B stage (q-1)%SB, which every wavefront finished reading
+    //     before the previous barrier).
+    //   wait for this wavefront's B loads of K-step it+1; barrier.
+    //   MFMAs BAR .. NT-1, interleaved with the operand reads of K-step it+1
+    //     into register set (q+1)%2.
+    auto kstep = [&](const int q, int it, const bool first) {
+        const int cur = q & 1, nxt = cur ^ 1;
+        auto mfma = [&](int x) {
+            if (first)
+                Mfma16x16<T>::first(acc[x / FN][x % FN], fb[cur][x % FN], fa[cur][x / FN]);
+            else
+                Mfma16x16<T>::acc(acc[x / FN][x % FN], fb[cur][x % FN], fa[cur][x / FN]);
+        };
+        constexpr int NOPS1 = A_LOADS + LOADS;
+#pragma unroll
+        for (int x = 0; x < BAR; ++x) {
+            mfma(x);
+#pragma unroll
+            for (int o = 0; o < NOPS1; ++o) {
+                if (o * BAR / NOPS1 != x) continue;
+                if (o < A_LOADS)
+                    store_a(nxt, (q + 1) % LEAD, o);
+                else if (o < 2 * A_LOADS)
+                    load_a(q, (it + LEAD) * kBK, o - A_LOADS);
+                else
+                    load_b((q + SB - 1) % SB, (it + SB - 1) * kBK, o - 2 * A_LOADS);
+            }
+        }
+        // The count below assumes every load of this K-step was issued
+        // above it: keep the compiler from sinking any (it may otherwise
+        // move loads whose results are needed only steps later).
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        constexpr int NOPS2 = FN + FM;
+#pragma unroll
+        for (int x = BAR; x < NT; ++x) {
+            mfma(x);
+#pragma unroll
+            for (int o = 0; o < NOPS2; ++o) {
+                if (o * (NT - BAR) / NOPS2 != x - BAR) continue;
+                if (o < FN)
+                    fb[nxt][o] = read_b((q + 1) % SB, o);
+                else
+                    fa[nxt][o - FN] = read_a(nxt, o - FN);
+            }
+        }
+    };
+
+    // K-steps, rounded up to the LEAD-step unroll and at least one round:
+    // the extra steps multiply the zeros their loads brought in.
+    const int nk = cdiv_i(cdiv_i(K, kBK), LEAD) * LEAD;
+    kstep(0, 0, true);
+#pragma unroll
+    for (int q = 1; q < LEAD; ++q) kstep(q, q, false);
+    for (int it = LEAD; it < nk; it += LEAD) {
+#pragma unroll
+        for (int q = 0; q < LEAD; ++q) kstep(q, it + q, false);
+    }
+
+    // ---- epilogue
+    // The last row of tiles was written by the most recent MFMAs: give them
+    // time to finish before any accumulator is read (the tiles of earlier
+    // rows are at least FN MFMAs old).
+    static_assert(FN <= 8, "the wait below lists the last row's tiles");
+    if constexpr (FN == 8)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]),
+                       "+a"(acc[FM - 1][4]), "+a"(acc[FM - 1][5]), "+a"(acc[FM - 1][6]), "+a"(acc[FM - 1][7]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
+    // All loads (the B ring's direct LDS writes included) have landed and
+    // every wavefront is done with the stages before they are reused for C:
+    // each wavefront stages its block through one B stage.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    store_c_block<T, WM, WN, B_BYTES>(acc, b_stage(wave), lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
+}
+
+template <typename T>
+hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
+{
+    const int tiles = cdiv_i(a.M, cfg.bm) * cdiv_i(a.N, cfg.bn);
+    const dim3 grid(tiles), block(256);
+    const T* A = static_cast<const T*>(a.A);
+    const T* B = static_cast<const T*>(a.B);
+    T* C = static_cast<T*>(a.C);
+    if (cfg.threads != 256 || cfg.bk != kBK) return hipErrorInvalidValue;
+#define DGR_LAUNCH(BM_, BN_)                                                                              \
+    if (cfg.bm == BM_ && cfg.bn == BN_) {                                                                \
+        hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_>), grid, block, 0, a.stream, A, B, C, a.M,    \
+                           a.N, a.K, cfg.group_m);                                                       \
+        return hipGetLastError();                                                                        \
+    }
+    DGR_LAUNCH(256, 256)
+    DGR_LAUNCH(256, 128)
+#undef DGR_LAUNCH
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_mfma16x16(const Config& cfg, const LaunchArgs& a)
+{
+    if (a.dtype == kF16) return launch_t<_Float16>(cfg, a);
+    if (a.dtype == kBF16) return launch_t<__bf16>(cfg, a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dgr

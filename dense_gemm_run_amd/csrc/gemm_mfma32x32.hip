@@ -1,5 +1,6 @@
-// Pipelined MFMA kernel for fp16/bf16 problems whose rows are 16-byte aligned
-// (K and N multiples of 8 elements, A, B, C 16-byte aligned).
+// Pipelined MFMA kernel built on v_mfma_f32_32x32x16_{f16,bf16}, for
+// fp16/bf16 problems whose rows are 16-byte aligned (K and N multiples of 8
+// elements, A, B, C 16-byte aligned).
 //
 // Structure (the tiled loop of kernels-book chapter "Matrix Multiplication",
 // section "Tiles"; one program per BM x BN output tile with an fp32
@@ -7,16 +8,16 @@
 //
 //  * Tile order: 1-D grid, XCD-aware remap + grouped band order
 //    (tile_of_block in gemm_internal.h).
-//  * Staging: K is walked in steps of 32.  Four LDS stages form a ring; the
-//    BM x 32 A tile and 32 x BN B tile of K-step it+3 are copied global -> LDS
-//    while K-step it is multiplied, by buffer loads that write LDS directly
-//    (16 bytes per lane, no VGPR round trip), spread over the step so the
-//    load path is never flooded.  Out-of-range 16-byte pieces (rows >= M,
-//    columns >= N, K positions >= K) get an offset past the buffer's end,
-//    which the buffer unit returns as zeros: the zero padding of the pages'
-//    tensor descriptors (chapter "Matrix Multiplication", section "The real
-//    tiled loop").
-//  * LDS layout: A tile [BM][32] and B tile [32][BN], both with their 16-byte
+//  * Staging: K is walked in steps of BK (32 or 64).  Global loads go to
+//    registers first: the BM x BK A tile and BK x BN B tile of K-step it+L
+//    (L = 128/BK register slots) are loaded while K-step it is multiplied,
+//    and K-step it+1 is written from its slot into the other of two LDS
+//    stages during the same step, so every load has L-1 K-steps to land.
+//    Out-of-range 16-byte pieces (rows >= M, columns >= N, K positions >= K)
+//    get an offset past the buffer's end, which the buffer unit returns as
+//    zeros: the zero padding of the pages' tensor descriptors (chapter
+//    "Matrix Multiplication", section "The real tiled loop").
+//  * LDS layout: A tile [BM][BK] and B tile [BK][BN], both with their 16-byte
 //    pieces XOR-swizzled by row so the MFMA operand reads hit every bank
 //    once per cycle (the pages pad rows for the same purpose; chapter "Fast
 //    matrix multiplication", section "Shared-memory bank conflicts").
@@ -27,8 +28,8 @@
 //    memory) and read with the gfx950 LDS transpose read, which hands each
 //    lane 4 consecutive K values of one column.  Operands of the next
 //    16-wide K-slice are read while the current one multiplies; one barrier
-//    per K-step, placed inside the step's second slice, publishes the next
-//    stage and retires the oldest one.
+//    per K-step, placed inside the step's last slice, publishes the next
+//    stage.
 //  * The MFMA is issued with its operands swapped (B fragment first), which
 //    computes the transposed 32x32 block: each lane holds 4 consecutive
 //    columns of one row.  The epilogue rounds the fp32 sums to the output
@@ -36,21 +37,12 @@
 //    and writes C with 16-byte stores covering whole row segments, skipping
 //    rows >= M and columns >= N.
 #include "gemm_internal.h"
+#include "gemm_device.h"
 
 namespace dgr {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) unsigned char lds_byte;
-
 constexpr int kLeadK = 128;          // K elements of global loads kept in flight
-constexpr unsigned kOOB = 0x80000000u;   // byte offset past any buffer (< 2^31 bytes)
 
 template <typename T> struct Op;
 template <> struct Op<_Float16> {
@@ -59,25 +51,12 @@ template <> struct Op<_Float16> {
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
-    // two fp32 -> two fp16 (round to nearest even), packed
-    static __device__ inline unsigned pack2(float a, float b)
-    {
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        h2 v = {(_Float16)a, (_Float16)b};
-        return __builtin_bit_cast(unsigned, v);
-    }
 };
 template <> struct Op<__bf16> {
     typedef bf16x8 V8;
     static __device__ inline f32x16 mfma(V8 a, V8 b, f32x16 c)
     {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    static __device__ inline unsigned pack2(float a, float b)
-    {
-        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-        b2 v = {(__bf16)a, (__bf16)b};
-        return __builtin_bit_cast(unsigned, v);
     }
 };
 
@@ -91,21 +70,6 @@ template <> struct Op<__bf16> {
 // different bank groups.
 template <int BK> __device__ __forceinline__ int swz_a(int row) { return (row / (128 / BK)) % (BK / 8); }
 template <int BN> __device__ __forceinline__ int swz_b(int k) { return ((k & 7) << 2) & (BN / 8 - 1); }
-
-// s_waitcnt immediate that waits until at most n vector-memory loads of this
-// wavefront are outstanding (gfx9 encoding: vmcnt bits 3:0 and 15:14,
-// expcnt and lgkmcnt left at their maximum, i.e. not waited for).
-constexpr unsigned waitcnt_vm(unsigned n)
-{
-    return (n & 15u) | (7u << 4) | (15u << 8) | ((n >> 4) << 14);
-}
-// ... and the one that waits for all of this wavefront's LDS operations.
-constexpr unsigned kWaitLgkm0 = 15u | (7u << 4) | (0u << 8) | (3u << 14);
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, unsigned bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 
 // Epilogue shared by the kernels: one wavefront's WM x WN block of fp32
 // accumulators (lane l holds row 32*bi + l%32, columns 32*bj + 8g + 4*(l/32)
@@ -134,8 +98,8 @@ __device__ __forceinline__ void store_c_block(const f32x16 (&acc)[WM / 32][WN / 
                 const int p = (4 * bj + g) ^ (r & (PR - 1));
                 const int h = (lane >> 5) ^ ((r / PR) & 1);
                 u32x2 v;
-                v[0] = Op<T>::pack2(acc[bi][bj][4 * g + 0], acc[bi][bj][4 * g + 1]);
-                v[1] = Op<T>::pack2(acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]);
+                v[0] = pack2<T>(acc[bi][bj][4 * g + 0], acc[bi][bj][4 * g + 1]);
+                v[1] = pack2<T>(acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]);
                 *(u32x2 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16 + h * 8) = v;
             }
         }
@@ -156,7 +120,7 @@ __device__ __forceinline__ void store_c_block(const f32x16 (&acc)[WM / 32][WN / 
 }
 
 template <typename T, int BM, int BN, int BK, int WAVES_N>
-__global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_mfma16_kernel(
+__global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_mfma32x32_kernel(
     const T* __restrict__ A, const T* __restrict__ B, T* __restrict__ C,
     int M, int N, int K, int group_m)
 {
@@ -428,7 +392,7 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     T* C = static_cast<T*>(a.C);
 #define DGR_LAUNCH(BM_, BN_, BK_, WN_)                                                               \
     if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_ && cfg.threads == 128 * WN_) {               \
-        hipLaunchKernelGGL((gemm_mfma16_kernel<T, BM_, BN_, BK_, WN_>), grid, block, 0, a.stream, A, B, C, \
+        hipLaunchKernelGGL((gemm_mfma32x32_kernel<T, BM_, BN_, BK_, WN_>), grid, block, 0, a.stream, A, B, C, \
                            a.M, a.N, a.K, cfg.group_m);                                            \
         return hipGetLastError();                                                                  \
     }
@@ -443,7 +407,7 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
 
 }  // namespace
 
-hipError_t launch_mfma16(const Config& cfg, const LaunchArgs& a)
+hipError_t launch_mfma32x32(const Config& cfg, const LaunchArgs& a)
 {
     if (a.dtype == kF16) return launch_t<_Float16>(cfg, a);
     if (a.dtype == kBF16) return launch_t<__bf16>(cfg, a);
