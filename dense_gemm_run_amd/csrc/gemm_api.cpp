@@ -90,10 +90,10 @@ bool accepts(const Entry& e, const void* A, const void* B, const void* C,
 }
 
 // Shape classes.  Small or oddly aligned problems take the generic kernel;
-// aligned fp16/bf16 problems take the MFMA kernel with the largest tile that
-// still gives every CU work, with 64-deep K-steps when K is long enough
-// (measured 2-3 % faster than 32-deep ones at 4096^3 and on the 8192-token
-// projections).
+// aligned fp16/bf16 problems take an MFMA kernel with the largest tile that
+// still gives every CU work.  For 256x256 tiles that is the 16x16x32 kernel
+// (measured 6-9 % faster than the 32x32x16 one at 4096^3 and 8192^3: it runs
+// at a higher clock under the power limit).
 int select(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
            int32_t dtype)
 {
@@ -103,7 +103,7 @@ int select(const void* A, const void* B, const void* C, int64_t M, int64_t N, in
     if (M * N * K < (int64_t)128 * 128 * 128) return 0;
     // largest tile that still leaves at least one tile per CU (256 CUs)
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-    if (t256 >= 256) return K >= 512 ? 5 : 1;
+    if (t256 >= 256) return 6;
     const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
     if (t128 >= 256) return 2;
     return 3;

@@ -29,14 +29,14 @@
 //    it.  Out-of-range 16-byte pieces read zeros, as in the 32x32 kernel (the
 //    zero padding of chapter "Matrix Multiplication", section "The real
 //    tiled loop").
-//  * LDS layout: A [BM][32] with 16-byte pieces XOR-swizzled by (row/4)%4,
-//    so the 16 rows one 16-lane group reads land on 16 different 16-byte
-//    bank groups; B [32][BN] with 16-byte pieces XOR-swizzled by an even
+//  * LDS layout: A [BM][32] with 16-byte pieces XOR-swizzled by (row/2)%4
+//    (the layout that measured free of bank conflicts for this read); B
+//    [32][BN] with 16-byte pieces XOR-swizzled by an even
 //    value taken from bits 0, 1 and 3 of the row, so the 8 rows that one
 //    half-wavefront's transpose read touches (k = r, r+8 for r in a group of
 //    4) cover all 64 banks (chapter "Fast matrix multiplication", section
 //    "Shared-memory bank conflicts", pads rows for the same purpose).
-//  * One barrier per K-step, a quarter of the way into its MFMAs: it
+//  * One barrier per K-step, half way through its MFMAs: it
 //    publishes K-step it+1 (A written by every wavefront, B landed), after
 //    which the operands of K-step it+1 are read into the second register set
 //    while the rest of K-step it multiplies.
@@ -77,9 +77,13 @@ template <> struct Mfma16x16<__bf16> {
     }
 };
 
-// A row of the A tile is 64 bytes (4 pieces of 16 bytes); 4 rows share one
-// 256-byte bank window.
-__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
+// A row of the A tile is 64 bytes (4 pieces of 16 bytes).  The operand read
+// has 16-lane group g read piece g of 16 consecutive rows.  XOR-ing the piece
+// with (row/2)%4 makes that read run without LDS bank conflicts on gfx950
+// (measured with the bank-conflict counter over candidate layouts); the
+// (row/4)%4 swizzle, which spreads each group's 16 reads over all 64 banks,
+// still conflicts there about 4 cycles per instruction.
+__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 3; }
 // B rows are BN*2 bytes (a multiple of 256): every row starts at bank 0.
 template <int BN> __device__ __forceinline__ int swz_b(int k)
 {
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     constexpr int A_LOADS = A_BYTES / 1024 / NW; // 16-byte-per-lane loads per wavefront
     constexpr int B_LOADS = B_BYTES / 1024 / NW;
     constexpr int LOADS = A_LOADS + B_LOADS;     // vector-memory instructions per K-step
-    constexpr int BAR = NT / 4;                  // MFMAs of a K-step before its barrier
+    constexpr int BAR = NT / 2;                  // MFMAs of a K-step before its barrier
     static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
     static_assert(ROW_B % 256 == 0, "B rows must be whole bank windows");
     // Every stage is an LDS object of its own: the compiler tracks the
@@ -267,10 +271,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     u32x4 fa[2][FM], fb[2][FN];
 
     // ---- software pipeline.  Vector-memory instructions are issued in
-    // groups, one per K-step: group it = [A loads of K-step it+LEAD, B loads
-    // of K-step it+SB-1].  The prologue issues groups -LEAD .. -1 (the parts
-    // that exist), so when K-step it waits for its B loads of K-step it+1
-    // (group it+2-SB), exactly SB-2 full groups were issued after them.
+    // groups, one per K-step: group it = [A loads of K-step it+LEAD (before
+    // the step's barrier), B loads of K-step it+SB-1 (after it)].  The
+    // prologue issues groups -LEAD .. -1 (the parts that exist).  When K-step
+    // it waits for its B loads of K-step it+1 (the end of group it+2-SB),
+    // group it-1 and the A loads of group it were issued after them: at most
+    // LOADS + A_LOADS of this wavefront's loads may still be in flight.
 #pragma unroll
     for (int g = -LEAD; g < 0; ++g) {
         if (g + LEAD >= 0)
@@ -296,12 +302,14 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // register set below is fixed at compile time.
     //   MFMAs 0 .. BAR-1, interleaved with: A writes of K-step it+1 (slot
     //     (q+1)%LEAD -> A stage (q+1)%2), A loads of K-step it+LEAD (-> slot
-    //     q, which K-step it left one step ago), B loads of K-step it+SB-1
-    //     (-> B stage (q-1)%SB, which every wavefront finished reading
-    //     before the previous barrier).
+    //     q, which K-step it left one step ago).
     //   wait for this wavefront's B loads of K-step it+1; barrier.
-    //   MFMAs BAR .. NT-1, interleaved with the operand reads of K-step it+1
-    //     into register set (q+1)%2.
+    //   MFMAs BAR .. NT-1, interleaved with: B loads of K-step it+SB-1 (->
+    //     B stage (q-1)%SB, which every wavefront finished reading before
+    //     this step's barrier), then the operand reads of K-step it+1 into
+    //     register set (q+1)%2.
+    // Issuing all of a step's loads in one burst stalls the in-order MFMA
+    // stream (measured); they are spread over both halves of the step.
     auto kstep = [&](const int q, int it, const bool first) {
         const int cur = q & 1, nxt = cur ^ 1;
         auto mfma = [&](int x) {
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
             else
                 Mfma16x16<T>::acc(acc[x / FN][x % FN], fb[cur][x % FN], fa[cur][x / FN]);
         };
-        constexpr int NOPS1 = A_LOADS + LOADS;
+        constexpr int NOPS1 = 2 * A_LOADS;
 #pragma unroll
         for (int x = 0; x < BAR; ++x) {
             mfma(x);
@@ -319,31 +327,31 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
                 if (o * BAR / NOPS1 != x) continue;
                 if (o < A_LOADS)
                     store_a(nxt, (q + 1) % LEAD, o);
-                else if (o < 2 * A_LOADS)
-                    load_a(q, (it + LEAD) * kBK, o - A_LOADS);
                 else
-                    load_b((q + SB - 1) % SB, (it + SB - 1) * kBK, o - 2 * A_LOADS);
+                    load_a(q, (it + LEAD) * kBK, o - A_LOADS);
             }
         }
         // The count below assumes every load of this K-step was issued
         // above it: keep the compiler from sinking any (it may otherwise
         // move loads whose results are needed only steps later).
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS + A_LOADS));
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        constexpr int NOPS2 = FN + FM;
+        constexpr int NOPS2 = B_LOADS + FN + FM;
 #pragma unroll
         for (int x = BAR; x < NT; ++x) {
             mfma(x);
 #pragma unroll
             for (int o = 0; o < NOPS2; ++o) {
                 if (o * (NT - BAR) / NOPS2 != x - BAR) continue;
-                if (o < FN)
-                    fb[nxt][o] = read_b((q + 1) % SB, o);
+                if (o < B_LOADS)
+                    load_b((q + SB - 1) % SB, (it + SB - 1) * kBK, o);
+                else if (o < B_LOADS + FN)
+                    fb[nxt][o - B_LOADS] = read_b((q + 1) % SB, o - B_LOADS);
                 else
-                    fa[nxt][o - FN] = read_a(nxt, o - FN);
+                    fa[nxt][o - B_LOADS - FN] = read_a(nxt, o - B_LOADS - FN);
             }
         }
     };

@@ -1,13 +1,13 @@
 """Structure of the generated code of the 16x16x32 MFMA kernel.
 
 Its B tiles reach LDS through direct buffer->LDS loads that the kernel waits
-for by count: before each barrier a wavefront waits until at most 2 K-steps of
-its own loads are outstanding, which is right only if every K-step issues its
-A loads, then its B loads, all before that wait.  The MFMAs are inline
-assembly, so the compiler may move other instructions around them; these
-tests compile the kernel to gfx950 assembly (no GPU needed) and check that
-the issue order is the one the counts assume, and that the accumulators stay
-in place.
+for by count: before each barrier a wavefront waits until at most a fixed
+number of its own loads are outstanding, which is right only if every K-step
+issues its A loads before its barrier and its B loads after it, in that
+order.  The MFMAs are inline assembly, so the compiler may move other
+instructions around them; these tests compile the kernel to gfx950 assembly
+(no GPU needed) and check that the issue order is the one the counts assume,
+and that the accumulators stay in place.
 """
 import os
 import re
@@ -65,23 +65,29 @@ def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels)
     for name, (bm, bn, body) in kernels.items():
         a_loads = bm * 64 // 1024 // 4
         b_loads = 32 * bn * 2 // 1024 // 4
-        count = 2 * (a_loads + b_loads)
+        count = a_loads + b_loads + a_loads
         ev = events(body)
         bars = [i for i, e in enumerate(ev) if e == "B"]
         # prologue + 4 peeled K-steps + the 4 of the loop body, then the epilogue's
         assert len(bars) == 10, (name, len(bars))
-        # prologue: A(0) A(1) B(0) A(2) B(1) A(3) B(2), then the counted wait
+        # prologue: A(0) A(1) B(0) A(2) B(1) A(3) B(2), then a wait for B(0)
         pro = [e for e in ev[:bars[0]] if e in ("g", "L")]
         assert pro == (["g"] * a_loads * 2 + ["L"] * b_loads + (["g"] * a_loads + ["L"] * b_loads) * 2), name
-        for k in range(8):   # the K-steps: between consecutive barriers
+        pro_waits = [e[1] for e in ev[:bars[0]] if isinstance(e, tuple)]
+        assert pro_waits and pro_waits[-1] == 2 * (a_loads + b_loads), (name, pro_waits)
+        # a K-step issues its A loads before its barrier and its B loads
+        # after it, so between two barriers: B loads of the previous step,
+        # then A loads of this one
+        for k in range(8):
             seg = ev[bars[k] + 1:bars[k + 1]]
             loads = [e for e in seg if e in ("g", "L")]
-            assert loads == ["g"] * a_loads + ["L"] * b_loads, (name, k, loads)
-            # the last vmcnt wait before the barrier is the counted one
+            expect = (["L"] * b_loads if k else []) + ["g"] * a_loads
+            assert loads == expect, (name, k, loads)
+            # the last vmcnt wait before the barrier is the counted one, and
+            # nothing inside the step waits for more
             waits = [e[1] for e in seg if isinstance(e, tuple)]
             assert waits and waits[-1] == count, (name, k, waits)
-            # nothing inside the step waits for more than the count allows
-            assert min(waits) >= count or min(waits) == waits[-1], (name, k, waits)
+            assert min(waits) == count, (name, k, waits)
 
 
 def test_accumulators_stay_in_place(kernels):
