@@ -41,6 +41,8 @@ const Entry kTable[] = {
     {{5, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma32x32_256x256x64"}, kMfma32x32},
     {{6, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x32"}, kMfma16x16},
     {{7, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x128x32"}, kMfma16x16},
+    {{8, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x64"}, kMfma16x16},
+    {{9, 256, 128, 64, 4, 256, 0x6, 1, 1, "mfma16x16_256x128x64"}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 

@@ -51,8 +51,6 @@
 namespace dgr {
 namespace {
 
-constexpr int kBK = 32;   // K-step = one MFMA K-slice
-
 template <typename T> struct Mfma16x16;
 template <> struct Mfma16x16<_Float16> {
     // c += b-fragment x a-fragment (16x16x32)
@@ -77,13 +75,14 @@ template <> struct Mfma16x16<__bf16> {
     }
 };
 
-// A row of the A tile is 64 bytes (4 pieces of 16 bytes).  The operand read
-// has 16-lane group g read piece g of 16 consecutive rows.  XOR-ing the piece
-// with (row/2)%4 makes that read run without LDS bank conflicts on gfx950
-// (measured with the bank-conflict counter over candidate layouts); the
-// (row/4)%4 swizzle, which spreads each group's 16 reads over all 64 banks,
-// still conflicts there about 4 cycles per instruction.
-__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 3; }
+// A rows are BK*2 bytes (4 or 8 pieces of 16 bytes).  The operand read has
+// 16-lane group g read logical piece 4*sl + g of 16 consecutive rows.
+// XOR-ing the piece with (row/2) % (BK/8) makes that read run without LDS
+// bank conflicts on gfx950 (measured with the bank-conflict counter over
+// candidate layouts); with 64-byte rows, the (row/4)%4 swizzle, which spreads
+// each group's 16 reads over all 64 banks, still conflicts there about 4
+// cycles per instruction.
+template <int BK> __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & (BK / 8 - 1); }
 // B rows are BN*2 bytes (a multiple of 256): every row starts at bank 0.
 template <int BN> __device__ __forceinline__ int swz_b(int k)
 {
@@ -140,7 +139,7 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
     }
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int BK>
 __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const T* A, const T* B, T* C,
     int M, int N, int K, int group_m)
@@ -148,27 +147,33 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
     constexpr int FM = WM / 16, FN = WN / 16;    // 16x16 tiles per wavefront
-    constexpr int NT = FM * FN;                  // MFMAs per wavefront per K-step
-    constexpr int LEAD = 4;                      // A register slots
-    constexpr int SB = 4;                        // B stages in the ring
-    constexpr int ROW_A = kBK * 2;               // 64 bytes
+    constexpr int NT = FM * FN;                  // MFMAs per wavefront per 32-deep K-slice
+    constexpr int NS = BK / 32;                  // K-slices per K-step
+    constexpr int XS = NS * NT;                  // MFMAs per wavefront per K-step
+    constexpr int LEAD = 128 / BK;               // A register slots (K-steps loaded ahead)
+    constexpr int SB = BK == 32 ? 4 : 2;         // B stages (K-steps loaded ahead)
+    constexpr int ROW_A = BK * 2;
+    constexpr int PA = BK / 8;                   // 16-byte pieces per A row
     constexpr int A_BYTES = BM * ROW_A;
     constexpr int ROW_B = BN * 2;
-    constexpr int B_BYTES = kBK * ROW_B;
+    constexpr int B_BYTES = BK * ROW_B;
     constexpr int A_LOADS = A_BYTES / 1024 / NW; // 16-byte-per-lane loads per wavefront
     constexpr int B_LOADS = B_BYTES / 1024 / NW;
     constexpr int LOADS = A_LOADS + B_LOADS;     // vector-memory instructions per K-step
-    constexpr int BAR = NT / 2;                  // MFMAs of a K-step before its barrier
+    constexpr int NR = FM + FN;                  // operand fragments per K-slice
+    constexpr int BAR = XS - NT / 2;             // MFMAs of a K-step before its barrier
+    static_assert(BK == 32 || BK == 64, "K-step");
     static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
     static_assert(ROW_B % 256 == 0, "B rows must be whole bank windows");
+    static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
     // Every stage is an LDS object of its own: the compiler tracks the
     // direct-to-LDS loads per object, so reading one B stage does not wait
     // for the loads still landing in the others.
     __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES], sb2[B_BYTES],
-        sb3[B_BYTES];
-    auto a_stage = [&](int st) { return (lds_byte*)(st == 0 ? sa0 : sa1); };
-    auto b_stage = [&](int st) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb2[SB > 2 ? B_BYTES : 1], sb3[SB > 2 ? B_BYTES : 1];
+    auto a_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sa0 : sa1); };
+    auto b_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int tm, tn;
@@ -182,17 +187,17 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * 2u);
 
     // ---- global load geometry
-    // A: load j of this wavefront fills 1 KB = 16 tile rows; lane -> row
-    //    +lane/4, physical piece lane%4 holding logical piece p ^ swz_a(row).
-    //    voffset = (row*K + piece*8)*2 (kOOB for rows >= M); the K-step's
-    //    k0*2 goes in the scalar offset.  Pieces starting at or past K read
-    //    zeros (checked per K-step).
+    // A: load j of this wavefront fills 1 KB = 1024/ROW_A tile rows; lane ->
+    //    row +lane/PA, physical piece lane%PA holding logical piece
+    //    p ^ swz_a(row).  voffset = (row*K + piece*8)*2 (kOOB for rows >= M);
+    //    the K-step's k0*2 goes in the scalar offset.  Pieces starting at or
+    //    past K read zeros (checked per K-step).
     unsigned a_voff[A_LOADS];
     int a_kp[A_LOADS];
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) {
-        const int row = 16 * (wave * A_LOADS + j) + (lane >> 2);
-        const int piece = (lane & 3) ^ swz_a(row);
+        const int row = (1024 / ROW_A) * (wave * A_LOADS + j) + lane / PA;
+        const int piece = (lane % PA) ^ swz_a<BK>(row);
         a_voff[j] = (m0 + row) < M ? ((unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 8u) * 2u : kOOB;
         a_kp[j] = piece * 8;
     }
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     //    it, physical piece (16*lane % ROW_B)/16 holding logical piece
     //    p ^ swz_b(k).  voffset = (k*N + col)*2 (kOOB for columns >= N)
     //    relative to a buffer that starts at row k0 and ends at row
-    //    min(K, k0 + 32), so rows >= K read zero.
+    //    min(K, k0 + BK), so rows >= K read zero.
     unsigned b_voff[B_LOADS];
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) {
@@ -213,21 +218,21 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
 
     u32x4 stg[LEAD][A_LOADS];
     // A rows of the K-step at k0 -> register slot `slot`, load j.
-    auto load_a = [&](int slot, int k0_in, int j) {
+    auto load_a = [&](int slot, int k0_in, int j) __attribute__((always_inline)) {
         const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
         const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
         stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0 * 2, 0));
     };
     // Register slot `slot`, load j -> A stage `st`.
-    auto store_a = [&](int st, int slot, int j) {
+    auto store_a = [&](int st, int slot, int j) __attribute__((always_inline)) {
         lds_byte* p = a_stage(st) + (wave * A_LOADS + j) * 1024 + lane * 16;
         *(u32x4 __attribute__((address_space(3)))*)p = stg[slot][j];
     };
     // B rows of the K-step at k0, load j -> B stage `st` (direct to LDS).
-    auto load_b = [&](int st, int k0_in, int j) {
+    auto load_b = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
         const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
         const int krem = K - k0;
-        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > kBK ? kBK : krem));
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
         const __amdgpu_buffer_rsrc_t rbk =
             make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
         // (copied to a local: clang's host pass drops the kernel stub when a
@@ -238,15 +243,19 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
             off, 0, 0, 0);
     };
 
-    // ---- operand read addresses (within a stage); the stage, the tile and
-    // the half of a transpose read are constants.
-    // A fragment (tile bi): row wm*WM + 16*bi + lane%16, logical piece
-    // lane/16 (K 8*(lane/16) .. +7); the swizzle depends only on lane%16.
-    const int a_rd = (wm * WM + (lane & 15)) * ROW_A + (((lane >> 4) ^ swz_a(lane & 15)) * 16);
+    // ---- operand read addresses (within a stage); the stage, the tile, the
+    // K-slice's B rows and the half of a transpose read are constants.
+    // A fragment (K-slice sl, tile bi): row wm*WM + 16*bi + lane%16, logical
+    // piece 4*sl + lane/16 (K 32*sl + 8*(lane/16) .. +7); the swizzle depends
+    // only on lane%16.
+    int a_rd[NS];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+        a_rd[sl] = (wm * WM + (lane & 15)) * ROW_A + (((4 * sl + (lane >> 4)) ^ swz_a<BK>(lane & 15)) * 16);
     // B fragment (tile bj) via two transpose reads: within each 16-lane group
-    // g = lane/16, lane 4r+q points at K row 8g + r (+4 for the second read),
-    // columns 4q..4q+3 of the tile; lane i of the group receives column i.
-    // The swizzle is the same for rows k and k+4.
+    // g = lane/16, lane 4r+q points at K row 8g + r (+4 for the second read,
+    // +32 per K-slice), columns 4q..4q+3 of the tile; lane i of the group
+    // receives column i.  The swizzle is the same for rows k, k+4 and k+32.
     int b_rd[FN];
 #pragma unroll
     for (int bj = 0; bj < FN; ++bj) {
@@ -256,11 +265,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
         const int piece = (n >> 3) ^ swz_b<BN>(k);
         b_rd[bj] = k * ROW_B + piece * 16 + (n & 7) * 2;
     }
-    auto read_a = [&](int st, int bi) -> u32x4 {
-        return *(const u32x4 __attribute__((address_space(3)))*)(a_stage(st) + a_rd + bi * 16 * ROW_A);
+    auto read_a = [&](int st, int sl, int bi) __attribute__((always_inline)) -> u32x4 {
+        return *(const u32x4 __attribute__((address_space(3)))*)(a_stage(st) + a_rd[sl] + bi * 16 * ROW_A);
     };
-    auto read_b = [&](int st, int bj) -> u32x4 {
-        const lds_byte* p = b_stage(st) + b_rd[bj];
+    auto read_b = [&](int st, int sl, int bj) __attribute__((always_inline)) -> u32x4 {
+        const lds_byte* p = b_stage(st) + b_rd[bj] + sl * 32 * ROW_B;
         const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
         const s16x4 h1 =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p + 4 * ROW_B));
@@ -268,97 +277,123 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     };
 
     f32x4 acc[FM][FN];
-    u32x4 fa[2][FM], fb[2][FN];
+    u32x4 fa[2][FM], fb[2][FN];   // two operand register sets, alternating by K-slice
+    // Fragment o of a K-slice (B tiles first, then A tiles) -> register set.
+    auto read_frag = [&](int set, int sta, int stb, int sl, int o) __attribute__((always_inline)) {
+        if (o < FN)
+            fb[set][o] = read_b(stb, sl, o);
+        else
+            fa[set][o - FN] = read_a(sta, sl, o - FN);
+    };
 
     // ---- software pipeline.  Vector-memory instructions are issued in
     // groups, one per K-step: group it = [A loads of K-step it+LEAD (before
-    // the step's barrier), B loads of K-step it+SB-1 (after it)].  The
-    // prologue issues groups -LEAD .. -1 (the parts that exist).  When K-step
-    // it waits for its B loads of K-step it+1 (the end of group it+2-SB),
-    // group it-1 and the A loads of group it were issued after them: at most
-    // LOADS + A_LOADS of this wavefront's loads may still be in flight.
+    // the step's barrier), B loads of K-step it+SB (after it)].  The
+    // prologue issues groups -max(LEAD, SB) .. -1 (the parts that exist).
+    // When K-step it waits for its B loads of K-step it+1 (the end of group
+    // it+1-SB), groups it+2-SB .. it-1 and the A loads of group it were
+    // issued after them: at most (SB-2)*LOADS + A_LOADS of this wavefront's
+    // loads may still be in flight.
 #pragma unroll
     for (int g = -LEAD; g < 0; ++g) {
         if (g + LEAD >= 0)
 #pragma unroll
-            for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * kBK, j);
-        if (g + SB - 1 >= 0)
+            for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * BK, j);
+        if (g + SB >= 0)
 #pragma unroll
-            for (int j = 0; j < B_LOADS; ++j) load_b(g + SB - 1, (g + SB - 1) * kBK, j);
+            for (int j = 0; j < B_LOADS; ++j) load_b(g + SB, (g + SB) * BK, j);
     }
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS));   // group -SB+1 (B of K-step 0) landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 1) * LOADS));   // group -SB (B of K-step 0) landed
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int bj = 0; bj < FN; ++bj) fb[0][bj] = read_b(0, bj);
-#pragma unroll
-    for (int bi = 0; bi < FM; ++bi) fa[0][bi] = read_a(0, bi);
+    for (int o = 0; o < NR; ++o) read_frag(0, 0, 0, 0, o);
 
     // One K-step; q = it % LEAD is a literal, so every slot, stage and
-    // register set below is fixed at compile time.
-    //   MFMAs 0 .. BAR-1, interleaved with: A writes of K-step it+1 (slot
-    //     (q+1)%LEAD -> A stage (q+1)%2), A loads of K-step it+LEAD (-> slot
-    //     q, which K-step it left one step ago).
+    // register set below is fixed at compile time.  K-slice sl of K-step it
+    // uses register set (q*NS + sl) % 2.
+    //   MFMAs 0 .. BAR-1, interleaved with: the operand reads of K-slices
+    //     1 .. NS-1 of this K-step (each during the slice before it); A
+    //     writes of K-step it+1 (slot (q+1)%LEAD -> A stage (q+1)%2); A loads
+    //     of K-step it+LEAD (-> slot q, which K-step it left one step ago).
     //   wait for this wavefront's B loads of K-step it+1; barrier.
-    //   MFMAs BAR .. NT-1, interleaved with: B loads of K-step it+SB-1 (->
-    //     B stage (q-1)%SB, which every wavefront finished reading before
-    //     this step's barrier), then the operand reads of K-step it+1 into
-    //     register set (q+1)%2.
+    //   MFMAs BAR .. XS-1, interleaved with: B loads of K-step it+SB (-> B
+    //     stage q%SB: every wavefront finished reading K-step it from it
+    //     before this barrier), then the operand reads of K-slice 0 of K-step
+    //     it+1.
     // Issuing all of a step's loads in one burst stalls the in-order MFMA
-    // stream (measured); they are spread over both halves of the step.
-    auto kstep = [&](const int q, int it, const bool first) {
-        const int cur = q & 1, nxt = cur ^ 1;
-        auto mfma = [&](int x) {
-            if (first)
-                Mfma16x16<T>::first(acc[x / FN][x % FN], fb[cur][x % FN], fa[cur][x / FN]);
-            else
-                Mfma16x16<T>::acc(acc[x / FN][x % FN], fb[cur][x % FN], fa[cur][x / FN]);
-        };
+    // stream (measured); they are spread over the step.
+    // n operations spread evenly over `span` MFMAs: the ones issued after
+    // MFMA number pos are op_lo(pos) .. op_lo(pos+1)-1.
+    auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
+
+    // K-slice sl of K-step it (q = it % LEAD): its MFMAs before the barrier
+    // (x < BAR, counting over the whole K-step), then those after it.  (Two
+    // loops rather than one with a branch: the compiler only unrolls loops
+    // below a size limit, and everything here must unroll.)
+    auto kslice = [&](const int q, int it, const int sl, const bool first) __attribute__((always_inline)) {
+        const int sta = q & 1, stb = q % SB, set = (q * NS + sl) & 1;
         constexpr int NOPS1 = 2 * A_LOADS;
+        constexpr int NOPS2 = B_LOADS + NR;
+        auto mfma = [&](int xx) __attribute__((always_inline)) {
+            if (first && sl == 0)
+                Mfma16x16<T>::first(acc[xx / FN][xx % FN], fb[set][xx % FN], fa[set][xx / FN]);
+            else
+                Mfma16x16<T>::acc(acc[xx / FN][xx % FN], fb[set][xx % FN], fa[set][xx / FN]);
+        };
+        const int lo = sl * NT, hi = lo + NT;
 #pragma unroll
-        for (int x = 0; x < BAR; ++x) {
-            mfma(x);
+        for (int x = lo; x < (hi < BAR ? hi : BAR); ++x) {
+            const int xx = x - lo;
+            mfma(xx);
+            if (sl + 1 < NS) {
 #pragma unroll
-            for (int o = 0; o < NOPS1; ++o) {
-                if (o * BAR / NOPS1 != x) continue;
+                for (int o = op_lo(xx, NR, NT); o < op_lo(xx + 1, NR, NT); ++o)
+                    read_frag(set ^ 1, sta, stb, sl + 1, o);
+            }
+#pragma unroll
+            for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
                 if (o < A_LOADS)
-                    store_a(nxt, (q + 1) % LEAD, o);
+                    store_a(sta ^ 1, (q + 1) % LEAD, o);
                 else
-                    load_a(q, (it + LEAD) * kBK, o - A_LOADS);
+                    load_a(q, (it + LEAD) * BK, o - A_LOADS);
             }
         }
-        // The count below assumes every load of this K-step was issued
-        // above it: keep the compiler from sinking any (it may otherwise
-        // move loads whose results are needed only steps later).
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LOADS + A_LOADS));
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        constexpr int NOPS2 = B_LOADS + FN + FM;
+        if (lo < BAR && BAR <= hi) {
+            // The count below assumes every load of this K-step before the
+            // barrier was issued above it: keep the compiler from sinking
+            // any (it may otherwise move loads whose results are needed only
+            // steps later).
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS + A_LOADS));
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
 #pragma unroll
-        for (int x = BAR; x < NT; ++x) {
-            mfma(x);
+        for (int x = (lo > BAR ? lo : BAR); x < hi; ++x) {
+            mfma(x - lo);
 #pragma unroll
-            for (int o = 0; o < NOPS2; ++o) {
-                if (o * (NT - BAR) / NOPS2 != x - BAR) continue;
+            for (int o = op_lo(x - BAR, NOPS2, XS - BAR); o < op_lo(x + 1 - BAR, NOPS2, XS - BAR); ++o) {
                 if (o < B_LOADS)
-                    load_b((q + SB - 1) % SB, (it + SB - 1) * kBK, o);
-                else if (o < B_LOADS + FN)
-                    fb[nxt][o - B_LOADS] = read_b((q + 1) % SB, o - B_LOADS);
+                    load_b(stb, (it + SB) * BK, o);
                 else
-                    fa[nxt][o - B_LOADS - FN] = read_a(nxt, o - B_LOADS - FN);
+                    read_frag(((q + 1) * NS) & 1, sta ^ 1, (q + 1) % SB, 0, o - B_LOADS);
             }
         }
+    };
+    auto kstep = [&](const int q, int it, const bool first) __attribute__((always_inline)) {
+        kslice(q, it, 0, first);
+        if constexpr (NS > 1) kslice(q, it, 1, false);
     };
 
     // K-steps, rounded up to the LEAD-step unroll and at least one round:
     // the extra steps multiply the zeros their loads brought in.
-    const int nk = cdiv_i(cdiv_i(K, kBK), LEAD) * LEAD;
+    const int nk = cdiv_i(cdiv_i(K, BK), LEAD) * LEAD;
     kstep(0, 0, true);
 #pragma unroll
     for (int q = 1; q < LEAD; ++q) kstep(q, q, false);
@@ -371,7 +406,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // The last row of tiles was written by the most recent MFMAs: give them
     // time to finish before any accumulator is read (the tiles of earlier
     // rows are at least FN MFMAs old).
-    static_assert(FN <= 8, "the wait below lists the last row's tiles");
+    static_assert(FN == 4 || FN == 8, "the wait below lists the last row's tiles");
     if constexpr (FN == 8)
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                      : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]),
@@ -379,12 +414,19 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     else
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
                      : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
-    // All loads (the B ring's direct LDS writes included) have landed and
+    // All loads (the B stages' direct LDS writes included) have landed and
     // every wavefront is done with the stages before they are reused for C:
-    // each wavefront stages its block through one B stage.
+    // each wavefront stages its block through one stage of its own.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    store_c_block<T, WM, WN, B_BYTES>(acc, b_stage(wave), lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
+    const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    if constexpr (SB == 4) {
+        store_c_block<T, WM, WN, B_BYTES>(acc, b_stage(wave), lane, row0, col0, M, N, C);
+    } else {
+        constexpr int CW = A_BYTES < B_BYTES ? A_BYTES : B_BYTES;
+        lds_byte* cw = wave < 2 ? a_stage(wave) : b_stage(wave - 2);
+        store_c_block<T, WM, WN, CW>(acc, cw, lane, row0, col0, M, N, C);
+    }
 }
 
 template <typename T>
@@ -395,15 +437,17 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     const T* A = static_cast<const T*>(a.A);
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
-    if (cfg.threads != 256 || cfg.bk != kBK) return hipErrorInvalidValue;
-#define DGR_LAUNCH(BM_, BN_)                                                                              \
-    if (cfg.bm == BM_ && cfg.bn == BN_) {                                                                \
-        hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_>), grid, block, 0, a.stream, A, B, C, a.M,    \
-                           a.N, a.K, cfg.group_m);                                                       \
-        return hipGetLastError();                                                                        \
+    if (cfg.threads != 256) return hipErrorInvalidValue;
+#define DGR_LAUNCH(BM_, BN_, BK_)                                                                        \
+    if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                              \
+        hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_>), grid, block, 0, a.stream, A, B, C, \
+                           a.M, a.N, a.K, cfg.group_m);                                                 \
+        return hipGetLastError();                                                                       \
     }
-    DGR_LAUNCH(256, 256)
-    DGR_LAUNCH(256, 128)
+    DGR_LAUNCH(256, 256, 32)
+    DGR_LAUNCH(256, 128, 32)
+    DGR_LAUNCH(256, 256, 64)
+    DGR_LAUNCH(256, 128, 64)
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;
 }
