@@ -1,16 +1,20 @@
 """Throughput of C = A·B on one MI355X through the library's C ABI.
 
-One step = one gemm_run of the whole workload (default: the square fp16
-4096^3 product, A and B ~ N(0,1)/sqrt(K), fp32 accumulation, fp16 output),
-with inputs already resident in HBM.  W untimed warm-up steps, then exactly K
+One step = one gemm_run (one gemm_run_batched for a batched workload) of the
+whole workload (default: the square fp16 4096^3 product, A and B ~
+N(0,1)/sqrt(K), fp32 accumulation, fp16 output), with inputs already resident
+in HBM.  W untimed warm-up steps, then exactly K
 timed steps bracketed by a device synchronisation on both sides; the kernel
 time is taken with HIP events recorded on the stream the kernels run on.
 
 Prints one JSON line (stdout):
   metric/value/unit   GEMM TFLOP/s = 2MNK / time per step
   roofline            achieved FLOP rate of the GEMM kernel against the MI355X
-                      dense fp16/bf16 MFMA peak (2516.6 TFLOP/s); ``traffic``
-                      is the HBM bytes per launch from the committed rocprofv3
+                      dense fp16/bf16 MFMA peak (2516.6 TFLOP/s); for a
+                      workload whose compulsory bytes put it below the ridge
+                      (peak / 8 TB/s), the achieved compulsory-byte rate
+                      against the 8 TB/s HBM peak instead.  ``traffic`` is the
+                      HBM bytes per launch from the committed rocprofv3
                       counter summary when it was taken on the current kernel
                       source, else null
   cpu_baseline        the CPU oracle (fp64 three loops) timed on a bounded
@@ -60,10 +64,14 @@ def traffic_from_profiles(kernel_cfg: str, workload: str):
 
 
 def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
-    """Time the oracle on a block of leading rows of the same product."""
+    """Time the oracle on a block of leading rows of the same product (of the
+    first product of a batch)."""
     import numpy as np
     import torch
     from oracle import gemm64
+    batch = A.shape[0] if A.ndim == 3 else 1
+    if A.ndim == 3:
+        A, B = A[0], B[0] if B.ndim == 3 else B
     M, K = A.shape
     N = B.shape[1]
     threads = gemm64.default_threads()
@@ -76,8 +84,10 @@ def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
     t, _ = gemm64.time_rows_f64(A64, B64, 0, rows, threads)
     flops = 2.0 * rows * N * K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product ({rows / M:.4f} of the "
-                      f"work), fp64 three-loop oracle, {t:.2f} s on {threads} threads"}
+            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product"
+                      f"{' (the first of the batch of %d)' % batch if batch > 1 else ''} "
+                      f"({rows / M / batch:.4f} of the work), fp64 three-loop oracle, "
+                      f"{t:.2f} s on {threads} threads"}
 
 
 def main(argv=None) -> int:
@@ -103,24 +113,34 @@ def main(argv=None) -> int:
     from dense_gemm_run_amd.inputs import WORKLOADS, workload_operands
 
     w = WORKLOADS[args.workload]
-    log(f"[bench] workload {w.name} M={w.M} N={w.N} K={w.K} {w.dtype}")
+    log(f"[bench] workload {w.name} batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype}")
     A, B = workload_operands(w.name)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     a = A.to(dev)
     b = B.to(dev)
-    c = torch.empty((w.M, w.N), dtype=a.dtype, device=dev)
+    c = torch.empty((w.batch, w.M, w.N) if w.batch > 1 else (w.M, w.N), dtype=a.dtype, device=dev)
     code = dg.dtype_code(a.dtype)
     h = dg.gemm_create()
-    cid = args.config if args.config is not None else dg.gemm_select_config(
-        a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code)
+    strides = (w.M * w.K, w.K * w.N, w.M * w.N)
+    if args.config is not None:
+        cid = args.config
+    elif w.batch > 1:
+        cid = dg.gemm_select_config_batched(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch,
+                                            w.M, w.N, w.K, *strides, code)
+    else:
+        cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code)
     cfg = dg.gemm_config_info(cid)
     log(f"[bench] kernel configuration {cid} {cfg['name']}")
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        dg.gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
-                           cid, stream.cuda_stream)
+        if w.batch > 1:
+            dg.gemm_run_batched_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch, w.M,
+                                       w.N, w.K, *strides, code, cid, stream.cuda_stream)
+        else:
+            dg.gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
+                               cid, stream.cuda_stream)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -152,6 +172,17 @@ def main(argv=None) -> int:
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = traffic_from_profiles(cfg["name"], w.name)
+    esize = a.element_size()
+    compulsory = w.batch * (w.M * w.K + w.K * w.N + w.M * w.N) * esize
+    if w.flops / compulsory < peak * 1e12 / (HBM_GBPS * 1e9):
+        # below the ridge: the compulsory bytes, not the MFMAs, bound the step
+        gbps = compulsory / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
+                    "frac": round(gbps / HBM_GBPS, 4), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma" if w.dtype != "f32" else "alu",
+                    "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4), "traffic": traffic}
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -165,12 +196,10 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+        "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "distribution": w.dist, "seed": w.seed,
                    "kernel_config": cfg["name"], "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu",
-                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "roofline": roofline,
         "wall_s_timed_region": round(wall, 4),
     }
     dg.gemm_destroy(h)

@@ -9,13 +9,16 @@ PyTorch supplies device memory and the stream; nothing else.
 from __future__ import annotations
 
 from ._lib import (GEMM_BF16, GEMM_F16, GEMM_F32, GemmError, gemm_check_args,
-                   gemm_config_count, gemm_config_info, gemm_create, gemm_destroy,
-                   gemm_run, gemm_run_config, gemm_select_config, gemm_tile_of_block,
-                   status_string)
+                   gemm_check_args_batched, gemm_config_count, gemm_config_info, gemm_create,
+                   gemm_destroy, gemm_run, gemm_run_batched, gemm_run_batched_config,
+                   gemm_run_config, gemm_select_config, gemm_select_config_batched,
+                   gemm_tile_of_block, gemm_tile_of_block_batched, status_string)
 
-__all__ = ["gemm", "Gemm", "gemm_create", "gemm_run", "gemm_run_config", "gemm_destroy",
-           "gemm_check_args", "gemm_config_count", "gemm_config_info",
-           "gemm_select_config", "gemm_tile_of_block", "status_string", "GemmError",
+__all__ = ["gemm", "gemm_batched", "Gemm", "gemm_create", "gemm_run", "gemm_run_config",
+           "gemm_run_batched", "gemm_run_batched_config", "gemm_destroy",
+           "gemm_check_args", "gemm_check_args_batched", "gemm_config_count",
+           "gemm_config_info", "gemm_select_config", "gemm_select_config_batched",
+           "gemm_tile_of_block", "gemm_tile_of_block_batched", "status_string", "GemmError",
            "GEMM_F32", "GEMM_F16", "GEMM_BF16", "dtype_code"]
 
 
@@ -76,6 +79,50 @@ class Gemm:
                                 M, N, K, code, config, stream)
         return out
 
+    def batched(self, a, b, out=None, config: int | None = None):
+        """C[i] = a[i] @ b[i].  a is [batch, M, K] or [M, K] (shared by every
+        product), b is [batch, K, N] or [K, N]; at least one is 3-D.  Each
+        matrix must be contiguous row-major; the batch stride may be anything
+        (a 2-D operand has stride 0).  Returns [batch, M, N]."""
+        import torch
+        if a.ndim not in (2, 3) or b.ndim not in (2, 3) or (a.ndim == 2 and b.ndim == 2):
+            raise ValueError("gemm_batched expects [batch, M, K] @ [batch, K, N] "
+                             "(one side may be 2-D and shared)")
+        if a.shape[-1] != b.shape[-2]:
+            raise ValueError("gemm_batched expects [..., M, K] @ [..., K, N]")
+        batch = a.shape[0] if a.ndim == 3 else b.shape[0]
+        if (a.ndim == 3 and a.shape[0] != batch) or (b.ndim == 3 and b.shape[0] != batch):
+            raise ValueError("batch sizes differ")
+        if a.dtype != b.dtype:
+            raise TypeError(f"a and b must share a dtype ({a.dtype} vs {b.dtype})")
+        code = dtype_code(a.dtype)
+        if a.device != self.device or b.device != self.device:
+            raise ValueError(f"inputs must be on {self.device}")
+
+        def matrix_stride(t):
+            # each matrix contiguous row-major; returns the batch stride
+            if t.stride(-1) != 1 or (t.shape[-2] > 1 and t.stride(-2) != t.shape[-1]):
+                raise ValueError("every matrix must be contiguous row-major (no implicit copies)")
+            return 0 if t.ndim == 2 or t.shape[0] == 1 else t.stride(0)
+
+        sa, sb = matrix_stride(a), matrix_stride(b)
+        M, K = a.shape[-2], a.shape[-1]
+        N = b.shape[-1]
+        if out is None:
+            out = torch.empty((batch, M, N), device=self.device, dtype=a.dtype)
+        elif (out.shape != (batch, M, N) or out.dtype != a.dtype or out.device != self.device
+              or not out.is_contiguous()):
+            raise ValueError("out must be a contiguous [batch, M, N] tensor of the input dtype")
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        with torch.cuda.device(self.device):
+            if config is None:
+                gemm_run_batched(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), batch,
+                                 M, N, K, sa, sb, M * N, code, stream)
+            else:
+                gemm_run_batched_config(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                        batch, M, N, K, sa, sb, M * N, code, config, stream)
+        return out
+
 
 _default: dict[int, Gemm] = {}
 
@@ -87,3 +134,13 @@ def gemm(a, b, out=None, config: int | None = None):
     if g is None:
         g = _default[idx] = Gemm(idx)
     return g(a, b, out=out, config=config)
+
+
+def gemm_batched(a, b, out=None, config: int | None = None):
+    """C[i] = a[i] @ b[i] as one launch on a's device and the current stream
+    (see Gemm.batched)."""
+    idx = a.device.index if a.device.index is not None else 0
+    g = _default.get(idx)
+    if g is None:
+        g = _default[idx] = Gemm(idx)
+    return g.batched(a, b, out=out, config=config)

@@ -51,6 +51,16 @@ SIGNATURES = {
     "gemm_tile_of_block": (_I32, [_I32, _I64, _I64, _I64, ctypes.POINTER(_I64),
                                   ctypes.POINTER(_I64)]),
     "gemm_run_config": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _I32, _VP]),
+    "gemm_run_batched": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                _I32, _VP]),
+    "gemm_check_args_batched": (_I32, [_VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                       _I32]),
+    "gemm_select_config_batched": (_I32, [_VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64,
+                                          _I64, _I32]),
+    "gemm_tile_of_block_batched": (_I32, [_I32, _I64, _I64, _I64, _I64, ctypes.POINTER(_I64),
+                                          ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "gemm_run_batched_config": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64,
+                                       _I64, _I32, _I32, _VP]),
 }
 
 _lib = None
@@ -135,3 +145,39 @@ def gemm_tile_of_block(config_id: int, M: int, N: int, block: int) -> tuple[int,
     _check(lib().gemm_tile_of_block(config_id, M, N, block, ctypes.byref(tm), ctypes.byref(tn)),
            "gemm_tile_of_block")
     return tm.value, tn.value
+
+
+def gemm_run_batched(h, A: int, B: int, C: int, batch: int, M: int, N: int, K: int,
+                     stride_a: int, stride_b: int, stride_c: int, dtype: int,
+                     stream: int | None) -> None:
+    _check(lib().gemm_run_batched(h, A, B, C, batch, M, N, K, stride_a, stride_b, stride_c,
+                                  dtype, stream), "gemm_run_batched")
+
+
+def gemm_run_batched_config(h, A: int, B: int, C: int, batch: int, M: int, N: int, K: int,
+                            stride_a: int, stride_b: int, stride_c: int, dtype: int,
+                            config_id: int, stream: int | None) -> None:
+    _check(lib().gemm_run_batched_config(h, A, B, C, batch, M, N, K, stride_a, stride_b,
+                                         stride_c, dtype, config_id, stream),
+           "gemm_run_batched_config")
+
+
+def gemm_check_args_batched(A: int, B: int, C: int, batch: int, M: int, N: int, K: int,
+                            stride_a: int, stride_b: int, stride_c: int, dtype: int) -> int:
+    return lib().gemm_check_args_batched(A, B, C, batch, M, N, K, stride_a, stride_b, stride_c,
+                                         dtype)
+
+
+def gemm_select_config_batched(A: int, B: int, C: int, batch: int, M: int, N: int, K: int,
+                               stride_a: int, stride_b: int, stride_c: int, dtype: int) -> int:
+    return lib().gemm_select_config_batched(A, B, C, batch, M, N, K, stride_a, stride_b,
+                                            stride_c, dtype)
+
+
+def gemm_tile_of_block_batched(config_id: int, M: int, N: int, batch: int,
+                               block: int) -> tuple[int, int, int]:
+    b, tm, tn = _I64(), _I64(), _I64()
+    _check(lib().gemm_tile_of_block_batched(config_id, M, N, batch, block, ctypes.byref(b),
+                                            ctypes.byref(tm), ctypes.byref(tn)),
+           "gemm_tile_of_block_batched")
+    return b.value, tm.value, tn.value

@@ -48,6 +48,23 @@ constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
 inline int64_t elem_bytes(int32_t dtype) { return dtype == kF32 ? 4 : 2; }
 
+// One call's arguments: `batch` products, matrix b of A (B, C) starting
+// b*sa (b*sb, b*sc) elements after A (B, C).  A single product is batch 1.
+struct Problem {
+    const void* A;
+    const void* B;
+    void* C;
+    int64_t M, N, K;
+    int32_t dtype;
+    int64_t batch, sa, sb, sc;
+};
+
+inline Problem single(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int32_t dtype)
+{
+    return Problem{A, B, C, M, N, K, dtype, 1, M * K, K * N, M * N};
+}
+
 inline bool overlaps(const void* p, int64_t pbytes, const void* q, int64_t qbytes)
 {
     if (pbytes <= 0 || qbytes <= 0) return false;
@@ -56,70 +73,86 @@ inline bool overlaps(const void* p, int64_t pbytes, const void* q, int64_t qbyte
     return a0 < b1 && b0 < a1;
 }
 
-gemm_status_t check_args(const void* A, const void* B, const void* C,
-                         int64_t M, int64_t N, int64_t K, int32_t dtype)
+// Elements spanned by `batch` matrices of `elems` elements, `stride` apart
+// (0 when empty); -1 when that does not fit in int64.
+inline int64_t extent(int64_t batch, int64_t elems, int64_t stride)
 {
-    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
-    if (dtype != kF32 && dtype != kF16 && dtype != kBF16) return GEMM_ERR_UNSUPPORTED_DTYPE;
+    if (batch == 0 || elems == 0) return 0;
+    if (batch > 1 && stride > (INT64_MAX - elems) / (batch - 1)) return -1;
+    return (batch - 1) * stride + elems;
+}
+
+gemm_status_t check_args(const Problem& p)
+{
+    if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0 || p.sa < 0 || p.sb < 0 || p.sc < 0)
+        return GEMM_ERR_INVALID_VALUE;
+    if (p.dtype != kF32 && p.dtype != kF16 && p.dtype != kBF16) return GEMM_ERR_UNSUPPORTED_DTYPE;
     const int64_t lim = INT32_MAX;
-    if (M > lim || N > lim || K > lim) return GEMM_ERR_TOO_LARGE;
-    const int64_t s = elem_bytes(dtype);
+    if (p.M > lim || p.N > lim || p.K > lim || p.batch > lim) return GEMM_ERR_TOO_LARGE;
+    const int64_t s = elem_bytes(p.dtype);
     // each matrix must stay below 2^31 bytes (32-bit byte offsets in the kernels);
     // products of two sizes <= 2^31-1 fit in int64
     const int64_t max_elems = ((int64_t)1 << 31) / s;
-    const int64_t a_elems = M * K, b_elems = K * N, c_elems = M * N;
+    const int64_t a_elems = p.M * p.K, b_elems = p.K * p.N, c_elems = p.M * p.N;
     if (a_elems >= max_elems || b_elems >= max_elems || c_elems >= max_elems)
         return GEMM_ERR_TOO_LARGE;
-    if ((a_elems && !A) || (b_elems && !B) || (c_elems && !C)) return GEMM_ERR_INVALID_VALUE;
-    if (overlaps(C, c_elems * s, A, a_elems * s) || overlaps(C, c_elems * s, B, b_elems * s))
+    // the whole grid (at the smallest tile, 64 x 64) must fit a 32-bit id
+    if (((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch > lim) return GEMM_ERR_TOO_LARGE;
+    const int64_t ea = extent(p.batch, a_elems, p.sa), eb = extent(p.batch, b_elems, p.sb),
+                  ec = extent(p.batch, c_elems, p.sc);
+    if (ea < 0 || eb < 0 || ec < 0 || ea > INT64_MAX / s || eb > INT64_MAX / s || ec > INT64_MAX / s)
+        return GEMM_ERR_TOO_LARGE;
+    if ((ea && !p.A) || (eb && !p.B) || (ec && !p.C)) return GEMM_ERR_INVALID_VALUE;
+    if (overlaps(p.C, ec * s, p.A, ea * s) || overlaps(p.C, ec * s, p.B, eb * s))
         return GEMM_ERR_ALIASING;
+    if (p.batch > 1 && c_elems > 0 && p.sc < c_elems) return GEMM_ERR_ALIASING;   // C matrices overlap
     return GEMM_OK;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Whether configuration e can run these (already checked) arguments.
-bool accepts(const Entry& e, const void* A, const void* B, const void* C,
-             int64_t N, int64_t K, int32_t dtype)
+bool accepts(const Entry& e, const Problem& p)
 {
-    if (!((e.cfg.dtype_mask >> dtype) & 1)) return false;
+    if (!((e.cfg.dtype_mask >> p.dtype) & 1)) return false;
     if (e.cfg.needs_vec_align) {
-        const int64_t per16 = 16 / elem_bytes(dtype);
-        if (K % per16 || N % per16) return false;
-        if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
+        const int64_t per16 = 16 / elem_bytes(p.dtype);
+        if (p.K % per16 || p.N % per16) return false;
+        if (!aligned16(p.A) || !aligned16(p.B) || !aligned16(p.C)) return false;
+        if (p.batch > 1 && (p.sa % per16 || p.sb % per16 || p.sc % per16)) return false;
     }
     return true;
 }
 
 // Shape classes.  Small or oddly aligned problems take the generic kernel;
 // aligned fp16/bf16 problems take an MFMA kernel with the largest tile that
-// still gives every CU work.  For 256x256 tiles that is the 16x16x32 kernel
-// (measured 6-9 % faster than the 32x32x16 one at 4096^3 and 8192^3: it runs
-// at a higher clock under the power limit).
-int select(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
-           int32_t dtype)
+// still gives every CU work (counting the tiles of the whole batch).  For
+// 256x256 tiles that is the 16x16x32 kernel (measured 6-9 % faster than the
+// 32x32x16 one at 4096^3 and 8192^3: it runs at a higher clock under the
+// power limit).
+int select(const Problem& p)
 {
-    if (M == 0 || N == 0 || K == 0) return 0;
-    if (dtype == kF32) return 0;
-    if (!accepts(kTable[1], A, B, C, N, K, dtype)) return 0;
-    if (M * N * K < (int64_t)128 * 128 * 128) return 0;
+    if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
+    if (p.dtype == kF32) return 0;
+    if (!accepts(kTable[1], p)) return 0;
+    if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
     // largest tile that still leaves at least one tile per CU (256 CUs)
-    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
     if (t256 >= 256) return 6;
-    const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+    const int64_t t128 = ((p.M + 255) / 256) * ((p.N + 127) / 128) * p.batch;
     if (t128 >= 256) return 2;
     return 3;
 }
 
-gemm_status_t launch(const Entry& e, gemm_handle_t h, const void* A, const void* B, void* C,
-                     int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream)
+gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream)
 {
     if (!h) return GEMM_ERR_INVALID_VALUE;
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return GEMM_ERR_HIP;
     if (cur != h->device) return GEMM_ERR_INVALID_VALUE;
-    if (M == 0 || N == 0) return GEMM_OK;
-    LaunchArgs la{A, B, C, (int)M, (int)N, (int)K, dtype, static_cast<hipStream_t>(stream)};
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return GEMM_OK;
+    LaunchArgs la{p.A, p.B, p.C, (int)p.M, (int)p.N, (int)p.K, p.dtype, static_cast<hipStream_t>(stream),
+                  Batch{(int)p.batch, p.sa, p.sb, p.sc}};
     hipError_t err = hipSuccess;
     switch (e.kind) {
     case kGeneric: err = launch_generic(e.cfg, la); break;
@@ -127,6 +160,23 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const void* A, const void*
     case kMfma16x16: err = launch_mfma16x16(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+gemm_status_t run(gemm_handle_t h, const Problem& p, void* stream)
+{
+    const gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    return launch(kTable[select(p)], h, p, stream);
+}
+
+gemm_status_t run_config(gemm_handle_t h, const Problem& p, int32_t config_id, void* stream)
+{
+    const gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    if (config_id < 0 || config_id >= kTableSize) return GEMM_ERR_INVALID_VALUE;
+    const Entry& e = kTable[config_id];
+    if (!accepts(e, p)) return GEMM_ERR_CONFIG_MISMATCH;
+    return launch(e, h, p, stream);
 }
 
 }  // namespace
@@ -174,7 +224,7 @@ const char* gemm_status_string(int32_t s)
     case GEMM_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "unsupported device (needs a gfx950 GPU)";
     case GEMM_ERR_TOO_LARGE: return "problem too large";
-    case GEMM_ERR_ALIASING: return "C overlaps A or B";
+    case GEMM_ERR_ALIASING: return "C overlaps A, B or another C matrix";
     case GEMM_ERR_HIP: return "HIP runtime error";
     case GEMM_ERR_CONFIG_MISMATCH: return "configuration does not accept these arguments";
     default: return "unknown status";
@@ -184,7 +234,14 @@ const char* gemm_status_string(int32_t s)
 gemm_status_t gemm_check_args(const void* A, const void* B, const void* C,
                               int64_t M, int64_t N, int64_t K, int32_t dtype)
 {
-    return check_args(A, B, C, M, N, K, dtype);
+    return check_args(single(A, B, const_cast<void*>(C), M, N, K, dtype));
+}
+
+gemm_status_t gemm_check_args_batched(const void* A, const void* B, const void* C, int64_t batch,
+                                      int64_t M, int64_t N, int64_t K, int64_t stride_a,
+                                      int64_t stride_b, int64_t stride_c, int32_t dtype)
+{
+    return check_args(Problem{A, B, const_cast<void*>(C), M, N, K, dtype, batch, stride_a, stride_b, stride_c});
 }
 
 int32_t gemm_config_count(void) { return kTableSize; }
@@ -210,44 +267,72 @@ gemm_status_t gemm_config_info(int32_t id, gemm_config_info_t* out)
 int32_t gemm_select_config(const void* A, const void* B, const void* C,
                            int64_t M, int64_t N, int64_t K, int32_t dtype)
 {
-    if (check_args(A, B, C, M, N, K, dtype) != GEMM_OK) return -1;
-    return select(A, B, C, M, N, K, dtype);
+    const Problem p = single(A, B, const_cast<void*>(C), M, N, K, dtype);
+    if (check_args(p) != GEMM_OK) return -1;
+    return select(p);
 }
 
-gemm_status_t gemm_tile_of_block(int32_t id, int64_t M, int64_t N, int64_t block,
-                                 int64_t* tile_m, int64_t* tile_n)
+int32_t gemm_select_config_batched(const void* A, const void* B, const void* C, int64_t batch,
+                                   int64_t M, int64_t N, int64_t K, int64_t stride_a,
+                                   int64_t stride_b, int64_t stride_c, int32_t dtype)
 {
-    if (id < 0 || id >= kTableSize || !tile_m || !tile_n || M <= 0 || N <= 0 ||
-        M > INT32_MAX || N > INT32_MAX)
+    const Problem p{A, B, const_cast<void*>(C), M, N, K, dtype, batch, stride_a, stride_b, stride_c};
+    if (check_args(p) != GEMM_OK) return -1;
+    return select(p);
+}
+
+gemm_status_t gemm_tile_of_block_batched(int32_t id, int64_t M, int64_t N, int64_t batch, int64_t block,
+                                         int64_t* batch_index, int64_t* tile_m, int64_t* tile_n)
+{
+    if (id < 0 || id >= kTableSize || !batch_index || !tile_m || !tile_n || M <= 0 || N <= 0 ||
+        batch <= 0 || M > INT32_MAX || N > INT32_MAX || batch > INT32_MAX)
         return GEMM_ERR_INVALID_VALUE;
     const Config& c = kTable[id].cfg;
     const int tiles_m = cdiv_i((int)M, c.bm), tiles_n = cdiv_i((int)N, c.bn);
-    if (block < 0 || block >= (int64_t)tiles_m * tiles_n) return GEMM_ERR_INVALID_VALUE;
-    int tm, tn;
-    tile_of_block((int)block, tiles_m, tiles_n, c.group_m, c.xcd_remap != 0, tm, tn);
+    if ((int64_t)tiles_m * tiles_n * batch > INT32_MAX) return GEMM_ERR_TOO_LARGE;
+    if (block < 0 || block >= (int64_t)tiles_m * tiles_n * batch) return GEMM_ERR_INVALID_VALUE;
+    int b, tm, tn;
+    tile_of_block((int)block, tiles_m, tiles_n, (int)batch, c.group_m, c.xcd_remap != 0, b, tm, tn);
+    *batch_index = b;
     *tile_m = tm;
     *tile_n = tn;
     return GEMM_OK;
 }
 
+gemm_status_t gemm_tile_of_block(int32_t id, int64_t M, int64_t N, int64_t block,
+                                 int64_t* tile_m, int64_t* tile_n)
+{
+    int64_t b = 0;
+    return gemm_tile_of_block_batched(id, M, N, 1, block, &b, tile_m, tile_n);
+}
+
 gemm_status_t gemm_run(gemm_handle_t h, const void* A, const void* B, void* C,
                        int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream)
 {
-    const gemm_status_t st = check_args(A, B, C, M, N, K, dtype);
-    if (st != GEMM_OK) return st;
-    return launch(kTable[select(A, B, C, M, N, K, dtype)], h, A, B, C, M, N, K, dtype, stream);
+    return run(h, single(A, B, C, M, N, K, dtype), stream);
+}
+
+gemm_status_t gemm_run_batched(gemm_handle_t h, const void* A, const void* B, void* C, int64_t batch,
+                               int64_t M, int64_t N, int64_t K, int64_t stride_a, int64_t stride_b,
+                               int64_t stride_c, int32_t dtype, void* stream)
+{
+    return run(h, Problem{A, B, C, M, N, K, dtype, batch, stride_a, stride_b, stride_c}, stream);
 }
 
 gemm_status_t gemm_run_config(gemm_handle_t h, const void* A, const void* B, void* C,
                               int64_t M, int64_t N, int64_t K, int32_t dtype,
                               int32_t config_id, void* stream)
 {
-    const gemm_status_t st = check_args(A, B, C, M, N, K, dtype);
-    if (st != GEMM_OK) return st;
-    if (config_id < 0 || config_id >= kTableSize) return GEMM_ERR_INVALID_VALUE;
-    const Entry& e = kTable[config_id];
-    if (!accepts(e, A, B, C, N, K, dtype)) return GEMM_ERR_CONFIG_MISMATCH;
-    return launch(e, h, A, B, C, M, N, K, dtype, stream);
+    return run_config(h, single(A, B, C, M, N, K, dtype), config_id, stream);
+}
+
+gemm_status_t gemm_run_batched_config(gemm_handle_t h, const void* A, const void* B, void* C,
+                                      int64_t batch, int64_t M, int64_t N, int64_t K,
+                                      int64_t stride_a, int64_t stride_b, int64_t stride_c,
+                                      int32_t dtype, int32_t config_id, void* stream)
+{
+    return run_config(h, Problem{A, B, C, M, N, K, dtype, batch, stride_a, stride_b, stride_c},
+                      config_id, stream);
 }
 
 }  // extern "C"

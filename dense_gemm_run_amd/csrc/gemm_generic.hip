@@ -44,7 +44,7 @@ __device__ inline int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane
 template <typename T>
 __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
     const T* __restrict__ A, const T* __restrict__ B, T* __restrict__ C,
-    int M, int N, int K, int group_m)
+    int M, int N, int K, int group_m, Batch bt)
 {
     constexpr int BK = 32;
     constexpr int LDK = BK + 8;   // row pitch in elements: 80 bytes, keeps 16-byte alignment
@@ -52,8 +52,11 @@ __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
     __shared__ __attribute__((aligned(16))) T As[kBM * LDK];   // [m][k]
     __shared__ __attribute__((aligned(16))) T Bs[kBN * LDK];   // [n][k]: B tile stored transposed
 
-    int tm, tn;
-    tile_of_block(blockIdx.x, cdiv_i(M, kBM), cdiv_i(N, kBN), group_m, false, tm, tn);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, cdiv_i(M, kBM), cdiv_i(N, kBN), bt.count, group_m, false, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -98,15 +101,18 @@ __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
 // products and sums are fp32.
 __global__ __launch_bounds__(kThreads) void gemm_generic32_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C,
-    int M, int N, int K, int group_m)
+    int M, int N, int K, int group_m, Batch bt)
 {
     constexpr int BK = 16;
     constexpr int LDA = BK + 1;    // odd pitch: the 32 rows a wavefront reads land in 32 banks
     __shared__ float As[kBM * LDA];        // [m][k]
     __shared__ float Bs[BK * kBN];         // [k][n]
 
-    int tm, tn;
-    tile_of_block(blockIdx.x, cdiv_i(M, kBM), cdiv_i(N, kBN), group_m, false, tm, tn);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, cdiv_i(M, kBM), cdiv_i(N, kBN), bt.count, group_m, false, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
     const int m0 = tm * kBM, n0 = tn * kBN;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -146,22 +152,22 @@ __global__ __launch_bounds__(kThreads) void gemm_generic32_kernel(
 hipError_t launch_generic(const Config& cfg, const LaunchArgs& a)
 {
     const int tiles = cdiv_i(a.M, kBM) * cdiv_i(a.N, kBN);
-    const dim3 grid(tiles), block(kThreads);
+    const dim3 grid(tiles * a.batch.count), block(kThreads);
     switch (a.dtype) {
     case kF32:
         hipLaunchKernelGGL(gemm_generic32_kernel, grid, block, 0, a.stream,
                            static_cast<const float*>(a.A), static_cast<const float*>(a.B),
-                           static_cast<float*>(a.C), a.M, a.N, a.K, cfg.group_m);
+                           static_cast<float*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
         break;
     case kF16:
         hipLaunchKernelGGL(gemm_generic16_kernel<_Float16>, grid, block, 0, a.stream,
                            static_cast<const _Float16*>(a.A), static_cast<const _Float16*>(a.B),
-                           static_cast<_Float16*>(a.C), a.M, a.N, a.K, cfg.group_m);
+                           static_cast<_Float16*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
         break;
     case kBF16:
         hipLaunchKernelGGL(gemm_generic16_kernel<__bf16>, grid, block, 0, a.stream,
                            static_cast<const __bf16*>(a.A), static_cast<const __bf16*>(a.B),
-                           static_cast<__bf16*>(a.C), a.M, a.N, a.K, cfg.group_m);
+                           static_cast<__bf16*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
         break;
     default:
         return hipErrorInvalidValue;

@@ -12,28 +12,37 @@ constexpr int kNumXcd = 8;
 
 __host__ __device__ inline int cdiv_i(int a, int b) { return (a + b - 1) / b; }
 
-// Output tile owned by workgroup `bid`.
+// Batch index and output tile owned by workgroup `bid` of a grid of
+// batch * tiles_m * tiles_n workgroups.
 //
 // Step 1 (optional, xcd_remap): turn the hardware id into a logical id so
 // that the workgroups one XCD runs get consecutive logical ids.  Of the
 // first 8*q ids (q = total/8), XCD x runs ids x, x+8, x+16, ...; those become
 // logical ids x*q, x*q+1, ...  The last total%8 ids keep their value.
 //
-// Step 2: the grouped order of the pages (kernels-book chapter "Matrix
+// Step 2: logical id p belongs to batch p / (tiles_m*tiles_n) (the third
+// program axis of notebook "Triton tiled matmul", the exercises), so the
+// consecutive ids of one XCD stay in one or two matrices of the batch.
+//
+// Step 3: the grouped order of the pages (kernels-book chapter "Matrix
 // Multiplication", section "The naive version"; lesson "Matrix
-// multiplication", section "Connect to the real implementation"): logical
-// ids fill a band of group_m tile-rows going down the band first, then one
-// tile-column to the right, so the workgroups that run together share B
-// tiles (and A tiles) in L2.  The last band holds the remaining tile-rows.
-__host__ __device__ inline void tile_of_block(int bid, int tiles_m, int tiles_n, int group_m,
-                                              bool xcd_remap, int& tm, int& tn)
+// multiplication", section "Connect to the real implementation"): within a
+// matrix, ids fill a band of group_m tile-rows going down the band first,
+// then one tile-column to the right, so the workgroups that run together
+// share B tiles (and A tiles) in L2.  The last band holds the remaining
+// tile-rows.
+__host__ __device__ inline void tile_of_block(int bid, int tiles_m, int tiles_n, int batch,
+                                              int group_m, bool xcd_remap, int& b, int& tm, int& tn)
 {
+    const int tiles = tiles_m * tiles_n;
     int p = bid;
     if (xcd_remap) {
-        const int total = tiles_m * tiles_n;
+        const int total = tiles * batch;
         const int q = total / kNumXcd;
         if (bid < q * kNumXcd) p = (bid % kNumXcd) * q + bid / kNumXcd;
     }
+    b = p / tiles;
+    p -= b * tiles;
     const int band_size = group_m * tiles_n;
     const int band = p / band_size;
     const int within = p - band * band_size;
@@ -57,6 +66,13 @@ struct Config {
     const char* name;
 };
 
+// The batch a launch covers: `count` products, matrix b of A (B, C) starting
+// `sa` (`sb`, `sc`) elements after matrix b-1.  count = 1 is a single product.
+struct Batch {
+    int count;
+    long long sa, sb, sc;
+};
+
 struct LaunchArgs {
     const void* A;
     const void* B;
@@ -64,6 +80,7 @@ struct LaunchArgs {
     int M, N, K;
     int dtype;
     hipStream_t stream;
+    Batch batch;
 };
 
 // Kernel launchers; each returns the hipError_t of the launch.

@@ -142,7 +142,7 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
 template <typename T, int BM, int BN, int BK>
 __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const T* A, const T* B, T* C,
-    int M, int N, int K, int group_m)
+    int M, int N, int K, int group_m, Batch bt)
 {
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
@@ -176,8 +176,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     auto b_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
-    int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, true, tm, tn);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int t = threadIdx.x, lane = t & 63;
@@ -433,7 +436,7 @@ template <typename T>
 hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
 {
     const int tiles = cdiv_i(a.M, cfg.bm) * cdiv_i(a.N, cfg.bn);
-    const dim3 grid(tiles), block(256);
+    const dim3 grid(tiles * a.batch.count), block(256);
     const T* A = static_cast<const T*>(a.A);
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
@@ -441,7 +444,7 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
 #define DGR_LAUNCH(BM_, BN_, BK_)                                                                        \
     if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                              \
         hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_>), grid, block, 0, a.stream, A, B, C, \
-                           a.M, a.N, a.K, cfg.group_m);                                                 \
+                           a.M, a.N, a.K, cfg.group_m, a.batch);                                                 \
         return hipGetLastError();                                                                       \
     }
     DGR_LAUNCH(256, 256, 32)

@@ -122,7 +122,7 @@ __device__ __forceinline__ void store_c_block(const f32x16 (&acc)[WM / 32][WN / 
 template <typename T, int BM, int BN, int BK, int WAVES_N>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_mfma32x32_kernel(
     const T* __restrict__ A, const T* __restrict__ B, T* __restrict__ C,
-    int M, int N, int K, int group_m)
+    int M, int N, int K, int group_m, Batch bt)
 {
     typedef typename Op<T>::V8 V8;
     constexpr int NW = 2 * WAVES_N;           // wavefronts: 2 along M, WAVES_N along N
@@ -146,8 +146,11 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_mfma32x32_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
-    int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, true, tm, tn);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
     const int m0 = tm * BM, n0 = tn * BN;
 
     const int t = threadIdx.x, lane = t & 63;
@@ -386,14 +389,14 @@ template <typename T>
 hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
 {
     const int tiles = cdiv_i(a.M, cfg.bm) * cdiv_i(a.N, cfg.bn);
-    const dim3 grid(tiles), block(cfg.threads);
+    const dim3 grid(tiles * a.batch.count), block(cfg.threads);
     const T* A = static_cast<const T*>(a.A);
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
 #define DGR_LAUNCH(BM_, BN_, BK_, WN_)                                                               \
     if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_ && cfg.threads == 128 * WN_) {               \
         hipLaunchKernelGGL((gemm_mfma32x32_kernel<T, BM_, BN_, BK_, WN_>), grid, block, 0, a.stream, A, B, C, \
-                           a.M, a.N, a.K, cfg.group_m);                                            \
+                           a.M, a.N, a.K, cfg.group_m, a.batch);                                            \
         return hipGetLastError();                                                                  \
     }
     DGR_LAUNCH(256, 256, 32, 2)

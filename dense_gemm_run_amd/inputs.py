@@ -22,6 +22,10 @@ before drawing both operands) follows the correctness cell of the notebook
                    in [1, 2) whose low significand bits are all in use, so any
                    shortening of fp32 inputs (a 10- or 7-bit significand)
                    moves the product by far more than 1e-5 relative.
+
+Batched workloads draw the same way with one generator: all of A's matrices
+([batch, M, K], in order), then all of B's ([batch, K, N], or one [K, N] when
+B is shared by every product).
 """
 from __future__ import annotations
 
@@ -43,10 +47,11 @@ class Workload:
     dist: str
     seed: int
     about: str
+    batch: int = 1
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.N * self.K * self.batch
 
 
 # The workloads the product is checked and measured on, with their seeds.
@@ -67,6 +72,10 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              "prefill MLP up projection, 8192 tokens"),
     Workload("bf16_prefill_down_8192x4096x14336", 8192, 4096, 14336, "bf16", "prefill", 7,
              "prefill MLP down projection, 8192 tokens"),
+    Workload("bf16_batched_16x2048x2048x2048", 2048, 2048, 2048, "bf16", "uniform", 8,
+             "16 independent bf16 2048^3 products in one launch", batch=16),
+    Workload("bf16_batched_64x2048x2048x128", 2048, 2048, 128, "bf16", "normal_sqrtk", 9,
+             "attention-score shaped batch: 64 heads of [2048 x 128] @ [128 x 2048]", batch=64),
 ]}
 
 # Order in which the four prefill projections of one layer run.
@@ -106,6 +115,20 @@ def make_operands(M: int, N: int, K: int, dtype: str, dist: str, seed: int):
     return A, B
 
 
+def make_batched_operands(batch: int, M: int, N: int, K: int, dtype: str, dist: str,
+                          seed: int, share_b: bool = False):
+    """(A [batch,M,K], B [batch,K,N] or [K,N] when ``share_b``) as contiguous
+    CPU tensors of ``dtype``."""
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(DTYPES)}")
+    gen = torch.Generator().manual_seed(seed)
+    A = _draw((batch, M, K), dist, K, gen, "A").to(DTYPES[dtype]).contiguous()
+    B = _draw((K, N) if share_b else (batch, K, N), dist, K, gen, "B").to(DTYPES[dtype]).contiguous()
+    return A, B
+
+
 def workload_operands(name: str):
     w = WORKLOADS[name]
+    if w.batch > 1:
+        return make_batched_operands(w.batch, w.M, w.N, w.K, w.dtype, w.dist, w.seed)
     return make_operands(w.M, w.N, w.K, w.dtype, w.dist, w.seed)

@@ -57,7 +57,7 @@ typedef enum gemm_status {
     GEMM_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype is not one of gemm_dtype_t */
     GEMM_ERR_UNSUPPORTED_DEVICE = 3, /* no GPU, or the current device is not gfx950 */
     GEMM_ERR_TOO_LARGE = 4,          /* a dimension > 2^31-1 or a matrix of 2^31 bytes or more */
-    GEMM_ERR_ALIASING = 5,           /* C's bytes overlap A's or B's */
+    GEMM_ERR_ALIASING = 5,           /* C's bytes overlap A's or B's (or, batched, another C matrix) */
     GEMM_ERR_HIP = 6,                /* a HIP runtime call failed */
     GEMM_ERR_CONFIG_MISMATCH = 7     /* forced kernel configuration cannot run these arguments */
 } gemm_status_t;
@@ -86,6 +86,27 @@ gemm_status_t gemm_create(gemm_handle_t* out);
 gemm_status_t gemm_run(gemm_handle_t h, const void* A, const void* B, void* C,
                        int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream);
 
+/* Enqueue C[b] = A[b]·B[b] for b = 0 .. batch-1 on `stream`: the product
+ * above over an outer batch dimension, run as one launch whose workgroups
+ * cover every (batch, tile) pair (notebook "Triton tiled matmul", the
+ * exercises: a third program axis over the batch).
+ *   A, B, C  device pointers to the first matrix of each operand; matrix b
+ *            starts at A + b*stride_a, B + b*stride_b, C + b*stride_c
+ *            elements, and each matrix is row-major as in gemm_run.
+ *   batch    number of products, >= 0 (0: nothing is done).
+ *   strides  in elements, >= 0.  A stride of 0 uses the same matrix for
+ *            every b (one weight matrix B for a batch of activations, say).
+ *   M,N,K, dtype, stream  as in gemm_run, for every matrix of the batch.
+ * Each matrix must stay below 2^31 bytes; strides may be larger.  The C
+ * matrices may not overlap each other (stride_c >= M*N when batch > 1), and
+ * the span of C (from C to the end of matrix batch-1) may not overlap the
+ * span of A or of B: GEMM_ERR_ALIASING.  Other errors and ownership as in
+ * gemm_run; gemm_run(h, A, B, C, M, N, K, ...) is the batch = 1 case. */
+gemm_status_t gemm_run_batched(gemm_handle_t h, const void* A, const void* B, void* C,
+                               int64_t batch, int64_t M, int64_t N, int64_t K,
+                               int64_t stride_a, int64_t stride_b, int64_t stride_c,
+                               int32_t dtype, void* stream);
+
 /* Release a handle.  NULL is accepted and ignored.  No work may still be
  * using the handle (enqueued work does not refer to it). */
 gemm_status_t gemm_destroy(gemm_handle_t h);
@@ -103,6 +124,11 @@ const char* gemm_status_string(int32_t status);
 gemm_status_t gemm_check_args(const void* A, const void* B, const void* C,
                               int64_t M, int64_t N, int64_t K, int32_t dtype);
 
+/* As gemm_check_args, for gemm_run_batched's arguments. */
+gemm_status_t gemm_check_args_batched(const void* A, const void* B, const void* C, int64_t batch,
+                                      int64_t M, int64_t N, int64_t K, int64_t stride_a,
+                                      int64_t stride_b, int64_t stride_c, int32_t dtype);
+
 /* Kernel configurations.  A configuration fixes the output tile BM x BN, the
  * K-step BK, the band height GROUP_M of the tile order, the workgroup size,
  * and which element types and alignments it accepts. */
@@ -112,7 +138,7 @@ typedef struct gemm_config_info {
     int32_t group_m;           /* tile-rows walked before moving right */
     int32_t threads;           /* workgroup size */
     int32_t dtype_mask;        /* bit d set: accepts gemm_dtype_t d */
-    int32_t needs_vec_align;   /* 1: needs 16-byte aligned A, B, C and K, N multiples of 16 bytes / element size */
+    int32_t needs_vec_align;   /* 1: needs 16-byte aligned A, B, C and K, N (and batch strides) multiples of 16 bytes / element size */
     int32_t xcd_remap;         /* 1: workgroup ids are remapped so each XCD gets a compact block of tiles */
     char name[40];
 } gemm_config_info_t;
@@ -128,11 +154,23 @@ gemm_status_t gemm_config_info(int32_t id, gemm_config_info_t* out);
 int32_t gemm_select_config(const void* A, const void* B, const void* C,
                            int64_t M, int64_t N, int64_t K, int32_t dtype);
 
+/* As gemm_select_config, for gemm_run_batched's arguments (the shape class
+ * counts the tiles of the whole batch). */
+int32_t gemm_select_config_batched(const void* A, const void* B, const void* C, int64_t batch,
+                                   int64_t M, int64_t N, int64_t K, int64_t stride_a,
+                                   int64_t stride_b, int64_t stride_c, int32_t dtype);
+
 /* Output tile (tile_m, tile_n) computed by workgroup `block` of
  * configuration `id` for an M x N output, evaluated on the host with the
  * same function the kernels use.  Used to test the tile order. */
 gemm_status_t gemm_tile_of_block(int32_t id, int64_t M, int64_t N, int64_t block,
                                  int64_t* tile_m, int64_t* tile_n);
+
+/* Batch index and output tile of workgroup `block` of configuration `id`
+ * in a batched launch of `batch` M x N outputs (block < batch * tiles). */
+gemm_status_t gemm_tile_of_block_batched(int32_t id, int64_t M, int64_t N, int64_t batch,
+                                         int64_t block, int64_t* batch_index, int64_t* tile_m,
+                                         int64_t* tile_n);
 
 /* ---------------------------------------------------------------------------
  * gemm_run with a forced configuration, for measuring the alternatives.
@@ -142,6 +180,13 @@ gemm_status_t gemm_tile_of_block(int32_t id, int64_t M, int64_t N, int64_t block
 gemm_status_t gemm_run_config(gemm_handle_t h, const void* A, const void* B, void* C,
                               int64_t M, int64_t N, int64_t K, int32_t dtype,
                               int32_t config_id, void* stream);
+
+/* gemm_run_batched with a forced configuration (alignment also covers the
+ * strides: with batch > 1 they must be multiples of 16 bytes). */
+gemm_status_t gemm_run_batched_config(gemm_handle_t h, const void* A, const void* B, void* C,
+                                      int64_t batch, int64_t M, int64_t N, int64_t K,
+                                      int64_t stride_a, int64_t stride_b, int64_t stride_c,
+                                      int32_t dtype, int32_t config_id, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,13 @@ Functions and what pins them (tests/test_oracle_pins.py):
 ``gemm_points_f64``  the same sum for chosen (row, col) pairs, for sampling a
                      product too large to form whole.  Pinned against
                      ``gemm_f64`` entries and against exact integer sums.
+``gemm_batched_f64`` C[i] = A[i]·B[i] for every i of an outer batch
+                     dimension (notebook "Triton tiled matmul", the
+                     exercises: the same product with a third program axis
+                     over the batch), one ``gemm_f64`` per matrix; a 2-D
+                     operand is the same matrix for every i.  Pinned against
+                     numpy's batched matmul on integer inputs (exact), with
+                     each operand shared in turn and with an empty batch.
 ``round_to_bits``    fp64 -> fp16 / bf16 / fp32 round-to-nearest-even (the
                      reading of the final cast in "Connect to the real
                      implementation" and the Triton kernel of chapter "Fast
@@ -148,6 +155,25 @@ def gemm_points_f64(A, B, rows, cols, nthreads: int | None = None) -> np.ndarray
     return out
 
 
+def gemm_batched_f64(A, B, nthreads: int | None = None) -> np.ndarray:
+    """C[i] = A[i] @ B[i] for i in range(batch): A is [batch, M, K] or [M, K]
+    (shared by every i), B is [batch, K, N] or [K, N]."""
+    A = _f64(A)
+    B = _f64(B)
+    if A.ndim not in (2, 3) or B.ndim not in (2, 3) or (A.ndim == 2 and B.ndim == 2):
+        raise ValueError("batched oracle expects [batch, M, K] @ [batch, K, N]")
+    if A.shape[-1] != B.shape[-2]:
+        raise ValueError("batched oracle expects [..., M, K] @ [..., K, N]")
+    batch = A.shape[0] if A.ndim == 3 else B.shape[0]
+    if (A.ndim == 3 and A.shape[0] != batch) or (B.ndim == 3 and B.shape[0] != batch):
+        raise ValueError("batch sizes differ")
+    M, N = A.shape[-2], B.shape[-1]
+    C = np.empty((batch, M, N), dtype=np.float64)
+    for i in range(batch):
+        C[i] = gemm_f64(A[i] if A.ndim == 3 else A, B[i] if B.ndim == 3 else B, nthreads)
+    return C
+
+
 _ROUNDERS = {
     "f16": ("oracle_round_f16", np.uint16, ctypes.c_uint16),
     "bf16": ("oracle_round_bf16", np.uint16, ctypes.c_uint16),
@@ -184,4 +210,10 @@ def reference(A, B, dtype: str, nthreads: int | None = None):
     product rounded once to ``dtype``.  Returns (rounded values as fp64, the
     unrounded fp64 product)."""
     C64 = gemm_f64(A, B, nthreads)
+    return bits_to_f64(round_to_bits(C64, dtype), dtype), C64
+
+
+def reference_batched(A, B, dtype: str, nthreads: int | None = None):
+    """As ``reference``, for the batched product."""
+    C64 = gemm_batched_f64(A, B, nthreads)
     return bits_to_f64(round_to_bits(C64, dtype), dtype), C64

@@ -126,7 +126,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(8))
+@pytest.mark.parametrize("cid", range(10))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -161,3 +161,70 @@ def test_xcd_remap_gives_each_xcd_a_compact_block():
         cols = {t[1] for t in tiles}
         # a compact block touches far fewer rows+columns than a scattered one
         assert len(rows) * len(cols) <= 2 * len(tiles), (x, len(rows), len(cols))
+
+
+# ---------------------------------------------------------------- batched
+@pytest.mark.parametrize("args,want", [
+    # (A, B, C, batch, M, N, K, sa, sb, sc, dtype)
+    ((A, B, C, 3, 4, 5, 6, 24, 30, 20, 1), OK),
+    ((A, B, C, 0, 4, 5, 6, 24, 30, 20, 1), OK),            # empty batch
+    ((0, 0, 0, 0, 4, 5, 6, 24, 30, 20, 1), OK),            # ... with no data at all
+    ((A, B, C, 3, 4, 5, 6, 0, 0, 20, 1), OK),              # A and B shared by every product
+    ((A, B, C, -1, 4, 5, 6, 24, 30, 20, 1), INVALID),
+    ((A, B, C, 3, 4, 5, 6, -24, 30, 20, 1), INVALID),
+    ((A, B, C, 3, 4, 5, 6, 24, 30, -20, 1), INVALID),
+    ((A, B, C, 3, 4, 5, 6, 24, 30, 20, 5), BADTYPE),
+    ((0, B, C, 3, 4, 5, 6, 24, 30, 20, 1), INVALID),
+    ((A, B, C, 3, 4, 5, 6, 24, 30, 19, 1), ALIAS),         # C matrices overlap each other
+    ((A, B, C, 1, 4, 5, 6, 24, 30, 0, 1), OK),             # ... unless there is one
+    ((A, B, A + 2 * 48, 3, 4, 5, 6, 48, 30, 20, 1), ALIAS),  # C inside A's span, between matrices
+    ((A, B, C, 2 ** 31, 4, 5, 6, 24, 30, 20, 1), TOOBIG),
+    ((A, B, C, 2, 1 << 16, 1 << 14, 1, 0, 0, 1 << 30, 1), TOOBIG),   # one C matrix of 2^31 bytes
+    ((A, B, C, 3, 4, 5, 6, 1 << 62, 30, 20, 1), TOOBIG),   # A's span overflows
+    ((A, B, C, 1 << 20, 4096, 4096, 8, 0, 0, 1 << 24, 1), TOOBIG),   # grid of 2^32 workgroups
+])
+def test_check_args_batched(args, want):
+    assert dg.gemm_check_args_batched(*args) == want
+
+
+def test_single_calls_are_the_batch_of_one():
+    for args in [(A, B, C, 4, 5, 6, 1), (A, B, A + 4, 4, 5, 6, 1), (0, B, C, 4, 5, 6, 1),
+                 (A, B, C, 4096, 4096, 4096, 1)]:
+        a, b, c, M, N, K, dt = args
+        assert dg.gemm_check_args(*args) == dg.gemm_check_args_batched(a, b, c, 1, M, N, K,
+                                                                       M * K, K * N, M * N, dt)
+    Cb = C + (1 << 32)
+    for M, N, K, dt in [(4096, 4096, 4096, 1), (1000, 1000, 1000, 1), (64, 64, 64, 0)]:
+        Bb = A + (M * K * 2 + 4096) // 16 * 16
+        assert dg.gemm_select_config(A, Bb, Cb, M, N, K, dt) == dg.gemm_select_config_batched(
+            A, Bb, Cb, 1, M, N, K, M * K, K * N, M * N, dt)
+    for cid in (0, 6):
+        for b in range(0, 64, 7):
+            assert dg.gemm_tile_of_block(cid, 4096, 2048, b) == \
+                dg.gemm_tile_of_block_batched(cid, 4096, 2048, 1, b)[1:]
+
+
+def test_batched_selection_counts_the_whole_batch():
+    Cb = C + (1 << 34)
+    M = N = K = 2048          # 64 tiles of 256 x 256: too few alone, enough 16 at a time
+    Bb = A + (1 << 33)
+    alone = dg.gemm_select_config_batched(A, Bb, Cb, 1, M, N, K, M * K, K * N, M * N, 2)
+    many = dg.gemm_select_config_batched(A, Bb, Cb, 16, M, N, K, M * K, K * N, M * N, 2)
+    assert dg.gemm_config_info(alone)["bm"] * dg.gemm_config_info(alone)["bn"] < 256 * 256
+    assert (dg.gemm_config_info(many)["bm"], dg.gemm_config_info(many)["bn"]) == (256, 256)
+    # strides that break 16-byte alignment rule out the vector-load kernels
+    odd = dg.gemm_select_config_batched(A, Bb, Cb, 16, M, N, K, M * K + 1, K * N, M * N, 2)
+    assert dg.gemm_config_info(odd)["needs_vec_align"] == 0
+
+
+@pytest.mark.parametrize("cid", [0, 2, 6, 9])
+def test_batched_tile_order_is_a_bijection(cid):
+    info = dg.gemm_config_info(cid)
+    for M, N, batch in [(300, 700, 3), (1024, 1024, 8), (100, 100, 17)]:
+        tm_n, tn_n = -(-M // info["bm"]), -(-N // info["bn"])
+        total = tm_n * tn_n * batch
+        seen = [dg.gemm_tile_of_block_batched(cid, M, N, batch, b) for b in range(total)]
+        assert sorted(seen) == [(i, r, c) for i in range(batch) for r in range(tm_n)
+                                for c in range(tn_n)]
+        with pytest.raises(dg.GemmError):
+            dg.gemm_tile_of_block_batched(cid, M, N, batch, total)

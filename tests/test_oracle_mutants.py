@@ -75,3 +75,25 @@ def test_unmutated_copy_passes():
                                     "swapped_output"])
 def test_mutant_is_caught(mutant):
     assert not pins_pass(lambda A, B: three_loop(A, B, mutant))
+
+
+# ---------------------------------------------------------------- batched
+def batched_loop(A, B, mutant=None):
+    """A copy of the batched oracle's loop over matrices, with a planted
+    mistake."""
+    batch = A.shape[0]
+    out = []
+    for i in range(batch):
+        ia = 0 if mutant == "first_a_everywhere" else i
+        ib = (i + 1) % batch if mutant == "shifted_b" else i
+        out.append(three_loop(A[ia], B[ib]))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("mutant", [None, "first_a_everywhere", "shifted_b"])
+def test_batched_pin_catches(mutant):
+    rng = np.random.default_rng(3)
+    A = rng.integers(-4, 5, (4, 3, 5)).astype(np.float64)
+    B = rng.integers(-4, 5, (4, 5, 2)).astype(np.float64)
+    ok = np.array_equal(batched_loop(A, B, mutant), np.matmul(A, B))
+    assert ok == (mutant is None)

@@ -251,6 +251,39 @@ def test_points_rows_and_threads_agree():
     assert t >= 0 and np.array_equal(blk, full[3:7])
 
 
+def _int_batch(shape, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(-4, 5, shape).astype(np.float64)
+
+
+@pytest.mark.parametrize("a_shared,b_shared", [(False, False), (True, False), (False, True)])
+def test_batched_against_numpy_batched_matmul(a_shared, b_shared):
+    # integer entries with small K: every sum is exact in fp64 and in numpy
+    batch, M, N, K = 5, 7, 9, 33
+    A = _int_batch((M, K) if a_shared else (batch, M, K), 11)
+    B = _int_batch((K, N) if b_shared else (batch, K, N), 12)
+    got = gemm64.gemm_batched_f64(A, B)
+    assert got.shape == (batch, M, N)
+    assert np.array_equal(got, np.matmul(A, B))
+    # matrix i of the result depends on matrix i of each 3-D operand only
+    if not a_shared:
+        A2 = A.copy()
+        A2[2] += 1
+        d = gemm64.gemm_batched_f64(A2, B) != got
+        assert d[2].any() and not d[[0, 1, 3, 4]].any()
+
+
+def test_batched_degenerate_and_rounded():
+    assert gemm64.gemm_batched_f64(np.zeros((0, 3, 4)), np.zeros((0, 4, 5))).shape == (0, 3, 5)
+    A = _int_batch((3, 4, 6), 13)
+    B = _int_batch((3, 6, 2), 14)
+    ref, raw = gemm64.reference_batched(A, B, "bf16")
+    assert np.array_equal(raw, np.matmul(A, B))
+    assert np.array_equal(ref, raw)          # |sums| <= 96: exact in bf16
+    with pytest.raises(ValueError):
+        gemm64.gemm_batched_f64(np.zeros((2, 3, 4)), np.zeros((3, 4, 5)))
+
+
 def test_degenerate_sizes():
     assert gemm64.gemm_f64(np.zeros((0, 4)), np.zeros((4, 3))).shape == (0, 3)
     assert gemm64.gemm_f64(np.zeros((2, 4)), np.zeros((4, 0))).shape == (2, 0)
