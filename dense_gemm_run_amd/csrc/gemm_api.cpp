@@ -21,7 +21,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3 };
 
 struct Entry {
     Config cfg;
@@ -43,6 +43,10 @@ const Entry kTable[] = {
     {{7, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x128x32"}, kMfma16x16},
     {{8, 256, 256, 64, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x64"}, kMfma16x16},
     {{9, 256, 128, 64, 4, 256, 0x6, 1, 1, "mfma16x16_256x128x64"}, kMfma16x16},
+    // matrix-vector: bm = rows per workgroup, bn = the most columns of B, bk =
+    // the K elements one wavefront instruction covers
+    {{10, 8, 4, 512, 1, 256, 0x6, 1, 0, "gemv_8rows"}, kGemv},
+    {{11, 16, 4, 512, 1, 256, 0x6, 1, 0, "gemv_16rows"}, kGemv},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -115,6 +119,14 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 bool accepts(const Entry& e, const Problem& p)
 {
     if (!((e.cfg.dtype_mask >> p.dtype) & 1)) return false;
+    if (e.kind == kGemv) {
+        // 16-byte pieces of A rows and of B's 8-row runs; C is stored element-wise
+        const int64_t per16 = 16 / elem_bytes(p.dtype);
+        if (p.N < 1 || p.N > e.cfg.bn || p.K % per16) return false;
+        if (!aligned16(p.A) || !aligned16(p.B)) return false;
+        if (p.batch > 1 && (p.sa % per16 || p.sb % per16)) return false;
+        return true;
+    }
     if (e.cfg.needs_vec_align) {
         const int64_t per16 = 16 / elem_bytes(p.dtype);
         if (p.K % per16 || p.N % per16) return false;
@@ -134,6 +146,9 @@ int select(const Problem& p)
 {
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
     if (p.dtype == kF32) return 0;
+    // a few columns: stream A (chapter "Fast matrix multiplication", GEMV);
+    // 16 rows per workgroup once that still leaves several workgroups per CU
+    if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
     if (!accepts(kTable[1], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
     // largest tile that still leaves at least one tile per CU (256 CUs)
@@ -158,6 +173,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
     case kGeneric: err = launch_generic(e.cfg, la); break;
     case kMfma32x32: err = launch_mfma32x32(e.cfg, la); break;
     case kMfma16x16: err = launch_mfma16x16(e.cfg, la); break;
+    case kGemv: err = launch_gemv(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -87,5 +87,6 @@ struct LaunchArgs {
 hipError_t launch_generic(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_mfma32x32(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_mfma16x16(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_gemv(const Config& cfg, const LaunchArgs& a);
 
 }  // namespace dgr

@@ -16,6 +16,9 @@ before drawing both operands) follows the correctness cell of the notebook
 ``prefill``        activations A ~ N(0, 1), weights B [K, N] ~ N(0, 0.02)
                    (``0.02 * randn``), as a transformer projection with
                    tokens along M.
+``decode``         weights A [M, K] ~ N(0, 0.02) and activations B [K, N] ~
+                   N(0, 1): the matrix-vector product y = W·x of one decode
+                   step (few columns N).
 ``integers``       integers drawn uniformly from [-4, 4] for A and B (every
                    product and partial sum is then an exact small integer).
 ``fp32_fine``      values 1 + j·2^-23 with j uniform in [0, 2^23): fp32 numbers
@@ -76,6 +79,12 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              "16 independent bf16 2048^3 products in one launch", batch=16),
     Workload("bf16_batched_64x2048x2048x128", 2048, 2048, 128, "bf16", "normal_sqrtk", 9,
              "attention-score shaped batch: 64 heads of [2048 x 128] @ [128 x 2048]", batch=64),
+    Workload("bf16_gemv_14336x1x4096", 14336, 1, 4096, "bf16", "decode", 10,
+             "decode GEMV y = W x, W [14336, 4096] (MLP up, one token)"),
+    Workload("bf16_gemv_4096x1x14336", 4096, 1, 14336, "bf16", "decode", 11,
+             "decode GEMV y = W x, W [4096, 14336] (MLP down, one token)"),
+    Workload("bf16_gemv_12288x4x4096", 12288, 4, 4096, "bf16", "decode", 12,
+             "decode GEMV with 4 vectors, W [12288, 4096] (QKV, 4 tokens)"),
 ]}
 
 # Order in which the four prefill projections of one layer run.
@@ -97,6 +106,9 @@ def _draw(shape, dist: str, K: int, gen: torch.Generator, role: str) -> torch.Te
     if dist == "prefill":
         z = torch.randn(shape, generator=gen, dtype=torch.float32)
         return z if role == "A" else 0.02 * z
+    if dist == "decode":
+        z = torch.randn(shape, generator=gen, dtype=torch.float32)
+        return 0.02 * z if role == "A" else z
     if dist == "integers":
         return torch.randint(-4, 5, shape, generator=gen).to(torch.float32)
     if dist == "fp32_fine":

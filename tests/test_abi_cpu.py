@@ -126,7 +126,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(10))
+@pytest.mark.parametrize("cid", range(12))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -228,3 +228,18 @@ def test_batched_tile_order_is_a_bijection(cid):
                                 for c in range(tn_n)]
         with pytest.raises(dg.GemmError):
             dg.gemm_tile_of_block_batched(cid, M, N, batch, total)
+
+
+def test_few_columns_select_the_vector_kernel():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    for M, N, K in [(14336, 1, 4096), (4096, 1, 14336), (12288, 4, 4096), (1, 1, 8), (300, 3, 1040)]:
+        cid = dg.gemm_select_config(A, Bb, Cb, M, N, K, 2)
+        info = dg.gemm_config_info(cid)
+        assert info["name"].startswith("gemv") and N <= info["bn"], (M, N, K, info["name"])
+    # five columns, K not a multiple of 8, a misaligned B, or fp32: not the vector kernel
+    for args in [(A, Bb, Cb, 4096, 5, 4096, 2), (A, Bb, Cb, 4096, 1, 4090, 2),
+                 (A, Bb + 2, Cb, 4096, 1, 4096, 2), (A, Bb, Cb, 4096, 1, 4096, 0)]:
+        assert not dg.gemm_config_info(dg.gemm_select_config(*args))["name"].startswith("gemv")
+    # C needs no alignment for it
+    assert dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb + 2, 4096, 1, 4096, 2))["name"].startswith("gemv")

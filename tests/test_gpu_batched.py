@@ -12,6 +12,7 @@ import torch
 import dense_gemm_run_amd as dg
 from dense_gemm_run_amd.inputs import WORKLOADS, make_batched_operands, workload_operands
 from oracle import gemm64, tolerance
+from test_gpu_parity import accepts
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +48,8 @@ def test_batched_every_configuration(dtype, shape):
     for cid in range(dg.gemm_config_count()):
         info = dg.gemm_config_info(cid)
         if not (info["dtype_mask"] >> DT_CODE[dtype]) & 1:
+            continue
+        if not accepts(cid, a, b, M, N, K, batch):
             continue
         note(f"[batched] config {cid} {info['name']} {dtype} {shape}")
         c = dg.gemm_batched(a, b, config=cid)

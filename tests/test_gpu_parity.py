@@ -20,6 +20,7 @@ from oracle import gemm64, tolerance
 pytestmark = pytest.mark.gpu
 
 DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+DT_CODE_T = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 
 def note(msg):
@@ -33,6 +34,24 @@ def run_gpu(A, B, config=None, out=None):
     c = dg.gemm(a, b, out=out, config=config)
     torch.cuda.synchronize()
     return c
+
+
+def accepts(cid, a, b, M, N, K, batch=1):
+    """Whether configuration cid runs these arguments (a forced configuration
+    that does not, e.g. a matrix-vector one for many columns, is refused with
+    GEMM_ERR_CONFIG_MISMATCH before any launch)."""
+    h = dg.gemm_create()
+    try:
+        c = torch.empty((batch, M, N) if batch > 1 else (M, N), dtype=a.dtype, device=a.device)
+        st = dg._lib.lib().gemm_run_batched_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                                  batch, M, N, K, M * K if a.ndim == 3 else 0,
+                                                  K * N if b.ndim == 3 else 0, M * N,
+                                                  DT_CODE_T[a.dtype], cid, None)
+        torch.cuda.synchronize()
+        assert st in (0, 7), st        # ran, or refused as a mismatch
+        return st == 0
+    finally:
+        dg.gemm_destroy(h)
 
 
 def check_full(A, B, dtype, C_gpu, use_floor=True):
@@ -203,6 +222,8 @@ def test_every_configuration_that_accepts_the_arguments(dtype, shape):
     for cid in range(dg.gemm_config_count()):
         info = dg.gemm_config_info(cid)
         if not (info["dtype_mask"] >> DT_CODE[dtype]) & 1:
+            continue
+        if not accepts(cid, a, b, M, N, K):
             continue
         note(f"[parity] config {cid} {info['name']} {dtype} {shape}")
         c = dg.gemm(a, b, config=cid)
