@@ -19,6 +19,12 @@ Prints one JSON line (stdout):
                       source, else null
   cpu_baseline        the CPU oracle (fp64 three loops) timed on a bounded
                       block of rows of the same product on this host's cores
+
+``--sweep`` instead times every kernel configuration that accepts each shape
+of a size sweep (square 512^3 .. 8192^3, few-row products against the HBM
+roofline, the prefill projections) and prints one JSON line per (shape,
+configuration) plus the configuration gemm_run picks; it is the measurement
+behind the shape-class table.
 """
 from __future__ import annotations
 
@@ -90,6 +96,79 @@ def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
                       f"{t:.2f} s on {threads} threads"}
 
 
+SWEEP_SQUARE = [512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192]
+SWEEP_SKINNY = [(m, 4096, 4096) for m in (16, 32, 64, 128, 256, 512)] + \
+               [(m, 14336, 4096) for m in (16, 64, 256)]
+SWEEP_PREFILL = [(8192, 12288, 4096), (8192, 4096, 4096), (8192, 14336, 4096), (8192, 4096, 14336)]
+
+
+def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
+    """Time every accepting configuration on the sweep shapes (bf16 or fp16,
+    N(0,1)/sqrt(K) inputs, seed 100); with ``vendor``, also torch.matmul on the
+    same operands (the vendor library, for context)."""
+    import torch
+    import dense_gemm_run_amd as dg
+    from dense_gemm_run_amd import _lib
+    from dense_gemm_run_amd.inputs import make_operands
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    h = dg.gemm_create()
+    code = {"f16": 1, "bf16": 2}[dtype]
+    shapes = [(n, n, n) for n in SWEEP_SQUARE] + SWEEP_SKINNY + SWEEP_PREFILL
+    stream = torch.cuda.current_stream(dev)
+    for M, N, K in shapes:
+        A, B = make_operands(M, N, K, dtype, "normal_sqrtk", 100)
+        a, b = A.to(dev), B.to(dev)
+        c = torch.empty((M, N), dtype=a.dtype, device=dev)
+        chosen = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, code)
+        flops = 2.0 * M * N * K
+        compulsory = (M * K + K * N + M * N) * a.element_size()
+        for cid in range(dg.gemm_config_count()):
+            def run():
+                return _lib.lib().gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N,
+                                                  K, code, cid, stream.cuda_stream)
+            if run() != 0:          # this configuration refuses the shape
+                continue
+            for _ in range(3):
+                run()
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(iters):
+                run()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / iters
+            print(json.dumps({"M": M, "N": N, "K": K, "dtype": dtype, "config": cid,
+                              "name": dg.gemm_config_info(cid)["name"], "selected": cid == chosen,
+                              "us": round(ms * 1e3, 2),
+                              "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                              "compulsory_gbps": round(compulsory / (ms * 1e-3) / 1e9, 1)}),
+                  flush=True)
+        if vendor:
+            for _ in range(3):
+                torch.matmul(a, b)
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ev0.record(stream)
+            for _ in range(iters):
+                torch.matmul(a, b)
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            ms = ev0.elapsed_time(ev1) / iters
+            print(json.dumps({"M": M, "N": N, "K": K, "dtype": dtype, "config": None,
+                              "name": "torch.matmul", "selected": False, "us": round(ms * 1e3, 2),
+                              "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                              "compulsory_gbps": round(compulsory / (ms * 1e-3) / 1e9, 1)}),
+                  flush=True)
+        del a, b, c
+    dg.gemm_destroy(h)
+    return 0
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
@@ -100,6 +179,11 @@ def main(argv=None) -> int:
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for scaling HBM counters)")
+    p.add_argument("--sweep", choices=["f16", "bf16"], default=None,
+                   help="time every configuration on the shape sweep instead")
+    p.add_argument("--sweep-iters", type=int, default=20)
+    p.add_argument("--sweep-vendor", action="store_true",
+                   help="with --sweep: also time torch.matmul (context)")
     args = p.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -107,6 +191,9 @@ def main(argv=None) -> int:
               "(the product shards by output rows or columns with no exchange; see DESIGN.md)",
               file=sys.stderr)
         return 2
+
+    if args.sweep:
+        return sweep(args.sweep, args.sweep_iters, args.sweep_vendor)
 
     import torch
     import dense_gemm_run_amd as dg

@@ -47,6 +47,7 @@ const Entry kTable[] = {
     // the K elements one wavefront instruction covers
     {{10, 8, 4, 512, 1, 256, 0x6, 1, 0, "gemv_8rows"}, kGemv},
     {{11, 16, 4, 512, 1, 256, 0x6, 1, 0, "gemv_16rows"}, kGemv},
+    {{12, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_128x128x32"}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -136,27 +137,27 @@ bool accepts(const Entry& e, const Problem& p)
     return true;
 }
 
-// Shape classes.  Small or oddly aligned problems take the generic kernel;
-// aligned fp16/bf16 problems take an MFMA kernel with the largest tile that
-// still gives every CU work (counting the tiles of the whole batch).  For
-// 256x256 tiles that is the 16x16x32 kernel (measured 6-9 % faster than the
-// 32x32x16 one at 4096^3 and 8192^3: it runs at a higher clock under the
-// power limit).
+// Shape classes (measured with bench.py --sweep over square 512^3 .. 8192^3,
+// few-row products and the prefill projections):
+//  * N <= 4: the matrix-vector kernel (it streams A at HBM bandwidth);
+//  * small (M*N*K*batch < 128^3), fp32 or unaligned: the generic kernel;
+//  * at least 128 output tiles of 256 x 256 over the whole batch (half the
+//    256 CUs or more): the 16x16x32 kernel at 256 x 256.  At one wave of
+//    tiles it is 30-40 % faster than the 128 x 128 tile, and even at 144
+//    tiles (3072^3) it matches it;
+//  * otherwise the 16x16x32 kernel at 128 x 128, which gives 4x the tiles
+//    (2048^3: 842 TFLOP/s against 383 at 256 x 256).
+// The 32x32x16 configurations and the 256 x 128 tiles were never the fastest
+// in the sweep and stay available through gemm_run_config.
 int select(const Problem& p)
 {
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
     if (p.dtype == kF32) return 0;
-    // a few columns: stream A (chapter "Fast matrix multiplication", GEMV);
-    // 16 rows per workgroup once that still leaves several workgroups per CU
     if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
-    if (!accepts(kTable[1], p)) return 0;
+    if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
-    // largest tile that still leaves at least one tile per CU (256 CUs)
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    if (t256 >= 256) return 6;
-    const int64_t t128 = ((p.M + 255) / 256) * ((p.N + 127) / 128) * p.batch;
-    if (t128 >= 256) return 2;
-    return 3;
+    return t256 >= 128 ? 6 : 12;
 }
 
 gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream)

@@ -8,7 +8,7 @@
 // with these differences:
 //
 //  * Math: 4 wavefronts in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs
-//    as 16x16 MFMA tiles.  Per unit of work the 16x16x32 instruction moves
+//    as 16x16 MFMA tiles (BM x BN = 256 x 256, 256 x 128 or 128 x 128).  Per unit of work the 16x16x32 instruction moves
 //    half the accumulator data of the 32x32x16 one; under MI355X's power
 //    limit this runs at a higher clock for the same issue rate.
 //  * The MFMAs are written as inline assembly with the accumulator operand
@@ -451,6 +451,7 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     DGR_LAUNCH(256, 128, 32)
     DGR_LAUNCH(256, 256, 64)
     DGR_LAUNCH(256, 128, 64)
+    DGR_LAUNCH(128, 128, 32)
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;
 }

@@ -38,7 +38,8 @@ def kernels(tmp_path_factory):
         if m:
             end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
             found[m.group(1)] = (int(m.group(2)), int(m.group(3)), int(m.group(4)), lines[i:end])
-    assert len(found) == 8, sorted(found)   # {f16, bf16} x {256x256, 256x128} x {32, 64}
+    # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32)
+    assert len(found) == 10, sorted(found)
     return found
 
 
