@@ -10,7 +10,8 @@ time is taken with HIP events recorded on the stream the kernels run on.
 Prints one JSON line (stdout):
   metric/value/unit   GEMM TFLOP/s = 2MNK / time per step
   roofline            achieved FLOP rate of the GEMM kernel against the MI355X
-                      dense fp16/bf16 MFMA peak (2516.6 TFLOP/s); for a
+                      dense MFMA peak of the input type (fp16/bf16 2516.6,
+                      fp8 5033.2 TFLOP/s); for a
                       workload whose compulsory bytes put it below the ridge
                       (peak / 8 TB/s), the achieved compulsory-byte rate
                       against the 8 TB/s HBM peak instead.  ``traffic`` is the
@@ -39,7 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s (2MNK/t) at 4096³ fp16/bf16 on 1 GPU; % of MFMA dense peak"
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}   # MI355X dense, published
+# MI355X dense peaks, published (fp8: twice the fp16/bf16 rate)
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3, "fp8_e4m3": 5033.2, "fp8_e5m2": 5033.2}
 HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "f16_4096x4096x4096"
 
@@ -81,8 +83,14 @@ def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
     M, K = A.shape
     N = B.shape[1]
     threads = gemm64.default_threads()
-    A64 = np.ascontiguousarray(A.to(torch.float64).numpy())
-    B64 = np.ascontiguousarray(B.to(torch.float64).numpy())
+    fmt = {torch.float8_e4m3fn: "e4m3", torch.float8_e5m2: "e5m2"}.get(A.dtype)
+    if fmt:                          # 8-bit inputs: the oracle's own decode
+        from oracle import fp8
+        A64 = np.ascontiguousarray(fp8.decode(fp8._bits(A), fmt))
+        B64 = np.ascontiguousarray(fp8.decode(fp8._bits(B), fmt))
+    else:
+        A64 = np.ascontiguousarray(A.to(torch.float64).numpy())
+        B64 = np.ascontiguousarray(B.to(torch.float64).numpy())
     probe_rows = max(1, min(M, threads))
     t_probe, _ = gemm64.time_rows_f64(A64, B64, 0, probe_rows, threads)
     rows = int(min(M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
@@ -206,7 +214,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     a = A.to(dev)
     b = B.to(dev)
-    c = torch.empty((w.batch, w.M, w.N) if w.batch > 1 else (w.M, w.N), dtype=a.dtype, device=dev)
+    c = torch.empty((w.batch, w.M, w.N) if w.batch > 1 else (w.M, w.N), dtype=dg.out_dtype(a.dtype),
+                    device=dev)
     code = dg.dtype_code(a.dtype)
     h = dg.gemm_create()
     strides = (w.M * w.K, w.K * w.N, w.M * w.N)
@@ -259,8 +268,7 @@ def main(argv=None) -> int:
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = traffic_from_profiles(cfg["name"], w.name)
-    esize = a.element_size()
-    compulsory = w.batch * (w.M * w.K + w.K * w.N + w.M * w.N) * esize
+    compulsory = w.batch * ((w.M * w.K + w.K * w.N) * a.element_size() + w.M * w.N * c.element_size())
     if w.flops / compulsory < peak * 1e12 / (HBM_GBPS * 1e9):
         # below the ridge: the compulsory bytes, not the MFMAs, bound the step
         gbps = compulsory / (ms * 1e-3) / 1e9

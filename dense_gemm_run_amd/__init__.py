@@ -3,12 +3,13 @@
 ``gemm(a, b)`` takes two row-major CUDA/ROCm tensors of one dtype (fp32, fp16
 or bf16) and returns C = a @ b of that dtype, computed by the library's HIP
 kernels on the current stream (fp32 accumulation, round-to-nearest-even
-output).  The C-ABI functions are re-exported under their C names.
+output).  8-bit inputs (``torch.float8_e4m3fn`` or ``torch.float8_e5m2``,
+the OCP formats) give a bf16 C.  The C-ABI functions are re-exported under their C names.
 PyTorch supplies device memory and the stream; nothing else.
 """
 from __future__ import annotations
 
-from ._lib import (GEMM_BF16, GEMM_F16, GEMM_F32, GemmError, gemm_check_args,
+from ._lib import (GEMM_BF16, GEMM_F16, GEMM_F32, GEMM_FP8_E4M3, GEMM_FP8_E5M2, GemmError, gemm_check_args,
                    gemm_check_args_batched, gemm_config_count, gemm_config_info, gemm_create,
                    gemm_destroy, gemm_run, gemm_run_batched, gemm_run_batched_config,
                    gemm_run_config, gemm_select_config, gemm_select_config_batched,
@@ -19,15 +20,25 @@ __all__ = ["gemm", "gemm_batched", "Gemm", "gemm_create", "gemm_run", "gemm_run_
            "gemm_check_args", "gemm_check_args_batched", "gemm_config_count",
            "gemm_config_info", "gemm_select_config", "gemm_select_config_batched",
            "gemm_tile_of_block", "gemm_tile_of_block_batched", "status_string", "GemmError",
-           "GEMM_F32", "GEMM_F16", "GEMM_BF16", "dtype_code"]
+           "GEMM_F32", "GEMM_F16", "GEMM_BF16", "GEMM_FP8_E4M3", "GEMM_FP8_E5M2",
+           "dtype_code", "out_dtype"]
 
 
 def dtype_code(dt) -> int:
     import torch
-    codes = {torch.float32: GEMM_F32, torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16}
+    codes = {torch.float32: GEMM_F32, torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16,
+             torch.float8_e4m3fn: GEMM_FP8_E4M3, torch.float8_e5m2: GEMM_FP8_E5M2}
     if dt not in codes:
-        raise TypeError(f"dtype must be float32, float16 or bfloat16, got {dt}")
+        raise TypeError("dtype must be float32, float16, bfloat16, float8_e4m3fn or "
+                        f"float8_e5m2, got {dt}")
     return codes[dt]
+
+
+def out_dtype(dt):
+    """dtype of C for inputs of dtype ``dt`` (bf16 for the 8-bit formats)."""
+    import torch
+    dtype_code(dt)
+    return torch.bfloat16 if dt in (torch.float8_e4m3fn, torch.float8_e5m2) else dt
 
 
 class Gemm:
@@ -64,11 +75,12 @@ class Gemm:
             raise ValueError("inputs must be contiguous row-major (no implicit copies)")
         M, K = a.shape
         N = b.shape[1]
+        odt = out_dtype(a.dtype)
         if out is None:
-            out = torch.empty((M, N), device=self.device, dtype=a.dtype)
-        elif (out.shape != (M, N) or out.dtype != a.dtype or out.device != self.device
+            out = torch.empty((M, N), device=self.device, dtype=odt)
+        elif (out.shape != (M, N) or out.dtype != odt or out.device != self.device
               or not out.is_contiguous()):
-            raise ValueError("out must be a contiguous [M, N] tensor of the input dtype")
+            raise ValueError(f"out must be a contiguous [M, N] tensor of dtype {odt}")
         stream = torch.cuda.current_stream(self.device).cuda_stream
         with torch.cuda.device(self.device):
             if config is None:
@@ -108,11 +120,12 @@ class Gemm:
         sa, sb = matrix_stride(a), matrix_stride(b)
         M, K = a.shape[-2], a.shape[-1]
         N = b.shape[-1]
+        odt = out_dtype(a.dtype)
         if out is None:
-            out = torch.empty((batch, M, N), device=self.device, dtype=a.dtype)
-        elif (out.shape != (batch, M, N) or out.dtype != a.dtype or out.device != self.device
+            out = torch.empty((batch, M, N), device=self.device, dtype=odt)
+        elif (out.shape != (batch, M, N) or out.dtype != odt or out.device != self.device
               or not out.is_contiguous()):
-            raise ValueError("out must be a contiguous [batch, M, N] tensor of the input dtype")
+            raise ValueError(f"out must be a contiguous [batch, M, N] tensor of dtype {odt}")
         stream = torch.cuda.current_stream(self.device).cuda_stream
         with torch.cuda.device(self.device):
             if config is None:

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdense_gemm_run_amd.so")
 
-GEMM_F32, GEMM_F16, GEMM_BF16 = 0, 1, 2
+GEMM_F32, GEMM_F16, GEMM_BF16, GEMM_FP8_E4M3, GEMM_FP8_E5M2 = 0, 1, 2, 3, 4
 
 STATUS = {
     0: "GEMM_OK",

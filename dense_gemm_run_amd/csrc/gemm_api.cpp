@@ -21,7 +21,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4 };
 
 struct Entry {
     Config cfg;
@@ -29,11 +29,11 @@ struct Entry {
 };
 
 // Configuration table.  Entry 0 accepts everything and is the fallback.
-// The MFMA entries need 16-byte aligned A, B, C and K, N multiples of 8
-// elements (so every 16-byte global access lies wholly inside or wholly
-// outside a row).
+// The MFMA entries need 16-byte aligned A, B, C and K, N multiples of 16
+// bytes of their matrices' rows (so every 16-byte global access lies wholly
+// inside or wholly outside a row).
 const Entry kTable[] = {
-    {{0, 64, 64, 32, 8, 256, 0x7, 0, 0, "generic_64x64"}, kGeneric},
+    {{0, 64, 64, 32, 8, 256, 0x1f, 0, 0, "generic_64x64"}, kGeneric},
     {{1, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma32x32_256x256x32"}, kMfma32x32},
     {{2, 256, 128, 32, 4, 256, 0x6, 1, 1, "mfma32x32_256x128x32"}, kMfma32x32},
     {{3, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma32x32_128x128x32"}, kMfma32x32},
@@ -48,10 +48,16 @@ const Entry kTable[] = {
     {{10, 8, 4, 512, 1, 256, 0x6, 1, 0, "gemv_8rows"}, kGemv},
     {{11, 16, 4, 512, 1, 256, 0x6, 1, 0, "gemv_16rows"}, kGemv},
     {{12, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_128x128x32"}, kMfma16x16},
+    // 8-bit inputs (E4M3, E5M2), bf16 output; bk in elements (= bytes)
+    {{13, 256, 256, 64, 4, 256, 0x18, 1, 1, "fp8_256x256x64"}, kFp8},
+    {{14, 256, 256, 128, 4, 256, 0x18, 1, 1, "fp8_256x256x128"}, kFp8},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
-inline int64_t elem_bytes(int32_t dtype) { return dtype == kF32 ? 4 : 2; }
+// Bytes per element of A and B, and of C (8-bit inputs give a bf16 C).
+inline int64_t in_bytes(int32_t dtype) { return dtype == kF32 ? 4 : (dtype == kF16 || dtype == kBF16) ? 2 : 1; }
+inline int64_t out_bytes(int32_t dtype) { return dtype == kF32 ? 4 : 2; }
+inline bool valid_dtype(int32_t d) { return d >= kF32 && d <= kFP8E5M2; }
 
 // One call's arguments: `batch` products, matrix b of A (B, C) starting
 // b*sa (b*sb, b*sc) elements after A (B, C).  A single product is batch 1.
@@ -91,24 +97,24 @@ gemm_status_t check_args(const Problem& p)
 {
     if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0 || p.sa < 0 || p.sb < 0 || p.sc < 0)
         return GEMM_ERR_INVALID_VALUE;
-    if (p.dtype != kF32 && p.dtype != kF16 && p.dtype != kBF16) return GEMM_ERR_UNSUPPORTED_DTYPE;
+    if (!valid_dtype(p.dtype)) return GEMM_ERR_UNSUPPORTED_DTYPE;
     const int64_t lim = INT32_MAX;
     if (p.M > lim || p.N > lim || p.K > lim || p.batch > lim) return GEMM_ERR_TOO_LARGE;
-    const int64_t s = elem_bytes(p.dtype);
+    const int64_t si = in_bytes(p.dtype), so = out_bytes(p.dtype);
     // each matrix must stay below 2^31 bytes (32-bit byte offsets in the kernels);
     // products of two sizes <= 2^31-1 fit in int64
-    const int64_t max_elems = ((int64_t)1 << 31) / s;
     const int64_t a_elems = p.M * p.K, b_elems = p.K * p.N, c_elems = p.M * p.N;
-    if (a_elems >= max_elems || b_elems >= max_elems || c_elems >= max_elems)
+    const int64_t two31 = (int64_t)1 << 31;
+    if (a_elems >= two31 / si || b_elems >= two31 / si || c_elems >= two31 / so)
         return GEMM_ERR_TOO_LARGE;
     // the whole grid (at the smallest tile, 64 x 64) must fit a 32-bit id
     if (((p.M + 63) / 64) * ((p.N + 63) / 64) * p.batch > lim) return GEMM_ERR_TOO_LARGE;
     const int64_t ea = extent(p.batch, a_elems, p.sa), eb = extent(p.batch, b_elems, p.sb),
                   ec = extent(p.batch, c_elems, p.sc);
-    if (ea < 0 || eb < 0 || ec < 0 || ea > INT64_MAX / s || eb > INT64_MAX / s || ec > INT64_MAX / s)
+    if (ea < 0 || eb < 0 || ec < 0 || ea > INT64_MAX / si || eb > INT64_MAX / si || ec > INT64_MAX / so)
         return GEMM_ERR_TOO_LARGE;
     if ((ea && !p.A) || (eb && !p.B) || (ec && !p.C)) return GEMM_ERR_INVALID_VALUE;
-    if (overlaps(p.C, ec * s, p.A, ea * s) || overlaps(p.C, ec * s, p.B, eb * s))
+    if (overlaps(p.C, ec * so, p.A, ea * si) || overlaps(p.C, ec * so, p.B, eb * si))
         return GEMM_ERR_ALIASING;
     if (p.batch > 1 && c_elems > 0 && p.sc < c_elems) return GEMM_ERR_ALIASING;   // C matrices overlap
     return GEMM_OK;
@@ -122,17 +128,18 @@ bool accepts(const Entry& e, const Problem& p)
     if (!((e.cfg.dtype_mask >> p.dtype) & 1)) return false;
     if (e.kind == kGemv) {
         // 16-byte pieces of A rows and of B's 8-row runs; C is stored element-wise
-        const int64_t per16 = 16 / elem_bytes(p.dtype);
+        const int64_t per16 = 16 / in_bytes(p.dtype);
         if (p.N < 1 || p.N > e.cfg.bn || p.K % per16) return false;
         if (!aligned16(p.A) || !aligned16(p.B)) return false;
         if (p.batch > 1 && (p.sa % per16 || p.sb % per16)) return false;
         return true;
     }
     if (e.cfg.needs_vec_align) {
-        const int64_t per16 = 16 / elem_bytes(p.dtype);
-        if (p.K % per16 || p.N % per16) return false;
+        // elements per 16 bytes of A and B rows, and of C rows
+        const int64_t pi = 16 / in_bytes(p.dtype), po = 16 / out_bytes(p.dtype);
+        if (p.K % pi || p.N % pi || p.N % po) return false;
         if (!aligned16(p.A) || !aligned16(p.B) || !aligned16(p.C)) return false;
-        if (p.batch > 1 && (p.sa % per16 || p.sb % per16 || p.sc % per16)) return false;
+        if (p.batch > 1 && (p.sa % pi || p.sb % pi || p.sc % po)) return false;
     }
     return true;
 }
@@ -153,6 +160,10 @@ int select(const Problem& p)
 {
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
     if (p.dtype == kF32) return 0;
+    if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
+        if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
+        return 13;
+    }
     if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
     if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
@@ -175,6 +186,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
     case kMfma32x32: err = launch_mfma32x32(e.cfg, la); break;
     case kMfma16x16: err = launch_mfma16x16(e.cfg, la); break;
     case kGemv: err = launch_gemv(e.cfg, la); break;
+    case kFp8: err = launch_fp8(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -52,4 +52,59 @@ template <> __device__ __forceinline__ unsigned pack2<__bf16>(float a, float b)
     return __builtin_bit_cast(unsigned, v);
 }
 
+// Epilogue of the 32x32 MFMA kernels: one wavefront's WM x WN block of fp32
+// accumulators (lane l holds row 32*bi + l%32, columns 32*bj + 8g + 4*(l/32)
+// .. +3 of tile (bi, bj) in registers 4g..4g+3) is rounded to the output type
+// (round to nearest even) and written to C at (row0, col0) through the
+// wavefront's own LDS region `cw` of CW_BYTES: RP rows at a time are staged
+// there and read back as whole row segments for 16-byte stores, skipping
+// rows >= M and columns >= N.  The caller makes sure no other use of `cw` is
+// in flight.
+template <typename T, int WM, int WN, int CW_BYTES = WM * WN * 2>
+__device__ __forceinline__ void store_c_block_32x32(const f32x16 (&acc)[WM / 32][WN / 32], lds_byte* cw,
+                                                    int lane, int row0, int col0, int M, int N, T* C)
+{
+    constexpr int FN = WN / 32;
+    constexpr int RP = CW_BYTES / (WN * 2);   // rows per pass
+    static_assert(RP % 32 == 0 && WM % RP == 0, "passes must hold whole tile rows");
+    // Row-major in LDS with 16-byte pieces swizzled: piece p of row r sits at
+    // p ^ (r % PR) and its two 8-byte halves are swapped when (r / PR) is
+    // odd, so the 8-byte writes of 32 lanes (32 rows, one piece-half each)
+    // land on distinct banks.
+    constexpr int PR = WN / 8;                    // 16-byte pieces per C row
+    const int q = lane % PR;
+    const int col = col0 + q * 8;
+#pragma unroll
+    for (int pass = 0; pass < WM / RP; ++pass) {
+        if (pass) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // previous pass read back
+#pragma unroll
+        for (int bi = pass * RP / 32; bi < (pass + 1) * RP / 32; ++bi) {
+            const int r = 32 * bi + (lane & 31) - pass * RP;
+#pragma unroll
+            for (int bj = 0; bj < FN; ++bj) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int p = (4 * bj + g) ^ (r & (PR - 1));
+                    const int h = (lane >> 5) ^ ((r / PR) & 1);
+                    u32x2 v;
+                    v[0] = pack2<T>(acc[bi][bj][4 * g + 0], acc[bi][bj][4 * g + 1]);
+                    v[1] = pack2<T>(acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]);
+                    *(u32x2 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16 + h * 8) = v;
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's LDS writes done
+        // Read back whole row segments: lane -> row it*(64/PR) + lane/PR, piece lane%PR.
+#pragma unroll 4
+        for (int it = 0; it < RP * PR / 64; ++it) {
+            const int r = it * (64 / PR) + lane / PR;
+            const int p = q ^ (r & (PR - 1));
+            u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
+            if ((r / PR) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
+            const int row = row0 + pass * RP + r;
+            if (row < M && col < N) *(u32x4*)(C + (size_t)row * N + col) = v;
+        }
+    }
+}
+
 }  // namespace dgr

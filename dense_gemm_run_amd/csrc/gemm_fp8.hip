@@ -1,0 +1,371 @@
+// MFMA kernel for 8-bit floating-point inputs (OCP FP8: E4M3 or E5M2, both
+// operands of one format) with fp32 accumulation and a bf16 result: the FP8
+// input path of notebook "Triton tiled matmul" (the exercises: FP8 inputs,
+// the accumulator stays FP32, compared against FP16).  It is built on
+// v_mfma_f32_32x32x64_f8f6f4, which takes 32 one-byte values of each operand
+// per lane and forms every product exactly (two 4-bit significands) before
+// the fp32 sums.  Rows must be 16-byte aligned: K and N multiples of 16, A,
+// B and C 16-byte aligned.
+//
+// The structure is that of the 16x16x32 kernel (the tiled loop of
+// kernels-book chapter "Matrix Multiplication", section "Tiles": one
+// workgroup per 256 x 256 output tile, fp32 accumulators that live across
+// the whole K walk), with one-byte elements:
+//
+//  * Math: 4 wavefronts in a 2 x 2 grid, each owning 128 x 128 outputs as
+//    4 x 4 tiles of 32 x 32 (the 256 accumulator registers of a lane).  A
+//    64-deep K-slice is one MFMA per tile; a K-step of BK = 64 or 128 is one
+//    or two K-slices.  The MFMAs are inline assembly with the accumulator
+//    tied to the destination (and source C = 0 on the first K-slice), which
+//    also fixes their order against the memory instructions around them.
+//  * Operands: lane l of a tile's A fragment holds row l%32 and the 32
+//    bytes k = 32*(l/32) .. +31 of the K-slice; lane l of the B fragment
+//    holds column l%32 and the same 32 k.  The MFMA is given the B fragment
+//    first, so it computes the transposed tile and each lane ends with 4
+//    consecutive columns of one row (the layout the 32x32 epilogue takes).
+//  * Staging: A goes through registers (LEAD slots, K-step it+LEAD loaded
+//    during K-step it and written to one of two A stages during K-step
+//    it+LEAD-1); B goes global -> LDS directly into a ring of SB stages.
+//    16-byte pieces at or past K, rows past M and columns past N read zeros
+//    (the zero padding of chapter "Matrix Multiplication", section "The real
+//    tiled loop").
+//  * LDS layout: A [256][BK] with 16-byte pieces XOR-swizzled by (row/2) %
+//    (BK/16): each 16-lane group of a fragment read takes one piece of 16
+//    consecutive rows, the read that measured free of bank conflicts in the
+//    16-bit kernel.  B [BK][256] with piece p of row k stored at
+//    p ^ 2*(k%8): the 8-bit transpose read of a half-wavefront covers 8
+//    consecutive rows and one 32-byte column pair of each, and the swizzle
+//    puts those 8 pairs in 8 different 32-byte bank groups.
+//  * One barrier per K-step, half a K-slice before its end; the loads and
+//    LDS traffic of a K-step are spread over its MFMAs.
+//  * Epilogue: fp32 -> bf16 (round to nearest even), staged through LDS and
+//    written as whole row segments, skipping rows >= M and columns >= N.
+#include "gemm_internal.h"
+#include "gemm_device.h"
+
+namespace dgr {
+namespace {
+
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// c (+)= b-fragment x a-fragment over one 64-deep K-slice.  FMT 0: both
+// operands E4M3 (the instruction's default); FMT 1: both E5M2.
+template <int FMT> struct MfmaFp8;
+template <> struct MfmaFp8<0> {
+    static __device__ __forceinline__ void acc(f32x16& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+    }
+    static __device__ __forceinline__ void first(f32x16& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0" : "=a"(c) : "v"(b), "v"(a));
+    }
+};
+template <> struct MfmaFp8<1> {
+    static __device__ __forceinline__ void acc(f32x16& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(c) : "v"(b), "v"(a));
+    }
+    static __device__ __forceinline__ void first(f32x16& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0 cbsz:1 blgp:1" : "=a"(c) : "v"(b), "v"(a));
+    }
+};
+
+template <int BK> __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & (BK / 16 - 1); }
+__device__ __forceinline__ int swz_b(int k) { return 2 * (k & 7); }
+
+template <int FMT, int BK>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
+    const unsigned char* A, const unsigned char* B, __bf16* C,
+    int M, int N, int K, int group_m, Batch bt)
+{
+    constexpr int BM = 256, BN = 256;
+    constexpr int NW = 4;                        // wavefronts, 2 x 2
+    constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
+    constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 tiles per wavefront
+    constexpr int NT = FM * FN;                  // MFMAs per wavefront per 64-deep K-slice
+    constexpr int NS = BK / 64;                  // K-slices per K-step
+    constexpr int XS = NS * NT;                  // MFMAs per wavefront per K-step
+    constexpr int LEAD = 256 / BK;               // A register slots (K-steps loaded ahead)
+    constexpr int SB = BK == 64 ? 4 : 2;         // B stages (K-steps loaded ahead)
+    constexpr int ROW_A = BK;                    // bytes per A tile row
+    constexpr int PA = BK / 16;                  // 16-byte pieces per A row
+    constexpr int A_BYTES = BM * ROW_A;
+    constexpr int ROW_B = BN;
+    constexpr int B_BYTES = BK * ROW_B;
+    constexpr int A_LOADS = A_BYTES / 1024 / NW; // 16-byte-per-lane loads per wavefront
+    constexpr int B_LOADS = B_BYTES / 1024 / NW;
+    constexpr int LOADS = A_LOADS + B_LOADS;     // vector-memory instructions per K-step
+    constexpr int NR = FM + FN;                  // operand fragments per K-slice
+    constexpr int BAR = XS - NT / 2;             // MFMAs of a K-step before its barrier
+    static_assert(BK == 64 || BK == 128, "K-step");
+    static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
+    static_assert((SB - 1) * B_BYTES < 65536, "LDS immediate offsets");
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb2[SB > 2 ? B_BYTES : 1], sb3[SB > 2 ? B_BYTES : 1];
+    auto a_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sa0 : sa1); };
+    auto b_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+
+    const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K);
+
+    // ---- global load geometry (byte offsets; one element is one byte)
+    // A: load j fills 1 KB = 1024/ROW_A tile rows; lane -> row +lane/PA,
+    //    physical piece lane%PA holding logical piece p ^ swz_a(row).
+    unsigned a_voff[A_LOADS];
+    int a_kp[A_LOADS];
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+        const int row = (1024 / ROW_A) * (wave * A_LOADS + j) + lane / PA;
+        const int piece = (lane % PA) ^ swz_a<BK>(row);
+        a_voff[j] = (m0 + row) < M ? (unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 16u : kOOB;
+        a_kp[j] = piece * 16;
+    }
+    // B: load j fills 4 tile rows; lane -> row k = (1024*(wave*B_LOADS+j) +
+    //    16*lane) / 256, physical piece lane%16 holding logical piece
+    //    p ^ swz_b(k), i.e. columns n0 + 16*p .. +15 (kOOB past N), relative
+    //    to a buffer that starts at row k0 and ends at row min(K, k0 + BK).
+    unsigned b_voff[B_LOADS];
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+        const int byte = 1024 * (wave * B_LOADS + j) + lane * 16;
+        const int k = byte / ROW_B;
+        const int piece = ((byte % ROW_B) / 16) ^ swz_b(k);
+        const int col = n0 + piece * 16;
+        b_voff[j] = col < N ? (unsigned)k * (unsigned)N + (unsigned)col : kOOB;
+    }
+
+    u32x4 stg[LEAD][A_LOADS];
+    auto load_a = [&](int slot, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0, 0));
+    };
+    auto store_a = [&](int st, int slot, int j) __attribute__((always_inline)) {
+        lds_byte* p = a_stage(st) + (wave * A_LOADS + j) * 1024 + lane * 16;
+        *(u32x4 __attribute__((address_space(3)))*)p = stg[slot][j];
+    };
+    auto load_b = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const int krem = K - k0;
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
+        const __amdgpu_buffer_rsrc_t rbk =
+            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N);
+        const unsigned off = b_voff[j];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rbk, (void __attribute__((address_space(3)))*)(b_stage(st) + (wave * B_LOADS + j) * 1024), 16,
+            off, 0, 0, 0);
+    };
+
+    // ---- operand read addresses within a stage
+    // A fragment (K-slice sl, tile bi): row wm*WM + 32*bi + lane%32, logical
+    // pieces 4*sl + 2*(lane/32) and the next (32 bytes); the swizzle depends
+    // only on lane%32.
+    int a_rd[NS][2];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            a_rd[sl][h] = (wm * WM + (lane & 31)) * ROW_A +
+                          (((4 * sl + 2 * (lane >> 5) + h) ^ swz_a<BK>(lane & 31)) * 16);
+    // B fragment (tile bj) via four 8-bit transpose reads h = 0..3: in 16-lane
+    // group G = lane/16, lane 2r+q points at K row 32*(G/2) + 8h + r (+64 per
+    // K-slice), bytes 8q .. 8q+7 of the 16 columns wn*WN + 32*bj + 16*(G%2)
+    // .. +15; lane i of the group receives column i over those 8 rows, which
+    // are bytes 8h .. 8h+7 of its 32-byte operand.  The swizzle 2*(k%8) is
+    // 2r for every h and K-slice.
+    int b_rd[FN];
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) {
+        const int G = lane >> 4, r = (lane & 15) >> 1, q = lane & 1;
+        const int piece = (wn * WN + 32 * bj + 16 * (G & 1)) / 16;
+        b_rd[bj] = (32 * (G >> 1) + r) * ROW_B + ((piece ^ swz_b(r)) * 16) + 8 * q;
+    }
+    auto read_a = [&](int st, int sl, int bi) __attribute__((always_inline)) -> u32x8 {
+        const lds_byte* base = a_stage(st) + bi * 32 * ROW_A;
+        const u32x4 lo = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[sl][0]);
+        const u32x4 hi = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[sl][1]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto read_b = [&](int st, int sl, int bj) __attribute__((always_inline)) -> u32x8 {
+        const lds_byte* p = b_stage(st) + b_rd[bj] + sl * 64 * ROW_B;
+        i32x2 h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            h[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 __attribute__((address_space(3)))*)(p + 8 * i * ROW_B));
+        const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3));
+        const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    f32x16 acc[FM][FN];
+    u32x8 fa[2][FM], fb[2][FN];   // two operand register sets, alternating by K-slice
+    auto read_frag = [&](int set, int sta, int stb, int sl, int o) __attribute__((always_inline)) {
+        if (o < FN)
+            fb[set][o] = read_b(stb, sl, o);
+        else
+            fa[set][o - FN] = read_a(sta, sl, o - FN);
+    };
+
+    // ---- software pipeline.  Group it = [A loads of K-step it+LEAD (before
+    // the step's barrier), B loads of K-step it+SB (after it)]; the prologue
+    // issues groups -max(LEAD, SB) .. -1 (the parts that exist).  When K-step
+    // it waits for its B loads of K-step it+1 (the end of group it+1-SB),
+    // groups it+2-SB .. it-1 and the A loads of group it were issued after
+    // them: at most (SB-2)*LOADS + A_LOADS loads may still be in flight.
+#pragma unroll
+    for (int g = -LEAD; g < 0; ++g) {
+        if (g + LEAD >= 0)
+#pragma unroll
+            for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * BK, j);
+        if (g + SB >= 0)
+#pragma unroll
+            for (int j = 0; j < B_LOADS; ++j) load_b(g + SB, (g + SB) * BK, j);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 1) * LOADS));   // group -SB (B of K-step 0) landed
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int o = 0; o < NR; ++o) read_frag(0, 0, 0, 0, o);
+
+    // One K-step (q = it % LEAD, a literal): MFMAs 0 .. BAR-1 interleaved
+    // with the operand reads of the next K-slice of this step, the A writes of
+    // K-step it+1 and the A loads of K-step it+LEAD; the counted wait for
+    // this wavefront's B loads of K-step it+1 and the barrier; MFMAs BAR ..
+    // XS-1 interleaved with the B loads of K-step it+SB (into the stage every
+    // wavefront finished reading before the barrier) and the operand reads of
+    // K-slice 0 of K-step it+1.  n operations spread over `span` MFMAs: the
+    // ones issued after MFMA number pos are op_lo(pos) .. op_lo(pos+1)-1.
+    auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
+
+    auto kslice = [&](const int q, int it, const int sl, const bool first) __attribute__((always_inline)) {
+        const int sta = q & 1, stb = q % SB, set = (q * NS + sl) & 1;
+        constexpr int NOPS1 = 2 * A_LOADS;
+        constexpr int NOPS2 = B_LOADS + NR;
+        auto mfma = [&](int xx) __attribute__((always_inline)) {
+            if (first && sl == 0)
+                MfmaFp8<FMT>::first(acc[xx / FN][xx % FN], fb[set][xx % FN], fa[set][xx / FN]);
+            else
+                MfmaFp8<FMT>::acc(acc[xx / FN][xx % FN], fb[set][xx % FN], fa[set][xx / FN]);
+        };
+        const int lo = sl * NT, hi = lo + NT;
+#pragma unroll
+        for (int x = lo; x < (hi < BAR ? hi : BAR); ++x) {
+            const int xx = x - lo;
+            mfma(xx);
+            if (sl + 1 < NS) {
+#pragma unroll
+                for (int o = op_lo(xx, NR, NT); o < op_lo(xx + 1, NR, NT); ++o)
+                    read_frag(set ^ 1, sta, stb, sl + 1, o);
+            }
+#pragma unroll
+            for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
+                if (o < A_LOADS)
+                    store_a(sta ^ 1, (q + 1) % LEAD, o);
+                else
+                    load_a(q, (it + LEAD) * BK, o - A_LOADS);
+            }
+        }
+        if (lo < BAR && BAR <= hi) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS + A_LOADS));
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        }
+#pragma unroll
+        for (int x = (lo > BAR ? lo : BAR); x < hi; ++x) {
+            mfma(x - lo);
+#pragma unroll
+            for (int o = op_lo(x - BAR, NOPS2, XS - BAR); o < op_lo(x + 1 - BAR, NOPS2, XS - BAR); ++o) {
+                if (o < B_LOADS)
+                    load_b(stb, (it + SB) * BK, o);
+                else
+                    read_frag(((q + 1) * NS) & 1, sta ^ 1, (q + 1) % SB, 0, o - B_LOADS);
+            }
+        }
+    };
+    auto kstep = [&](const int q, int it, const bool first) __attribute__((always_inline)) {
+        kslice(q, it, 0, first);
+        if constexpr (NS > 1) kslice(q, it, 1, false);
+    };
+
+    // K-steps, rounded up to the LEAD-step unroll: the extra steps multiply
+    // the zeros their loads brought in.
+    const int nk = cdiv_i(cdiv_i(K, BK), LEAD) * LEAD;
+    kstep(0, 0, true);
+#pragma unroll
+    for (int q = 1; q < LEAD; ++q) kstep(q, q, false);
+    for (int it = LEAD; it < nk; it += LEAD) {
+#pragma unroll
+        for (int q = 0; q < LEAD; ++q) kstep(q, it + q, false);
+    }
+
+    // ---- epilogue.  The last row of tiles was written by the most recent
+    // MFMAs (16 passes each): wait them out before any accumulator is read;
+    // the other rows are at least FN MFMAs old.
+    static_assert(FN == 4, "the wait below lists the last row's tiles");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
+    // All loads (the B stages' direct LDS writes included) have landed and
+    // every wavefront is done with the stages before they are reused for C.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    if constexpr (SB == 4) {
+        store_c_block_32x32<__bf16, WM, WN, B_BYTES>(acc, b_stage(wave), lane, row0, col0, M, N, C);
+    } else {
+        static_assert(A_BYTES == B_BYTES, "one C region per wavefront");
+        lds_byte* cw = wave < 2 ? a_stage(wave) : b_stage(wave - 2);
+        store_c_block_32x32<__bf16, WM, WN, A_BYTES>(acc, cw, lane, row0, col0, M, N, C);
+    }
+}
+
+template <int FMT>
+hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
+{
+    const int tiles = cdiv_i(a.M, cfg.bm) * cdiv_i(a.N, cfg.bn);
+    const dim3 grid(tiles * a.batch.count), block(256);
+    const unsigned char* A = static_cast<const unsigned char*>(a.A);
+    const unsigned char* B = static_cast<const unsigned char*>(a.B);
+    __bf16* C = static_cast<__bf16*>(a.C);
+    if (cfg.threads != 256 || cfg.bm != 256 || cfg.bn != 256) return hipErrorInvalidValue;
+    if (cfg.bk == 64)
+        hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64>), grid, block, 0, a.stream, A, B, C, a.M, a.N, a.K,
+                           cfg.group_m, a.batch);
+    else if (cfg.bk == 128)
+        hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128>), grid, block, 0, a.stream, A, B, C, a.M, a.N, a.K,
+                           cfg.group_m, a.batch);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8(const Config& cfg, const LaunchArgs& a)
+{
+    if (a.dtype == kFP8E4M3) return launch_fmt<0>(cfg, a);
+    if (a.dtype == kFP8E5M2) return launch_fmt<1>(cfg, a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dgr

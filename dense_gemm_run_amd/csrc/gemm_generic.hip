@@ -1,4 +1,5 @@
-// Generic tiled kernels: any M, N, K, any pointer alignment, fp32/fp16/bf16.
+// Generic tiled kernels: any M, N, K, any pointer alignment, fp32/fp16/bf16,
+// and the 8-bit inputs (E4M3, E5M2) with a bf16 result.
 //
 // One workgroup of 256 lanes (4 wavefronts in a 2x2 grid) owns a 64x64 tile
 // of C and walks K in steps of BK (the tiled loop of kernels-book chapter
@@ -12,6 +13,11 @@
 // block of C held in 16 fp32 accumulator registers per lane and multiplies
 // with one MFMA per K-slice.  This path exists for ragged and unaligned
 // shapes; the aligned large shapes run the pipelined kernel instead.
+//
+// 8-bit inputs are widened to bf16 as they are staged: every finite E4M3
+// value (3 significand bits, exponents 2^-9 .. 2^8) and E5M2 value (2 bits,
+// 2^-16 .. 2^15) is a bf16 value, so the widening is exact and the bf16 MFMA
+// forms the same exact products and fp32 sums.
 #include "gemm_internal.h"
 
 namespace dgr {
@@ -36,14 +42,44 @@ __device__ inline f32x16 mfma16(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// One-byte storage types of the 8-bit formats (OCP FP8).
+struct E4M3 { unsigned char bits; };
+struct E5M2 { unsigned char bits; };
+
+// Value of an input element as the MFMA's operand type T.
+template <typename T> __device__ inline T widen(T x) { return x; }
+// E4M3: sign, 4 exponent bits (bias 7), 3 significand bits; exponent 0 is
+// subnormal (m * 2^-9); S.1111.111 is NaN; no infinities.
+__device__ inline __bf16 widen(E4M3 x)
+{
+    const unsigned b = x.bits, e = (b >> 3) & 15u, m = b & 7u;
+    unsigned f;
+    if (e == 0) f = __builtin_bit_cast(unsigned, (float)m * 0x1p-9f);
+    else if (e == 15 && m == 7) f = 0x7fc00000u;
+    else f = ((e + 120u) << 23) | (m << 20);
+    return (__bf16)__builtin_bit_cast(float, f | ((b & 0x80u) << 24));
+}
+// E5M2: sign, 5 exponent bits (bias 15), 2 significand bits; exponent 0 is
+// subnormal (m * 2^-16); exponent 31 is infinity (m = 0) or NaN.
+__device__ inline __bf16 widen(E5M2 x)
+{
+    const unsigned b = x.bits, e = (b >> 2) & 31u, m = b & 3u;
+    unsigned f;
+    if (e == 0) f = __builtin_bit_cast(unsigned, (float)m * 0x1p-16f);
+    else if (e == 31) f = m ? 0x7fc00000u : 0x7f800000u;
+    else f = ((e + 112u) << 23) | (m << 21);
+    return (__bf16)__builtin_bit_cast(float, f | ((b & 0x80u) << 24));
+}
+
 // 32x32 MFMA result layout: lane l holds column (l % 32); register r holds
 // row 8*(r/4) + 4*(l/32) + r%4.
 __device__ inline int acc_row(int lane, int r) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// ---------------------------------------------------------------- fp16/bf16
-template <typename T>
+// ------------------------------------------------- fp16/bf16 (and 8-bit in)
+// TI: storage type of A and B; T: the MFMA operand type and C's type.
+template <typename TI, typename T>
 __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
-    const T* __restrict__ A, const T* __restrict__ B, T* __restrict__ C,
+    const TI* __restrict__ A, const TI* __restrict__ B, T* __restrict__ C,
     int M, int N, int K, int group_m, Batch bt)
 {
     constexpr int BK = 32;
@@ -73,9 +109,9 @@ __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
         V8 av, bv;
         for (int e = 0; e < 8; ++e) {
             const int ka = k0 + a_k + e;
-            av[e] = (gm < M && ka < K) ? A[(size_t)gm * K + ka] : T(0.0f);
+            av[e] = (gm < M && ka < K) ? widen(A[(size_t)gm * K + ka]) : T(0.0f);
             const int kb = k0 + b_k + e;
-            bv[e] = (kb < K && gn < N) ? B[(size_t)kb * N + gn] : T(0.0f);
+            bv[e] = (kb < K && gn < N) ? widen(B[(size_t)kb * N + gn]) : T(0.0f);
         }
         *reinterpret_cast<V8*>(&As[a_row * LDK + a_k]) = av;
         *reinterpret_cast<V8*>(&Bs[b_col * LDK + b_k]) = bv;
@@ -160,13 +196,23 @@ hipError_t launch_generic(const Config& cfg, const LaunchArgs& a)
                            static_cast<float*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
         break;
     case kF16:
-        hipLaunchKernelGGL(gemm_generic16_kernel<_Float16>, grid, block, 0, a.stream,
+        hipLaunchKernelGGL((gemm_generic16_kernel<_Float16, _Float16>), grid, block, 0, a.stream,
                            static_cast<const _Float16*>(a.A), static_cast<const _Float16*>(a.B),
                            static_cast<_Float16*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
         break;
     case kBF16:
-        hipLaunchKernelGGL(gemm_generic16_kernel<__bf16>, grid, block, 0, a.stream,
+        hipLaunchKernelGGL((gemm_generic16_kernel<__bf16, __bf16>), grid, block, 0, a.stream,
                            static_cast<const __bf16*>(a.A), static_cast<const __bf16*>(a.B),
+                           static_cast<__bf16*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
+        break;
+    case kFP8E4M3:
+        hipLaunchKernelGGL((gemm_generic16_kernel<E4M3, __bf16>), grid, block, 0, a.stream,
+                           static_cast<const E4M3*>(a.A), static_cast<const E4M3*>(a.B),
+                           static_cast<__bf16*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
+        break;
+    case kFP8E5M2:
+        hipLaunchKernelGGL((gemm_generic16_kernel<E5M2, __bf16>), grid, block, 0, a.stream,
+                           static_cast<const E5M2*>(a.A), static_cast<const E5M2*>(a.B),
                            static_cast<__bf16*>(a.C), a.M, a.N, a.K, cfg.group_m, a.batch);
         break;
     default:

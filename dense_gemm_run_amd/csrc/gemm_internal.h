@@ -53,7 +53,9 @@ __host__ __device__ inline void tile_of_block(int bid, int tiles_m, int tiles_n,
     tm = top + (within - tn * height);
 }
 
-enum Dtype : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2 };
+// Element types.  The 8-bit formats are inputs only: their products are
+// written as bf16.
+enum Dtype : int32_t { kF32 = 0, kF16 = 1, kBF16 = 2, kFP8E4M3 = 3, kFP8E5M2 = 4 };
 
 struct Config {
     int32_t id;
@@ -88,5 +90,6 @@ hipError_t launch_generic(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_mfma32x32(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_mfma16x16(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_gemv(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_fp8(const Config& cfg, const LaunchArgs& a);
 
 }  // namespace dgr

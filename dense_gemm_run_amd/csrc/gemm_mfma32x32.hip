@@ -71,54 +71,6 @@ template <> struct Op<__bf16> {
 template <int BK> __device__ __forceinline__ int swz_a(int row) { return (row / (128 / BK)) % (BK / 8); }
 template <int BN> __device__ __forceinline__ int swz_b(int k) { return ((k & 7) << 2) & (BN / 8 - 1); }
 
-// Epilogue shared by the kernels: one wavefront's WM x WN block of fp32
-// accumulators (lane l holds row 32*bi + l%32, columns 32*bj + 8g + 4*(l/32)
-// .. +3 of tile (bi, bj) in registers 4g..4g+3) is rounded to the output type
-// (round to nearest even), written into the wavefront's own LDS region `cw`
-// (WM*WN*2 bytes) and read back as whole row segments for 16-byte stores to
-// C at (row0, col0), skipping rows >= M and columns >= N.  The caller makes
-// sure no other use of `cw` is in flight.
-template <typename T, int WM, int WN>
-__device__ __forceinline__ void store_c_block(const f32x16 (&acc)[WM / 32][WN / 32], lds_byte* cw,
-                                              int lane, int row0, int col0, int M, int N, T* C)
-{
-    constexpr int FM = WM / 32, FN = WN / 32;
-    // Row-major in LDS with 16-byte pieces swizzled: piece p of row r sits at
-    // p ^ (r % PR) and its two 8-byte halves are swapped when (r / PR) is
-    // odd, so the 8-byte writes of 32 lanes (32 rows, one piece-half each)
-    // land on distinct banks.
-    constexpr int PR = WN / 8;                    // 16-byte pieces per C row
-#pragma unroll
-    for (int bi = 0; bi < FM; ++bi) {
-        const int r = 32 * bi + (lane & 31);
-#pragma unroll
-        for (int bj = 0; bj < FN; ++bj) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int p = (4 * bj + g) ^ (r & (PR - 1));
-                const int h = (lane >> 5) ^ ((r / PR) & 1);
-                u32x2 v;
-                v[0] = pack2<T>(acc[bi][bj][4 * g + 0], acc[bi][bj][4 * g + 1]);
-                v[1] = pack2<T>(acc[bi][bj][4 * g + 2], acc[bi][bj][4 * g + 3]);
-                *(u32x2 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16 + h * 8) = v;
-            }
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's LDS writes done
-    // Read back whole row segments: lane -> row it*(64/PR) + lane/PR, piece lane%PR.
-    const int q = lane % PR;
-    const int col = col0 + q * 8;
-#pragma unroll 4
-    for (int it = 0; it < WM * PR / 64; ++it) {
-        const int r = it * (64 / PR) + lane / PR;
-        const int p = q ^ (r & (PR - 1));
-        u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
-        if ((r / PR) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
-        const int row = row0 + r;
-        if (row < M && col < N) *(u32x4*)(C + (size_t)row * N + col) = v;
-    }
-}
-
 template <typename T, int BM, int BN, int BK, int WAVES_N>
 __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_mfma32x32_kernel(
     const T* __restrict__ A, const T* __restrict__ B, T* __restrict__ C,
@@ -382,7 +334,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_mfma32x32_kernel(
     // wavefront is done with the stages before they are reused for C.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    store_c_block<T, WM, WN>(acc, (lds_byte*)smem + wave * C_BYTES, lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
+    store_c_block_32x32<T, WM, WN>(acc, (lds_byte*)smem + wave * C_BYTES, lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
 }
 
 template <typename T>

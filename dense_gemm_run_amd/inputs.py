@@ -6,7 +6,9 @@ and benchmark and the CPU oracle's callers.
 
 Recipe (every workload): a CPU ``torch.Generator`` seeded with the workload's
 seed draws A first, then B, in fp32; each is then cast to the workload's dtype
-with torch's round-to-nearest-even.  The seeding convention (a fixed seed
+with torch's round-to-nearest-even (for the 8-bit dtypes, torch's conversion
+to ``float8_e4m3fn`` / ``float8_e5m2``, the OCP formats; the distributions
+used with them stay far inside both formats' ranges).  The seeding convention (a fixed seed
 before drawing both operands) follows the correctness cell of the notebook
 "Triton tiled matmul".  Distributions:
 
@@ -37,7 +39,8 @@ from dataclasses import dataclass
 
 import torch
 
-DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+          "fp8_e4m3": torch.float8_e4m3fn, "fp8_e5m2": torch.float8_e5m2}
 
 
 @dataclass(frozen=True)
@@ -85,6 +88,12 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              "decode GEMV y = W x, W [4096, 14336] (MLP down, one token)"),
     Workload("bf16_gemv_12288x4x4096", 12288, 4, 4096, "bf16", "decode", 12,
              "decode GEMV with 4 vectors, W [12288, 4096] (QKV, 4 tokens)"),
+    Workload("fp8_e4m3_4096x4096x4096", 4096, 4096, 4096, "fp8_e4m3", "normal", 13,
+             "square 4096^3 with E4M3 inputs, N(0,1) rounded to E4M3, bf16 output"),
+    Workload("fp8_e5m2_4096x4096x4096", 4096, 4096, 4096, "fp8_e5m2", "normal", 14,
+             "square 4096^3 with E5M2 inputs, N(0,1) rounded to E5M2, bf16 output"),
+    Workload("fp8_e4m3_8192x8192x8192", 8192, 8192, 8192, "fp8_e4m3", "normal", 15,
+             "square 8192^3 with E4M3 inputs, N(0,1) rounded to E4M3, bf16 output"),
 ]}
 
 # Order in which the four prefill projections of one layer run.

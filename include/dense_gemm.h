@@ -18,6 +18,11 @@
  * (notebook "Triton tiled matmul", section "What"), and the fp32 sum is
  * rounded to the output type with round-to-nearest-even.  fp32 inputs are
  * multiplied at full fp32 precision (no reduced-precision input mode).
+ * The 8-bit floating-point inputs (the FP8 input path of the same
+ * notebook's exercises: the accumulator stays fp32) are the two OCP FP8
+ * formats, E4M3 and E5M2, for both A and B; C is then bf16, which holds
+ * every product's range, and the fp32 sum is rounded to bf16 (nearest
+ * even).  Every product of two such values is exact in fp32.
  *
  * Edges: M, N and K need not be multiples of any tile size.  Out-of-range
  * input elements read as zero (zero padding is neutral for the sum) and only
@@ -44,11 +49,16 @@
 extern "C" {
 #endif
 
-/* Element type of A, B and C. */
+/* Element type of A and B; C has the same type, except for the 8-bit
+ * inputs, whose C is bf16. */
 typedef enum gemm_dtype {
-    GEMM_F32 = 0,   /* IEEE binary32 */
-    GEMM_F16 = 1,   /* IEEE binary16 */
-    GEMM_BF16 = 2   /* bfloat16: fp32's exponent, 8-bit significand */
+    GEMM_F32 = 0,      /* IEEE binary32 */
+    GEMM_F16 = 1,      /* IEEE binary16 */
+    GEMM_BF16 = 2,     /* bfloat16: fp32's exponent, 8-bit significand */
+    GEMM_FP8_E4M3 = 3, /* OCP E4M3: bias 7, 3 significand bits, max 448, NaN
+                        * S.1111.111, no infinities; C is bf16 */
+    GEMM_FP8_E5M2 = 4  /* OCP E5M2: bias 15, 2 significand bits, max 57344,
+                        * IEEE-style infinities and NaNs; C is bf16 */
 } gemm_dtype_t;
 
 typedef enum gemm_status {
@@ -78,7 +88,8 @@ gemm_status_t gemm_create(gemm_handle_t* out);
  *   C      device pointer to M*N elements, row-major [M,N]    (written)
  *   M,N,K  sizes, each >= 0.  M == 0 or N == 0: nothing is written.
  *          K == 0: C is filled with zeros (an empty sum).
- *   dtype  a gemm_dtype_t value, the type of all three matrices.
+ *   dtype  a gemm_dtype_t value, the type of A and B and (8-bit inputs
+ *          aside, whose C is bf16) of C.
  *   stream a hipStream_t, or NULL for the null stream.
  * A pointer may be NULL only when its matrix has no elements.  C may not
  * overlap A or B.  The device current on the calling thread must be the
@@ -94,8 +105,10 @@ gemm_status_t gemm_run(gemm_handle_t h, const void* A, const void* B, void* C,
  *            starts at A + b*stride_a, B + b*stride_b, C + b*stride_c
  *            elements, and each matrix is row-major as in gemm_run.
  *   batch    number of products, >= 0 (0: nothing is done).
- *   strides  in elements, >= 0.  A stride of 0 uses the same matrix for
- *            every b (one weight matrix B for a batch of activations, say).
+ *   strides  in elements of their own matrix (one byte for 8-bit A and B,
+ *            bf16 elements for their C), >= 0.  A stride of 0 uses the same
+ *            matrix for every b (one weight matrix B for a batch of
+ *            activations, say).
  *   M,N,K, dtype, stream  as in gemm_run, for every matrix of the batch.
  * Each matrix must stay below 2^31 bytes; strides may be larger.  The C
  * matrices may not overlap each other (stride_c >= M*N when batch > 1), and
@@ -138,7 +151,8 @@ typedef struct gemm_config_info {
     int32_t group_m;           /* tile-rows walked before moving right */
     int32_t threads;           /* workgroup size */
     int32_t dtype_mask;        /* bit d set: accepts gemm_dtype_t d */
-    int32_t needs_vec_align;   /* 1: needs 16-byte aligned A, B, C and K, N (and batch strides) multiples of 16 bytes / element size */
+    int32_t needs_vec_align;   /* 1: needs 16-byte aligned A, B, C, and K, N and batch strides that keep every
+                                * row of A, B and C a multiple of 16 bytes (in each matrix's element size) */
     int32_t xcd_remap;         /* 1: workgroup ids are remapped so each XCD gets a compact block of tiles */
     char name[40];
 } gemm_config_info_t;

@@ -57,8 +57,17 @@ A, B, C = 0x10000, 0x200000, 0x4000000   # fake, never dereferenced
     ((A, B, C, -1, 5, 6, 1), INVALID),
     ((A, B, C, 4, -5, 6, 1), INVALID),
     ((A, B, C, 4, 5, -6, 1), INVALID),
-    ((A, B, C, 4, 5, 6, 3), BADTYPE),
+    ((A, B, C, 4, 5, 6, 5), BADTYPE),
     ((A, B, C, 4, 5, 6, -1), BADTYPE),
+    ((A, B, C, 4, 5, 6, 3), OK),          # 8-bit inputs, bf16 C
+    ((A, B, C, 4, 5, 6, 4), OK),
+    ((A, B, A + 24, 4, 5, 6, 3), OK),     # A holds 24 one-byte elements: adjacent, no overlap
+    ((A, B, A + 23, 4, 5, 6, 3), ALIAS),
+    ((A + 40, B, A, 4, 5, 6, 3), OK),     # C holds 20 bf16 = 40 bytes: adjacent
+    ((A + 39, B, A, 4, 5, 6, 3), ALIAS),
+    ((A, B, C, 1 << 16, 1 << 14, 1, 3), TOOBIG),   # C = 2^30 bf16 = 2^31 bytes
+    ((A, B, C, 1 << 16, 1 << 14, 1 << 15, 3), TOOBIG),  # A = 2^31 one-byte elements
+    ((A, 1 << 33, 1 << 34, 1 << 16, (1 << 14) - 1, (1 << 15) - 1, 3), OK),   # just below both limits
     ((0, B, C, 4, 5, 6, 1), INVALID),
     ((A, 0, C, 4, 5, 6, 1), INVALID),
     ((A, B, 0, 4, 5, 6, 1), INVALID),
@@ -105,7 +114,7 @@ def test_config_table():
         assert info["threads"] % 64 == 0
         names.add(info["name"])
     assert len(names) == n
-    assert dg.gemm_config_info(0)["dtype_mask"] == 0x7 and dg.gemm_config_info(0)["needs_vec_align"] == 0
+    assert dg.gemm_config_info(0)["dtype_mask"] == 0x1f and dg.gemm_config_info(0)["needs_vec_align"] == 0
     with pytest.raises(dg.GemmError):
         dg.gemm_config_info(n)
 
@@ -126,7 +135,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(13))
+@pytest.mark.parametrize("cid", range(15))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -243,3 +252,32 @@ def test_few_columns_select_the_vector_kernel():
         assert not dg.gemm_config_info(dg.gemm_select_config(*args))["name"].startswith("gemv")
     # C needs no alignment for it
     assert dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb + 2, 4096, 1, 4096, 2))["name"].startswith("gemv")
+
+
+def test_8bit_inputs_select_their_kernels():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    fp8_cfgs = [i for i in range(dg.gemm_config_count())
+                if dg.gemm_config_info(i)["dtype_mask"] == 0x18]
+    assert len(fp8_cfgs) >= 1
+    for dt in (3, 4):
+        for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (1000, 1008, 1024)]:
+            cid = dg.gemm_select_config(A, Bb, Cb, M, N, K, dt)
+            assert cid in fp8_cfgs, (M, N, K, dt, cid)
+        # rows of A or B not whole 16-byte pieces, a misaligned pointer, or a
+        # small product: the generic kernel (which widens to bf16)
+        for args in [(A, Bb, Cb, 4096, 4096, 4088, dt), (A, Bb, Cb, 4096, 4088, 4096, dt),
+                     (A + 8, Bb, Cb, 4096, 4096, 4096, dt), (A, Bb, Cb + 8, 4096, 4096, 4096, dt),
+                     (A, Bb, Cb, 64, 64, 64, dt), (A, Bb, Cb, 4096, 1, 4096, dt)]:
+            assert dg.gemm_select_config(*args) == 0, args
+    # the 16-bit kernels refuse 8-bit inputs and the 8-bit ones refuse the rest
+    for i in range(dg.gemm_config_count()):
+        m = dg.gemm_config_info(i)["dtype_mask"]
+        assert i == 0 or (m & 0x18) == 0 or (m & 0x7) == 0
+    # batch strides: in one-byte elements for A and B, bf16 elements for C
+    assert dg.gemm_select_config_batched(A, Bb, Cb, 4, 1024, 1024, 1024, 1024 * 1024,
+                                         1024 * 1024, 1024 * 1024, 3) in fp8_cfgs
+    assert dg.gemm_select_config_batched(A, Bb, Cb, 4, 1024, 1024, 1024, 1024 * 1024 + 8,
+                                         1024 * 1024, 1024 * 1024, 3) == 0
+    assert dg.gemm_select_config_batched(A, Bb, Cb, 4, 1024, 1024, 1024, 1024 * 1024,
+                                         1024 * 1024, 1024 * 1024 + 8, 3) in fp8_cfgs

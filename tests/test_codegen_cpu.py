@@ -1,6 +1,7 @@
-"""Structure of the generated code of the 16x16x32 MFMA kernel.
+"""Structure of the generated code of the pipelined MFMA kernels (16x16x32
+for fp16/bf16, 32x32x64 for the 8-bit formats).
 
-Its B tiles reach LDS through direct buffer->LDS loads that the kernel waits
+Their B tiles reach LDS through direct buffer->LDS loads that the kernel waits
 for by count: before each barrier a wavefront waits until at most a fixed
 number of its own loads are outstanding, which is right only if every K-step
 issues its A loads before its barrier and its B loads after it, in that
@@ -17,39 +18,62 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "dense_gemm_run_amd", "csrc", "gemm_mfma16x16.hip")
+CSRC = os.path.join(ROOT, "dense_gemm_run_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# source file, kernel-name pattern (-> bm, bn, bk), instances, element bytes,
+# MFMA mnemonic, K depth of one MFMA, outputs of one MFMA
+FAMILIES = {
+    "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)E",
+                  # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32)
+                  10, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
+    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)E",
+            # {e4m3, e5m2} x {64, 128}, all 256x256
+            4, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
+}
+
+
+def compile_family(fam, tmp):
+    src, pat, count, ebytes, mnem, kdepth, outs = FAMILIES[fam]
+    out = tmp / (fam + ".s")
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
+           "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = out.read_text().split("\n")
+    found = {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_Z\S*" + pat + r"\S*):", l)
+        if m:
+            g = [int(x) for x in m.groups()[1:]]
+            bm, bn, bk = g if len(g) == 3 else (256, 256, g[0])
+            end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+            found[m.group(1)] = Kernel(fam, bm, bn, bk, ebytes, mnem, kdepth, outs, lines[i:end])
+    assert len(found) == count, sorted(found)
+    return found
+
+
+class Kernel:
+    def __init__(self, fam, bm, bn, bk, ebytes, mnem, kdepth, outs, body):
+        self.fam, self.bm, self.bn, self.bk, self.body = fam, bm, bn, bk, body
+        self.mnem, self.kdepth, self.outs = mnem, kdepth, outs
+        # loads per wavefront per K-step and the pipeline depths
+        self.a_loads = bm * bk * ebytes // 1024 // 4
+        self.b_loads = bk * bn * ebytes // 1024 // 4
+        self.lead = 256 // (bk * ebytes)                  # A register slots
+        self.sb = 4 if bk * ebytes == 64 else 2           # B stages
 
 
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
     if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "k.s"
-    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
-           "--cuda-device-only", "-S", SRC, "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr
-    lines = out.read_text().split("\n")
+    tmp = tmp_path_factory.mktemp("asm")
     found = {}
-    for i, l in enumerate(lines):
-        m = re.match(r"^(_Z\S*gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)E\S*):", l)
-        if m:
-            end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
-            found[m.group(1)] = (int(m.group(2)), int(m.group(3)), int(m.group(4)), lines[i:end])
-    # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32)
-    assert len(found) == 10, sorted(found)
+    for fam in FAMILIES:
+        found.update(compile_family(fam, tmp))
     return found
-
-
-def geometry(bm, bn, bk):
-    """Loads per wavefront per K-step and the pipeline depths of one instance."""
-    a_loads = bm * bk * 2 // 1024 // 4
-    b_loads = bk * bn * 2 // 1024 // 4
-    lead = 128 // bk               # A register slots
-    sb = 4 if bk == 32 else 2      # B stages
-    return a_loads, b_loads, lead, sb
 
 
 def events(body):
@@ -72,8 +96,8 @@ def events(body):
 
 
 def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels):
-    for name, (bm, bn, bk, body) in kernels.items():
-        a_loads, b_loads, lead, sb = geometry(bm, bn, bk)
+    for name, kn in kernels.items():
+        a_loads, b_loads, lead, sb, body = kn.a_loads, kn.b_loads, kn.lead, kn.sb, kn.body
         loads = a_loads + b_loads
         count = (sb - 2) * loads + a_loads
         ev = events(body)
@@ -103,17 +127,17 @@ def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels)
 
 
 def test_accumulators_stay_in_place(kernels):
-    for name, (bm, bn, bk, body) in kernels.items():
-        _, _, lead, _ = geometry(bm, bn, bk)
-        text = [x.strip() for x in body]
-        mfma = [x for x in text if x.startswith("v_mfma_f32_16x16x32")]
-        per_slice = (bm // 32) * (bn // 32)
-        # peeled K-steps + the loop body's, bk/32 K-slices each
-        assert len(mfma) == 2 * lead * (bk // 32) * per_slice, (name, len(mfma))
+    for name, kn in kernels.items():
+        text = [x.strip() for x in kn.body]
+        mfma = [x for x in text if x.startswith(kn.mnem)]
+        per_slice = kn.bm * kn.bn // 4 // kn.outs     # MFMAs per wavefront per K-slice
+        # peeled K-steps + the loop body's, bk/kdepth K-slices each
+        assert len(mfma) == 2 * kn.lead * (kn.bk // kn.kdepth) * per_slice, (name, len(mfma))
         # only the first K-slice starts from 0
-        assert sum(1 for x in mfma if x.endswith(", 0")) == per_slice, name
+        ops_of = lambda x: [o.strip().split()[0] for o in x.split(None, 1)[1].split(",")]
+        assert sum(1 for x in mfma if ops_of(x)[3] == "0") == per_slice, name
         for x in mfma:
-            ops = [o.strip() for o in x.split(None, 1)[1].split(",")]
+            ops = ops_of(x)
             assert ops[3] in (ops[0], "0"), x   # accumulate in place or start from 0
         first = next(i for i, x in enumerate(text) if x.startswith("v_mfma"))
         last = max(i for i, x in enumerate(text) if x.startswith("v_mfma"))

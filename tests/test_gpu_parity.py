@@ -20,7 +20,6 @@ from oracle import gemm64, tolerance
 pytestmark = pytest.mark.gpu
 
 DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
-DT_CODE_T = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 
 def note(msg):
@@ -42,11 +41,13 @@ def accepts(cid, a, b, M, N, K, batch=1):
     GEMM_ERR_CONFIG_MISMATCH before any launch)."""
     h = dg.gemm_create()
     try:
-        c = torch.empty((batch, M, N) if batch > 1 else (M, N), dtype=a.dtype, device=a.device)
+        # C of the output type (bf16 for 8-bit inputs), M*N elements per matrix
+        c = torch.empty((batch, M, N) if batch > 1 else (M, N), dtype=dg.out_dtype(a.dtype),
+                        device=a.device)
         st = dg._lib.lib().gemm_run_batched_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(),
                                                   batch, M, N, K, M * K if a.ndim == 3 else 0,
                                                   K * N if b.ndim == 3 else 0, M * N,
-                                                  DT_CODE_T[a.dtype], cid, None)
+                                                  dg.dtype_code(a.dtype), cid, None)
         torch.cuda.synchronize()
         assert st in (0, 7), st        # ran, or refused as a mismatch
         return st == 0

@@ -97,3 +97,61 @@ def test_batched_pin_catches(mutant):
     B = rng.integers(-4, 5, (4, 5, 2)).astype(np.float64)
     ok = np.array_equal(batched_loop(A, B, mutant), np.matmul(A, B))
     assert ok == (mutant is None)
+
+
+# ---------------------------------------------------------------- 8-bit decode
+def decode_mutant(bits, fmt, mutant=None):
+    """A copy of the oracle's 8-bit decode with one planted mistake."""
+    b = np.asarray(bits).astype(np.int64) & 0xFF
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    if fmt == "e4m3":
+        ebits, mbits, bias = 4, 3, 7
+    else:
+        ebits, mbits, bias = 5, 2, 15
+    if mutant == "wrong_bias":
+        bias += 1
+    e = (b >> mbits) & ((1 << ebits) - 1)
+    m = (b & ((1 << mbits) - 1)).astype(np.float64)
+    frac = m / (1 << mbits)
+    if mutant == "subnormal_as_normal":
+        sub = (1.0 + frac) * np.exp2(1.0 - bias - 1)
+    else:
+        sub = frac * 2.0 ** (1 - bias)
+    mag = np.where(e == 0, sub, (1.0 + frac) * np.exp2(e - float(bias)))
+    top = (1 << ebits) - 1
+    if fmt == "e4m3":
+        if mutant == "ieee_specials":
+            mag = np.where(e == top, np.where(m == 0, np.inf, np.nan), mag)
+        else:
+            mag = np.where((e == top) & (m == 7), np.nan, mag)
+    else:
+        mag = np.where(e == top, np.where(m == 0, np.inf, np.nan), mag)
+    if mutant == "sign_dropped":
+        sign = np.ones_like(sign)
+    return sign * mag
+
+
+def decode_pins_pass(fn) -> bool:
+    from test_oracle_pins import FP8_HAND, FP8_MAXCODE, FP8_NAN
+    import math
+    for fmt in ("e4m3", "e5m2"):
+        for code, want in FP8_HAND[fmt].items():
+            got = float(fn(np.array([code]), fmt)[0])
+            if not (got == want and math.copysign(1, got) == math.copysign(1, want)):
+                return False
+        if not np.isnan(fn(np.array(FP8_NAN[fmt]), fmt)).all():
+            return False
+        pos = fn(np.arange(0, FP8_MAXCODE[fmt] + 1), fmt)
+        if not (np.diff(pos) > 0).all():
+            return False
+    return True
+
+
+def test_unmutated_decode_passes():
+    assert decode_pins_pass(lambda b, f: decode_mutant(b, f))
+
+
+@pytest.mark.parametrize("mutant", ["wrong_bias", "subnormal_as_normal", "ieee_specials",
+                                    "sign_dropped"])
+def test_decode_mutant_is_caught(mutant):
+    assert not decode_pins_pass(lambda b, f: decode_mutant(b, f, mutant))

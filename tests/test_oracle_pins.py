@@ -420,3 +420,102 @@ def test_tolerance_rule():
         assert tolerance.compare(np.array([v * (1 + 2 ** -10)]), np.array([v]), "f16", 1, 1e-9, 1e-9)["ok"]
         assert tolerance.compare(np.array([v * (1 + 2 ** -7)]), np.array([v]), "bf16", 1, 1e-9, 1e-9)["ok"]
     assert not tolerance.compare(np.array([1.0 + 2e-5]), np.array([1.0]), "f32", 1, 1e-9, 1e-9)["ok"]
+
+
+# ---------------------------------------------------------------- 8-bit inputs
+# The 8-bit formats are the OCP FP8 ones (E4M3: bias 7, 3 significand bits,
+# S.1111.111 NaN, no infinities; E5M2: bias 15, 2 significand bits, IEEE-style
+# infinities and NaNs).  Hand-checked codes from those definitions:
+FP8_HAND = {
+    "e4m3": {0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+             0x38: 1.0, 0xB8: -1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0,
+             0x77: 240.0, 0x3F: 1.875},
+    "e5m2": {0x00: 0.0, 0x80: -0.0, 0x01: 2.0 ** -16, 0x03: 3 * 2.0 ** -16, 0x04: 2.0 ** -14,
+             0x3C: 1.0, 0xBC: -1.0, 0x3D: 1.25, 0x7B: 57344.0, 0xFB: -57344.0,
+             0x7C: math.inf, 0xFC: -math.inf},
+}
+FP8_NAN = {"e4m3": [0x7F, 0xFF], "e5m2": [0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]}
+FP8_MAXCODE = {"e4m3": 0x7E, "e5m2": 0x7B}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_hand_values(fmt):
+    from oracle import fp8
+    for code, want in FP8_HAND[fmt].items():
+        got = float(fp8.decode(np.array([code]), fmt)[0])
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (hex(code), got)
+    nan = fp8.decode(np.array(FP8_NAN[fmt]), fmt)
+    assert np.isnan(nan).all()
+    everything = fp8.decode(np.arange(256), fmt)
+    assert int(np.isnan(everything).sum()) == len(FP8_NAN[fmt])
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_decode_matches_torch_on_every_code(fmt, tdt):
+    from oracle import fp8
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    want = codes.view(tdt).to(torch.float64).numpy()
+    got = fp8.decode(codes.numpy(), fmt)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def test_fp8_e5m2_is_binary16_with_low_byte_zero():
+    from oracle import fp8
+    codes = np.arange(256, dtype=np.uint16)
+    want = (codes << 8).view(np.float16).astype(np.float64)
+    got = fp8.decode(codes, "e5m2")
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_order_and_sign(fmt):
+    from oracle import fp8
+    top = FP8_MAXCODE[fmt]
+    pos = fp8.decode(np.arange(0, top + 1), fmt)
+    assert (np.diff(pos) > 0).all()
+    neg = fp8.decode(np.arange(0, top + 1) | 0x80, fmt)
+    assert np.array_equal(neg, -pos)
+    # every value is exact in bf16 and in fp16 (the widenings the GPU path may use)
+    v = pos[1:]
+    assert np.array_equal(v.astype(np.float16).astype(np.float64), v)
+    bf = gemm64.bits_to_f64(gemm64.round_to_bits(v, "bf16"), "bf16")
+    assert np.array_equal(bf, v)
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_reference_on_integers(fmt, tdt):
+    # integers in [-4, 4] are exact in both formats; with K = 16 every sum
+    # is an integer of magnitude <= 256, which bf16 holds exactly
+    from oracle import fp8
+    rng = np.random.default_rng(21)
+    M, N, K = 9, 11, 16
+    A = rng.integers(-4, 5, (M, K))
+    B = rng.integers(-4, 5, (K, N))
+    At = torch.from_numpy(A.astype(np.float32)).to(tdt)
+    Bt = torch.from_numpy(B.astype(np.float32)).to(tdt)
+    ref, raw = fp8.reference_fp8(At, Bt, fmt)
+    exact_c = np.array(exact.exact_gemm(A.tolist(), B.tolist()), dtype=np.float64)
+    assert np.array_equal(raw, exact_c)
+    assert np.array_equal(ref, exact_c)      # |sums| <= 256: exact in bf16
+    # batched, B shared
+    A3 = np.stack([A, -A, 2 * A])
+    r3, raw3 = fp8.reference_fp8(torch.from_numpy(A3.astype(np.float32)).to(tdt), Bt, fmt)
+    assert np.array_equal(raw3, np.stack([exact_c, -exact_c, 2 * exact_c]))
+
+
+def test_fp8_reference_rounds_once_to_bf16():
+    from oracle import fp8
+    # [1, 1, 1] . [1, 2^-8, 2^-12] = 1 + 2^-8 + 2^-12 is not a bf16 value; it
+    # lies above the half-way point 1 + 2^-8, so it rounds to 1 + 2^-7 (a
+    # rounding of the partial sum 1 + 2^-8 first would give the tie and 1.0)
+    b5 = np.array([[0x3C], [0x1C], [0x0C]], dtype=np.uint8)   # E5M2: 1, 2^-8, 2^-12
+    a5 = np.array([[0x3C, 0x3C, 0x3C]], dtype=np.uint8)
+    assert list(fp8.decode(b5.ravel(), "e5m2")) == [1.0, 2.0 ** -8, 2.0 ** -12]
+    ref, raw = fp8.reference_fp8(a5, b5, "e5m2")
+    assert raw[0, 0] == 1 + 2.0 ** -8 + 2.0 ** -12
+    assert ref[0, 0] == 1 + 2.0 ** -7
