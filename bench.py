@@ -50,10 +50,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+# Kernel source of each configuration family (by configuration-name prefix).
+KERNEL_FILES = {"mfma16x16": "gemm_mfma16x16.hip", "mfma32x32": "gemm_mfma32x32.hip",
+                "fp8": "gemm_fp8.hip", "gemv": "gemm_gemv.hip", "generic": "gemm_generic.hip"}
+# What every kernel's code and launch depend on besides its own file.
+SHARED_FILES = ["gemm_device.h", "gemm_internal.h", "gemm_api.cpp"]
+
+
+def kernel_source_digest(kernel_cfg: str) -> str:
+    """sha256 (16 hex digits) of the sources configuration ``kernel_cfg``
+    is built and launched from: its kernel file and the shared headers and
+    host table."""
+    fam = next(f for p, f in KERNEL_FILES.items() if kernel_cfg.startswith(p))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_run_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted([fam] + SHARED_FILES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -66,7 +77,7 @@ def traffic_from_profiles(kernel_cfg: str, workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_digest") != kernel_source_digest():
+    if rec.get("kernel_source_digest") != kernel_source_digest(kernel_cfg):
         return None
     return rec.get("hbm_bytes_per_launch")
 

@@ -29,11 +29,14 @@
 //    16-byte pieces at or past K, rows past M and columns past N read zeros
 //    (the zero padding of chapter "Matrix Multiplication", section "The real
 //    tiled loop").
-//  * LDS layout: A [256][BK] with 16-byte pieces XOR-swizzled by (row/2) %
-//    (BK/16): each 16-lane group of a fragment read takes one piece of 16
-//    consecutive rows, the read that measured free of bank conflicts in the
-//    16-bit kernel.  B [BK][256] with piece p of row k stored at
-//    p ^ 2*(k%8): the 8-bit transpose read of a half-wavefront covers 8
+//  * LDS layout: A [256][BK] with 16-byte pieces XOR-swizzled: a fragment
+//    read has its four 16-lane groups take one piece each of rows 0-15,
+//    16-31, 0-15 and 16-31 of a tile.  Measured with the bank-conflict
+//    counter on that exact read, XOR (row/4) % 4 is conflict-free for 64-byte
+//    rows (BK = 64) where (row/2) % 4 costs a 2-way conflict, and XOR
+//    (row/2) % 8 is conflict-free for 128-byte rows.  B [BK][256] with
+//    piece p of row k stored at p ^ 2*(k%8): the 8-bit transpose read of a
+//    half-wavefront covers 8
 //    consecutive rows and one 32-byte column pair of each, and the swizzle
 //    puts those 8 pairs in 8 different 32-byte bank groups.
 //  * One barrier per K-step, half a K-slice before its end; the loads and
@@ -73,7 +76,10 @@ template <> struct MfmaFp8<1> {
     }
 };
 
-template <int BK> __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & (BK / 16 - 1); }
+template <int BK> __device__ __forceinline__ int swz_a(int row)
+{
+    return BK == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
 __device__ __forceinline__ int swz_b(int k) { return 2 * (k & 7); }
 
 template <int FMT, int BK>
@@ -173,8 +179,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
 
     // ---- operand read addresses within a stage
     // A fragment (K-slice sl, tile bi): row wm*WM + 32*bi + lane%32, logical
-    // pieces 4*sl + 2*(lane/32) and the next (32 bytes); the swizzle depends
-    // only on lane%32.
+    // pieces 4*sl + 2*(lane/32) and the next (32 bytes); the swizzle uses bits
+    // 1-3 of the row only, so it depends on lane%32 alone.
     int a_rd[NS][2];
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl)
