@@ -121,10 +121,27 @@ SWEEP_SKINNY = [(m, 4096, 4096) for m in (16, 32, 64, 128, 256, 512)] + \
 SWEEP_PREFILL = [(8192, 12288, 4096), (8192, 4096, 4096), (8192, 14336, 4096), (8192, 4096, 14336)]
 
 
+def _time_us(fn, iters, stream) -> float:
+    import torch
+    for _ in range(3):
+        fn()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(iters):
+        fn()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / iters * 1e3
+
+
 def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
-    """Time every accepting configuration on the sweep shapes (bf16 or fp16,
-    N(0,1)/sqrt(K) inputs, seed 100); with ``vendor``, also torch.matmul on the
-    same operands (the vendor library, for context)."""
+    """Time every accepting configuration on the sweep shapes (N(0,1)/sqrt(K)
+    inputs for fp16/bf16, N(0,1) rounded to the format for the 8-bit inputs;
+    seed 100); with ``vendor``, also the vendor library on the same operands
+    for context: torch.matmul, or torch._scaled_mm (unit scales, B handed
+    over column-major as it requires) for the 8-bit inputs."""
     import torch
     import dense_gemm_run_amd as dg
     from dense_gemm_run_amd import _lib
@@ -133,56 +150,45 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     h = dg.gemm_create()
-    code = {"f16": 1, "bf16": 2}[dtype]
+    eight_bit = dtype.startswith("fp8")
     shapes = [(n, n, n) for n in SWEEP_SQUARE] + SWEEP_SKINNY + SWEEP_PREFILL
     stream = torch.cuda.current_stream(dev)
     for M, N, K in shapes:
-        A, B = make_operands(M, N, K, dtype, "normal_sqrtk", 100)
+        A, B = make_operands(M, N, K, dtype, "normal" if eight_bit else "normal_sqrtk", 100)
         a, b = A.to(dev), B.to(dev)
-        c = torch.empty((M, N), dtype=a.dtype, device=dev)
+        code = dg.dtype_code(a.dtype)
+        c = torch.empty((M, N), dtype=dg.out_dtype(a.dtype), device=dev)
         chosen = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, code)
         flops = 2.0 * M * N * K
-        compulsory = (M * K + K * N + M * N) * a.element_size()
+        compulsory = (M * K + K * N) * a.element_size() + M * N * c.element_size()
+
+        def line(cid, name, us):
+            print(json.dumps({"M": M, "N": N, "K": K, "dtype": dtype, "config": cid, "name": name,
+                              "selected": cid == chosen, "us": round(us, 2),
+                              "tflops": round(flops / (us * 1e-6) / 1e12, 1),
+                              "compulsory_gbps": round(compulsory / (us * 1e-6) / 1e9, 1)}),
+                  flush=True)
+
         for cid in range(dg.gemm_config_count()):
-            def run():
+            def run(cid=cid):
                 return _lib.lib().gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N,
                                                   K, code, cid, stream.cuda_stream)
             if run() != 0:          # this configuration refuses the shape
                 continue
-            for _ in range(3):
-                run()
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            ev0.record(stream)
-            for _ in range(iters):
-                run()
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            ms = ev0.elapsed_time(ev1) / iters
-            print(json.dumps({"M": M, "N": N, "K": K, "dtype": dtype, "config": cid,
-                              "name": dg.gemm_config_info(cid)["name"], "selected": cid == chosen,
-                              "us": round(ms * 1e3, 2),
-                              "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-                              "compulsory_gbps": round(compulsory / (ms * 1e-3) / 1e9, 1)}),
-                  flush=True)
+            line(cid, dg.gemm_config_info(cid)["name"], _time_us(run, iters, stream))
         if vendor:
-            for _ in range(3):
-                torch.matmul(a, b)
-            ev0 = torch.cuda.Event(enable_timing=True)
-            ev1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            ev0.record(stream)
-            for _ in range(iters):
-                torch.matmul(a, b)
-            ev1.record(stream)
-            torch.cuda.synchronize()
-            ms = ev0.elapsed_time(ev1) / iters
-            print(json.dumps({"M": M, "N": N, "K": K, "dtype": dtype, "config": None,
-                              "name": "torch.matmul", "selected": False, "us": round(ms * 1e3, 2),
-                              "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-                              "compulsory_gbps": round(compulsory / (ms * 1e-3) / 1e9, 1)}),
-                  flush=True)
+            if eight_bit:
+                bt = b.t().contiguous().t()
+                one = torch.ones((), dtype=torch.float32, device=dev)
+                try:
+                    def vrun():
+                        return torch._scaled_mm(a, bt, one, one, out_dtype=torch.bfloat16)
+                    line(None, "torch._scaled_mm", _time_us(vrun, iters, stream))
+                except Exception as e:   # context only: report and go on
+                    log(f"[sweep] torch._scaled_mm unavailable for {dtype}: {e}")
+                    vendor = False
+            else:
+                line(None, "torch.matmul", _time_us(lambda: torch.matmul(a, b), iters, stream))
         del a, b, c
     dg.gemm_destroy(h)
     return 0
@@ -198,11 +204,11 @@ def main(argv=None) -> int:
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for scaling HBM counters)")
-    p.add_argument("--sweep", choices=["f16", "bf16"], default=None,
+    p.add_argument("--sweep", choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2"], default=None,
                    help="time every configuration on the shape sweep instead")
     p.add_argument("--sweep-iters", type=int, default=20)
     p.add_argument("--sweep-vendor", action="store_true",
-                   help="with --sweep: also time torch.matmul (context)")
+                   help="with --sweep: also time the vendor library (context)")
     args = p.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
