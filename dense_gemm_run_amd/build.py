@@ -20,8 +20,13 @@ SOURCES = ["gemm_api.cpp", "gemm_generic.hip", "gemm_mfma32x32.hip", "gemm_mfma1
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# The pipelined kernels unroll whole K-steps (hundreds of MFMAs with their
+# loads and LDS operations); the pragma-unroll size limit is raised so that
+# every such loop unrolls and the per-slot register arrays never fall back to
+# scratch memory (tests/test_codegen_cpu.py checks for scratch use).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-pragma-unroll-threshold=1000000",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(HERE, "..", "include")]
 
 

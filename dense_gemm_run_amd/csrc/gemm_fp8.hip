@@ -227,22 +227,27 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
             fa[set][o - FN] = read_a(sta, sl, o - FN);
     };
 
-    // ---- software pipeline.  Group it = [A loads of K-step it+LEAD (before
-    // the step's barrier), B loads of K-step it+SB (after it)]; the prologue
-    // issues groups -max(LEAD, SB) .. -1 (the parts that exist).  When K-step
+    // ---- software pipeline.  Vector-memory instructions are issued in
+    // groups, one per K-step: group it = [A loads of K-step it+LEAD (before
+    // the step's barrier), B loads of K-step it+SB (after it)].  The
+    // prologue issues groups -max(LEAD, SB) .. -1 (the parts that exist), in
+    // the same order within a group (the empty statements with a memory
+    // clobber keep the compiler from interleaving the parts).  When K-step
     // it waits for its B loads of K-step it+1 (the end of group it+1-SB),
     // groups it+2-SB .. it-1 and the A loads of group it were issued after
-    // them: at most (SB-2)*LOADS + A_LOADS loads may still be in flight.
+    // them: at most (SB-2)*LOADS + A_LOADS of this wavefront's loads may
+    // still be in flight.
 #pragma unroll
     for (int g = -LEAD; g < 0; ++g) {
         if (g + LEAD >= 0)
 #pragma unroll
             for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * BK, j);
+        asm volatile("" ::: "memory");
         if (g + SB >= 0)
 #pragma unroll
             for (int j = 0; j < B_LOADS; ++j) load_b(g + SB, (g + SB) * BK, j);
+        asm volatile("" ::: "memory");
     }
-    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 1) * LOADS));   // group -SB (B of K-step 0) landed
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);

@@ -36,9 +36,9 @@ FAMILIES = {
 def compile_family(fam, tmp):
     src, pat, count, ebytes, mnem, kdepth, outs = FAMILIES[fam]
     out = tmp / (fam + ".s")
-    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"),
-           "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    cmd = [HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     lines = out.read_text().split("\n")
@@ -50,6 +50,15 @@ def compile_family(fam, tmp):
             bm, bn, bk = g if len(g) == 3 else (256, 256, g[0])
             end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
             found[m.group(1)] = Kernel(fam, bm, bn, bk, ebytes, mnem, kdepth, outs, lines[i:end])
+    # per-kernel scratch use from the kernel descriptors
+    for i, l in enumerate(lines):
+        m = re.match(r"^\s*\.amdhsa_kernel (\S+)", l)
+        if m and m.group(1) in found:
+            for l2 in lines[i:i + 80]:
+                m2 = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", l2)
+                if m2:
+                    found[m.group(1)].scratch = int(m2.group(1))
+                    break
     assert len(found) == count, sorted(found)
     return found
 
@@ -63,6 +72,7 @@ class Kernel:
         self.b_loads = bk * bn * ebytes // 1024 // 4
         self.lead = 256 // (bk * ebytes)                  # A register slots
         self.sb = 4 if bk * ebytes == 64 else 2           # B stages
+        self.scratch = None
 
 
 @pytest.fixture(scope="module")
@@ -112,7 +122,10 @@ def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels)
             expect += ["g"] * a_loads + (["L"] * b_loads if g + sb >= 0 else [])
         assert pro == expect, (name, pro)
         pro_waits = [e[1] for e in ev[:bars[0]] if isinstance(e, tuple)]
-        assert pro_waits and pro_waits[-1] == (sb - 1) * loads, (name, pro_waits)
+        # before the prologue barrier at most the loads issued after the B
+        # loads of K-step 0 may be in flight (the compiler may replace the
+        # counted wait by stricter ones of its own)
+        assert pro_waits and pro_waits[-1] <= (sb - 1) * loads, (name, pro_waits)
         # a K-step issues its A loads before its barrier and its B loads
         # after it, so between two barriers: B loads of the previous step,
         # then A loads of this one
@@ -145,3 +158,11 @@ def test_accumulators_stay_in_place(kernels):
         assert not [x for x in between if x.startswith(("v_accvgpr_write", "v_accvgpr_mov", "v_accvgpr_read"))], name
         # no accumulator is written before the first MFMA (it starts from 0)
         assert not [x for x in text[:first] if x.startswith("v_accvgpr_write")], name
+
+
+def test_no_kernel_uses_scratch(kernels):
+    # every loop over slots, stages and tiles is unrolled, so the register
+    # arrays stay in registers: a rolled loop would index them at run time
+    # and move them to scratch memory
+    for name, kn in kernels.items():
+        assert kn.scratch == 0, (name, kn.scratch)
