@@ -116,8 +116,8 @@ def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
 
 
 SWEEP_SQUARE = [512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192]
-SWEEP_SKINNY = [(m, 4096, 4096) for m in (16, 32, 64, 128, 256, 512)] + \
-               [(m, 14336, 4096) for m in (16, 64, 256)]
+SWEEP_SKINNY = [(m, 4096, 4096) for m in (1, 4, 8, 16, 32, 64, 128, 256, 512)] + \
+               [(m, 14336, 4096) for m in (16, 64, 256)] + [(16, 4096, 14336), (64, 4096, 14336)]
 SWEEP_PREFILL = [(8192, 12288, 4096), (8192, 4096, 4096), (8192, 14336, 4096), (8192, 4096, 14336)]
 
 

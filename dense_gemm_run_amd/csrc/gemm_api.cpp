@@ -21,7 +21,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5 };
 
 struct Entry {
     Config cfg;
@@ -51,6 +51,16 @@ const Entry kTable[] = {
     // 8-bit inputs (E4M3, E5M2), bf16 output; bk in elements (= bytes)
     {{13, 256, 256, 64, 4, 256, 0x18, 1, 1, "fp8_256x256x64"}, kFp8},
     {{14, 256, 256, 128, 4, 256, 0x18, 1, 1, "fp8_256x256x128"}, kFp8},
+    // few rows: bm = rows of A per workgroup (all of M, normally), bn =
+    // columns of the strip, bk = K per step; the wavefronts (threads / 64)
+    // of a workgroup split K
+    {{15, 16, 16, 64, 1, 512, 0x6, 1, 1, "skinny_16x16x64"}, kSkinny},
+    {{16, 32, 16, 64, 1, 512, 0x6, 1, 1, "skinny_32x16x64"}, kSkinny},
+    {{17, 64, 16, 32, 1, 256, 0x6, 1, 1, "skinny_64x16x32"}, kSkinny},
+    {{18, 16, 32, 64, 1, 256, 0x6, 1, 1, "skinny_16x32x64"}, kSkinny},
+    {{19, 32, 32, 64, 1, 256, 0x6, 1, 1, "skinny_32x32x64"}, kSkinny},
+    {{20, 64, 32, 32, 1, 256, 0x6, 1, 1, "skinny_64x32x32"}, kSkinny},
+    {{21, 16, 16, 32, 1, 512, 0x6, 1, 1, "skinny_16x16x32"}, kSkinny},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -147,6 +157,11 @@ bool accepts(const Entry& e, const Problem& p)
 // Shape classes (measured with bench.py --sweep over square 512^3 .. 8192^3,
 // few-row products and the prefill projections):
 //  * N <= 4: the matrix-vector kernel (it streams A at HBM bandwidth);
+//  * M <= 128 (few rows, B streamed once): the split-K strip kernel, whose
+//    N/16 or N/32 workgroups fill the chip where the tiled kernels have a
+//    few dozen tiles (M = 16, N = K = 4096: 44 against 18 TFLOP/s) - up to
+//    32 rows with strips of 32 columns for N >= 8192, and from 33 rows only
+//    for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles were faster);
 //  * small (M*N*K*batch < 128^3), fp32 or unaligned: the generic kernel;
 //  * at least 128 output tiles of 256 x 256 over the whole batch (half the
 //    256 CUs or more): the 16x16x32 kernel at 256 x 256.  At one wave of
@@ -167,6 +182,15 @@ int select(const Problem& p)
     if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
     if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
+    if (p.M <= 128) {
+        // few rows: the split-K strip kernel, except for wide B (N >= 8192)
+        // from 33 rows up, where the 128 x 128 tiles already give enough
+        // workgroups
+        const bool wide = p.N >= 8192;
+        if (p.M <= 16) return wide ? 18 : (p.K >= 8192 ? 15 : 21);
+        if (p.M <= 32) return wide ? 19 : 16;
+        if (!wide) return p.M <= 64 ? 19 : 20;
+    }
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
     return t256 >= 128 ? 6 : 12;
 }
@@ -187,6 +211,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
     case kMfma16x16: err = launch_mfma16x16(e.cfg, la); break;
     case kGemv: err = launch_gemv(e.cfg, la); break;
     case kFp8: err = launch_fp8(e.cfg, la); break;
+    case kSkinny: err = launch_skinny(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

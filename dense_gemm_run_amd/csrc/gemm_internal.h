@@ -91,5 +91,6 @@ hipError_t launch_mfma32x32(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_mfma16x16(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_gemv(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_fp8(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_skinny(const Config& cfg, const LaunchArgs& a);
 
 }  // namespace dgr

@@ -135,7 +135,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(15))
+@pytest.mark.parametrize("cid", range(22))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -281,3 +281,21 @@ def test_8bit_inputs_select_their_kernels():
                                          1024 * 1024, 1024 * 1024, 3) == 0
     assert dg.gemm_select_config_batched(A, Bb, Cb, 4, 1024, 1024, 1024, 1024 * 1024,
                                          1024 * 1024, 1024 * 1024 + 8, 3) in fp8_cfgs
+
+
+def test_few_rows_select_the_strip_kernel():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
+    for M, N, K in [(16, 4096, 4096), (1, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
+                    (128, 4096, 4096), (16, 14336, 4096), (16, 4096, 14336), (32, 14336, 4096)]:
+        for dt in (1, 2):
+            n = name(A, Bb, Cb, M, N, K, dt)
+            assert n.startswith("skinny"), (M, N, K, n)
+            info = dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb, M, N, K, dt))
+            assert info["bm"] >= min(M, 32) or M > 64
+    # wide B from 33 rows up, many rows, fp32, 8-bit inputs, unaligned rows: not
+    for args in [(A, Bb, Cb, 64, 14336, 4096, 2), (A, Bb, Cb, 256, 4096, 4096, 2),
+                 (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4096, 3),
+                 (A, Bb, Cb, 16, 4096, 4092, 2)]:
+        assert not name(*args).startswith("skinny"), args
