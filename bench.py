@@ -52,21 +52,27 @@ def log(*a):
 
 # Kernel source of each configuration family (by configuration-name prefix).
 KERNEL_FILES = {"mfma16x16": "gemm_mfma16x16.hip", "mfma32x32": "gemm_mfma32x32.hip",
-                "fp8": "gemm_fp8.hip", "gemv": "gemm_gemv.hip", "generic": "gemm_generic.hip"}
-# What every kernel's code and launch depend on besides its own file.
-SHARED_FILES = ["gemm_device.h", "gemm_internal.h", "gemm_api.cpp"]
+                "fp8": "gemm_fp8.hip", "gemv": "gemm_gemv.hip", "generic": "gemm_generic.hip",
+                "skinny": "gemm_skinny.hip"}
+# What every kernel's code depends on besides its own file.
+SHARED_FILES = ["gemm_device.h", "gemm_internal.h"]
 
 
 def kernel_source_digest(kernel_cfg: str) -> str:
-    """sha256 (16 hex digits) of the sources configuration ``kernel_cfg``
-    is built and launched from: its kernel file and the shared headers and
-    host table."""
+    """sha256 (16 hex digits) of what configuration ``kernel_cfg`` runs: its
+    kernel file, the shared headers, and its own entry of the configuration
+    table (tile, K-step, workgroup size and order, as the library reports
+    them)."""
+    import dense_gemm_run_amd as dg
     fam = next(f for p, f in KERNEL_FILES.items() if kernel_cfg.startswith(p))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_run_amd", "csrc")
     for f in sorted([fam] + SHARED_FILES):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
+    info = next(dg.gemm_config_info(i) for i in range(dg.gemm_config_count())
+                if dg.gemm_config_info(i)["name"] == kernel_cfg)
+    h.update(json.dumps({k: info[k] for k in sorted(info) if k != "id"}).encode())
     return h.hexdigest()[:16]
 
 

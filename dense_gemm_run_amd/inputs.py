@@ -94,6 +94,10 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              "square 4096^3 with E5M2 inputs, N(0,1) rounded to E5M2, bf16 output"),
     Workload("fp8_e4m3_8192x8192x8192", 8192, 8192, 8192, "fp8_e4m3", "normal", 15,
              "square 8192^3 with E4M3 inputs, N(0,1) rounded to E4M3, bf16 output"),
+    Workload("bf16_tokens16_16x4096x4096", 16, 4096, 4096, "bf16", "prefill", 16,
+             "16 tokens through a 4096 x 4096 projection (weights B [K, N])"),
+    Workload("bf16_tokens128_128x4096x4096", 128, 4096, 4096, "bf16", "prefill", 17,
+             "128 tokens through a 4096 x 4096 projection (weights B [K, N])"),
 ]}
 
 # Order in which the four prefill projections of one layer run.
