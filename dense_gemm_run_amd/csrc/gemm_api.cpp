@@ -61,6 +61,11 @@ const Entry kTable[] = {
     {{19, 32, 32, 64, 1, 256, 0x6, 1, 1, "skinny_32x32x64"}, kSkinny},
     {{20, 64, 32, 32, 1, 256, 0x6, 1, 1, "skinny_64x32x32"}, kSkinny},
     {{21, 16, 16, 32, 1, 512, 0x6, 1, 1, "skinny_16x16x32"}, kSkinny},
+    // the same for 8-bit inputs (bk in elements = bytes)
+    {{22, 16, 16, 128, 1, 512, 0x18, 1, 1, "skinny8_16x16x128"}, kSkinny},
+    {{23, 32, 16, 128, 1, 512, 0x18, 1, 1, "skinny8_32x16x128"}, kSkinny},
+    {{24, 16, 32, 128, 1, 256, 0x18, 1, 1, "skinny8_16x32x128"}, kSkinny},
+    {{25, 32, 32, 128, 1, 256, 0x18, 1, 1, "skinny8_32x32x128"}, kSkinny},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -177,6 +182,12 @@ int select(const Problem& p)
     if (p.dtype == kF32) return 0;
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
+        if (p.M <= 64) {   // few rows: the strip kernel, as for 16-bit inputs
+            const bool wide = p.N >= 8192;
+            if (p.M <= 16) return wide ? 24 : 22;
+            if (p.M <= 32) return wide ? 25 : 23;
+            if (!wide) return 25;
+        }
         return 13;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;

@@ -1,6 +1,7 @@
 // Few-row products: C = A·B with small M (a batch of tokens against a weight
-// matrix B [K, N]), fp16/bf16, rows 16-byte aligned (K and N multiples of 8
-// elements, A and B 16-byte aligned, C 8-byte aligned).
+// matrix B [K, N]), fp16/bf16 or 8-bit (E4M3 / E5M2, bf16 C) inputs, rows
+// 16-byte aligned (K and N multiples of 16 bytes of A's and B's rows, N a
+// multiple of 8, A, B and C 16-byte aligned).
 //
 // With few rows of A, every element of B is used M times at most, so the
 // product is bound by streaming B from HBM (arithmetic intensity about M
@@ -23,10 +24,11 @@
 //    from global memory into registers 4 K-steps ahead (A is small and stays
 //    in the L2 cache, so a shorter lead covers it, and fewer registers hold
 //    it);
-//  * the MFMA is v_mfma_f32_16x16x32 (the compiler's builtin), given the B
-//    fragment (two 16-bit
-//    transpose reads: each lane gets 8 consecutive K of one column) first,
-//    so each lane accumulates 4 consecutive columns of one row;
+//  * the MFMA is v_mfma_f32_16x16x32 for 16-bit inputs and
+//    v_mfma_f32_16x16x128_f8f6f4 for 8-bit ones (compiler builtins), given
+//    the B fragment first (transpose reads: each lane gets 8 consecutive K
+//    of one column from a 16-bit read pair, or 32 from four 8-bit reads), so
+//    each lane accumulates 4 consecutive columns of one row;
 //  * at the end the partial sums of the wavefronts are added through LDS,
 //    rounded (nearest even) and stored, skipping rows >= M.
 // Out-of-range pieces read zeros through the buffer range check, as in the
@@ -66,44 +68,81 @@ constexpr int after_prologue(int t, int b_loads, int a_loads)
     return (kStages - 1 - t) * b_loads + (kStages - t < kLeadA ? kStages - t : kLeadA) * a_loads;
 }
 
-// c += b-fragment x a-fragment (16x16x32).  The compiler's builtin, not
-// inline assembly: the tails of this kernel merge into one epilogue, and the
-// compiler copies accumulators there; it only waits out the MFMA latency
-// before such copies when it knows the instruction is an MFMA.
-template <typename T> struct Mfma;
-template <> struct Mfma<_Float16> {
-    static __device__ __forceinline__ void acc(f32x4& c, const u32x4& b, const u32x4& a)
+// Element types of A and B.  Per lane, an MFMA operand fragment is FRAG
+// bytes of one row of A (or column of B): KI consecutive K.  c += b-fragment
+// x a-fragment.  The compiler's builtins, not inline assembly: the tails of
+// this kernel merge into one epilogue, and the compiler copies accumulators
+// there; it only waits out the MFMA latency before such copies when it knows
+// the instruction is an MFMA.
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+struct E4M3 {};
+struct E5M2 {};
+template <typename E> struct Elem;
+template <> struct Elem<_Float16> {
+    using Out = _Float16;
+    using Frag = u32x4;
+    static constexpr int BYTES = 2, KI = 32;
+    static __device__ __forceinline__ void mma(f32x4& c, const Frag& b, const Frag& a)
     {
         c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, b), __builtin_bit_cast(f16x8, a), c, 0,
                                                    0, 0);
     }
 };
-template <> struct Mfma<__bf16> {
-    static __device__ __forceinline__ void acc(f32x4& c, const u32x4& b, const u32x4& a)
+template <> struct Elem<__bf16> {
+    using Out = __bf16;
+    using Frag = u32x4;
+    static constexpr int BYTES = 2, KI = 32;
+    static __device__ __forceinline__ void mma(f32x4& c, const Frag& b, const Frag& a)
     {
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a), c,
                                                     0, 0, 0);
     }
 };
+// 8-bit: operand format 0 = E4M3, 1 = E5M2 for both operands; the scale
+// operands are 0, which the compiler emits as the unscaled instruction.
+template <int FMT> struct Elem8 {
+    using Out = __bf16;
+    using Frag = u32x8;
+    static constexpr int BYTES = 1, KI = 128;
+    static __device__ __forceinline__ void mma(f32x4& c, const Frag& b, const Frag& a)
+    {
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_bit_cast(i32x8, b),
+                                                              __builtin_bit_cast(i32x8, a), c, FMT, FMT, 0, 0, 0, 0);
+    }
+};
+template <> struct Elem<E4M3> : Elem8<0> {};
+template <> struct Elem<E5M2> : Elem8<1> {};
 
-template <typename T, int BMS, int BN, int BK, int W>
-__global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, const T* B, T* C, int M, int N, int K,
+template <typename E, int BMS, int BN, int BK, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const unsigned char* A, const unsigned char* B,
+                                                              typename Elem<E>::Out* C, int M, int N, int K,
                                                               Batch bt)
 {
+    using Frag = typename Elem<E>::Frag;
+    using Out = typename Elem<E>::Out;
+    constexpr int ES = Elem<E>::BYTES;               // bytes per element of A and B
+    constexpr int KI = Elem<E>::KI;                  // K per MFMA
+    constexpr int FRAG = (int)sizeof(Frag);          // fragment bytes per lane (KI/4 * ES)
     constexpr int FM = BMS / 16, FN = BN / 16;       // 16x16 tiles
-    constexpr int NS = BK / 32;                      // K-slices per K-step
-    constexpr int ROW_B = BN * 2;                    // bytes of one B row in LDS
+    constexpr int NS = BK / KI;                      // K-slices per K-step
+    constexpr int ROW_B = BN * ES;                   // bytes of one B row in LDS
     constexpr int STEP_B = BK * ROW_B;               // bytes of one K-step of B
     constexpr int B_LOADS = STEP_B / 1024;           // direct-to-LDS loads per K-step
-    constexpr int A_LOADS = NS * FM;                 // 16-byte-per-lane A loads per K-step
+    constexpr int AP = FRAG / 16;                    // 16-byte loads per A fragment
+    constexpr int A_LOADS = NS * FM * AP;            // A loads per K-step
     constexpr int L = B_LOADS + A_LOADS;             // vector-memory instructions per K-step
-    // Rows k and k+8 of a stage land on the same banks; the transpose reads of
-    // a half-wavefront take rows r..r+3 and r+8..r+11, so rows with k & 8 are
-    // XOR-ed by half of the bank span those 4 rows touch.
-    constexpr int SWZ = BN == 16 ? 128 : 32;
+    // The transpose reads of a half-wavefront take rows r.. of two row
+    // groups that land on the same banks (16-bit: rows k and k+8, 4 rows per
+    // group; 8-bit: rows k and k+32, 8 rows per group): rows with that row
+    // bit set are XOR-ed by half of the bank span a group touches.
+    constexpr int SWZ_BIT = ES == 2 ? 8 : 32;
+    constexpr int SWZ = BN == 16 ? 128 : (ES == 2 ? 32 : 16);
     static_assert(BN == 16 || BN == 32, "strip width");
-    static_assert(BK == 32 || BK == 64, "K-step");
+    static_assert(BK % KI == 0 && (BK == KI || BK == 2 * KI), "K-step");
     static_assert(BMS % 16 == 0 && BMS <= 64, "rows");
+    static_assert(STEP_B % 1024 == 0, "a K-step of B is whole 1 KB loads");
     static_assert(kStages * L <= 63, "loads in flight must fit the vmcnt field");
     static_assert(kStages * W * STEP_B <= 160 * 1024, "LDS");
     static_assert(BMS * BN * 4 <= kStages * STEP_B, "partial sums must fit a wavefront's slices of the stages");
@@ -117,46 +156,57 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, cons
     const int tiles_m = cdiv_i(M, BMS), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, 1, true, b, tm, tn);
-    A += b * bt.sa;
-    B += b * bt.sb;
+    A += b * bt.sa * ES;
+    B += b * bt.sb * ES;
     C += b * bt.sc;
     const int m0 = tm * BMS, n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * 2u);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * ES);
 
     // A fragment of tile mi, K-slice s: lane -> row m0 + 16*mi + lane%16, K
-    // 32*s + 8*(lane/16) .. +7 of the step (kOOB for rows >= M; pieces at or
-    // past K per step).
+    // KI*s + (KI/4)*(lane/16) .. of the step, AP pieces of 16 bytes (kOOB for
+    // rows >= M; pieces at or past K per step).
     unsigned a_voff[FM];
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi) {
         const int m = m0 + 16 * mi + (lane & 15);
-        a_voff[mi] = m < M ? ((unsigned)m * (unsigned)K + 8u * (unsigned)(lane >> 4)) * 2u : kOOB;
+        a_voff[mi] = m < M ? (unsigned)m * (unsigned)K * ES + (unsigned)(FRAG * (lane >> 4)) : kOOB;
     }
     // B load j of a step: lane -> LDS byte p = 1024*j + 16*lane of the stage
-    // slice, holding logical byte p ^ swizzle = row k, piece c: global
-    // (k*N + n0 + 8c)*2 relative to the step's first row (kOOB past N).
+    // slice, holding logical byte p ^ swizzle = row k, 16-byte piece c:
+    // global k*N*ES + n0*ES + 16c relative to the step's first row (kOOB past N).
     unsigned b_voff[B_LOADS];
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j) {
         const int p = 1024 * j + 16 * lane;
-        const int lg = p ^ (((p / ROW_B) & 8) ? SWZ : 0);
+        const int lg = p ^ (((p / ROW_B) & SWZ_BIT) ? SWZ : 0);
         const int k = lg / ROW_B, c = (lg % ROW_B) / 16;
-        const int col = n0 + 8 * c;
-        b_voff[j] = col < N ? ((unsigned)k * (unsigned)N + (unsigned)col) * 2u : kOOB;
+        const int col = n0 + c * (16 / ES);
+        b_voff[j] = col < N ? ((unsigned)k * (unsigned)N + (unsigned)col) * ES : kOOB;
     }
-    // B fragment of tile ni, K-slice s by two transpose reads: in 16-lane
-    // group g, lane 4r+q points at rows 32s + 8g + r and 32s + 8g + 4 + r,
-    // columns 16*ni + 4q .. +3 (the swizzle only depends on bit 3 of the row).
-    int b_rd[FN][2];
+    // B fragment of tile ni, K-slice s by transpose reads (RD of them):
+    //  16-bit: in 16-lane group g, lane 4r+q points at rows KI*s + 8g + 4h + r
+    //    (h = 0, 1), columns 16*ni + 4q .. +3: lane i gets column i over 4 rows;
+    //  8-bit: in 16-lane group g, lane 2r+q points at rows KI*s + 32g + 8h + r
+    //    (h = 0..3), bytes 8q .. 8q+7 of the 16 columns of tile ni: lane i gets
+    //    column i over 8 rows.
+    constexpr int RD = ES == 2 ? 2 : 4;
+    int b_rd[FN][RD];
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int k = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
-            const int lg = k * ROW_B + (16 * ni + 4 * (lane & 3)) * 2;
-            b_rd[ni][h] = lg ^ ((k & 8) ? SWZ : 0);
+        for (int h = 0; h < RD; ++h) {
+            int k, byte;
+            if constexpr (ES == 2) {
+                k = 8 * (lane >> 4) + 4 * h + ((lane & 15) >> 2);
+                byte = (16 * ni + 4 * (lane & 3)) * 2;
+            } else {
+                k = 32 * (lane >> 4) + 8 * h + ((lane & 15) >> 1);
+                byte = 16 * ni + 8 * (lane & 1);
+            }
+            const int lg = k * ROW_B + byte;
+            b_rd[ni][h] = lg ^ ((k & SWZ_BIT) ? SWZ : 0);
         }
 
     const int nsteps = cdiv_i(K, BK);
@@ -168,7 +218,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, cons
         const int krem = K - k0;
         const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
         const __amdgpu_buffer_rsrc_t rbk =
-            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
+            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N * ES, (unsigned)rows * (unsigned)N * ES);
 #pragma unroll
         for (int l = 0; l < B_LOADS; ++l) {
             const unsigned off = b_voff[l];
@@ -178,7 +228,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, cons
         }
         asm volatile("" ::: "memory");
     };
-    u32x4 areg[kStages][NS][FM];
+    Frag areg[kStages][NS][FM];
     // A fragments of K-step j -> slot sl.  Pieces at or past K read zeros:
     // their offset is forced to kOOB with a mask (a select here became a
     // branch around the load).
@@ -186,16 +236,43 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, cons
         const int k0 = __builtin_amdgcn_readfirstlane((wave + W * j) * BK);
         const int krem = K - k0;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const unsigned past = 0u - (unsigned)(32 * s + 8 * (lane >> 4) >= krem);
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int mi = 0; mi < FM; ++mi) {
-                const unsigned off = (a_voff[mi] + 64u * s) | (past & kOOB);
-                areg[sl][s][mi] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, (k0 < K ? k0 : 0) * 2, 0));
+                u32x4 piece[AP];
+#pragma unroll
+                for (int h = 0; h < AP; ++h) {
+                    const int kk = KI * s + (KI / 4) * (lane >> 4) + (16 / ES) * h;   // first K of the piece
+                    const unsigned past = 0u - (unsigned)(kk >= krem);
+                    const unsigned off = (a_voff[mi] + (unsigned)((KI * s + (16 / ES) * h) * ES)) | (past & kOOB);
+                    piece[h] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, (k0 < K ? k0 : 0) * ES, 0));
+                }
+                if constexpr (AP == 1)
+                    areg[sl][s][mi] = __builtin_bit_cast(Frag, piece[0]);
+                else
+                    areg[sl][s][mi] = __builtin_bit_cast(Frag, __builtin_shufflevector(piece[0], piece[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
-        }
         asm volatile("" ::: "memory");
+    };
+    // Fragment of tile ni, K-slice s from stage st.
+    auto read_b = [&](int st, int s, int ni) __attribute__((always_inline)) -> Frag {
+        const lds_byte* base = stage(st) + wave * STEP_B + KI * s * ROW_B;
+        if constexpr (ES == 2) {
+            const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3)))*)(base + b_rd[ni][0]));
+            const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (s16x4 __attribute__((address_space(3)))*)(base + b_rd[ni][1]));
+            return __builtin_bit_cast(Frag, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            i32x2 h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                h[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 __attribute__((address_space(3)))*)(base + b_rd[ni][i]));
+            const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3));
+            const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3));
+            return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     };
 
     f32x4 acc[FN][FM];
@@ -221,25 +298,18 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, cons
                     __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(count_c)::value));
         asm volatile("" ::: "memory");
-        u32x4 bf[NS][FN];
+        Frag bf[NS][FN];
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int ni = 0; ni < FN; ++ni) {
-                const lds_byte* base = stage(st) + wave * STEP_B + 32 * s * ROW_B;
-                const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (s16x4 __attribute__((address_space(3)))*)(base + b_rd[ni][0]));
-                const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (s16x4 __attribute__((address_space(3)))*)(base + b_rd[ni][1]));
-                bf[s][ni] = __builtin_bit_cast(u32x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
+            for (int ni = 0; ni < FN; ++ni) bf[s][ni] = read_b(st, s, ni);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the stage is read: it may be refilled
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
-                for (int mi = 0; mi < FM; ++mi) Mfma<T>::acc(acc[ni][mi], bf[s][ni], areg[st][s][mi]);
+                for (int mi = 0; mi < FM; ++mi) Elem<E>::mma(acc[ni][mi], bf[s][ni], areg[st][s][mi]);
         if (refill) issue_b(st, j + kStages);
         if (refill || fetch_a) issue_a((st + kLeadA) % kStages, j + kLeadA);
     };
@@ -318,33 +388,40 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const T* A, cons
         const int row = m0 + m, col = n0 + n;
         if (row < M && col < N) {
             u32x2 v;
-            v[0] = pack2<T>(sum[0], sum[1]);
-            v[1] = pack2<T>(sum[2], sum[3]);
+            v[0] = pack2<Out>(sum[0], sum[1]);
+            v[1] = pack2<Out>(sum[2], sum[3]);
             *(u32x2*)(C + (size_t)row * N + col) = v;
         }
     }
 }
 
-template <typename T>
-hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
+template <typename E>
+hipError_t launch_e(const Config& cfg, const LaunchArgs& a)
 {
     const int tiles = cdiv_i(a.M, cfg.bm) * cdiv_i(a.N, cfg.bn);
-    const T* A = static_cast<const T*>(a.A);
-    const T* B = static_cast<const T*>(a.B);
-    T* C = static_cast<T*>(a.C);
+    const unsigned char* A = static_cast<const unsigned char*>(a.A);
+    const unsigned char* B = static_cast<const unsigned char*>(a.B);
+    auto* C = static_cast<typename Elem<E>::Out*>(a.C);
 #define DGR_LAUNCH(BMS_, BN_, BK_, W_)                                                                  \
     if (cfg.bm == BMS_ && cfg.bn == BN_ && cfg.bk == BK_ && cfg.threads == 64 * W_) {                  \
-        hipLaunchKernelGGL((gemm_skinny_kernel<T, BMS_, BN_, BK_, W_>), dim3(tiles * a.batch.count),   \
+        hipLaunchKernelGGL((gemm_skinny_kernel<E, BMS_, BN_, BK_, W_>), dim3(tiles * a.batch.count),   \
                            dim3(64 * W_), 0, a.stream, A, B, C, a.M, a.N, a.K, a.batch);               \
         return hipGetLastError();                                                                      \
     }
-    DGR_LAUNCH(16, 16, 64, 8)
-    DGR_LAUNCH(32, 16, 64, 8)
-    DGR_LAUNCH(64, 16, 32, 4)
-    DGR_LAUNCH(16, 32, 64, 4)
-    DGR_LAUNCH(32, 32, 64, 4)
-    DGR_LAUNCH(64, 32, 32, 4)
-    DGR_LAUNCH(16, 16, 32, 8)
+    if constexpr (Elem<E>::BYTES == 2) {
+        DGR_LAUNCH(16, 16, 64, 8)
+        DGR_LAUNCH(32, 16, 64, 8)
+        DGR_LAUNCH(64, 16, 32, 4)
+        DGR_LAUNCH(16, 32, 64, 4)
+        DGR_LAUNCH(32, 32, 64, 4)
+        DGR_LAUNCH(64, 32, 32, 4)
+        DGR_LAUNCH(16, 16, 32, 8)
+    } else {
+        DGR_LAUNCH(16, 16, 128, 8)
+        DGR_LAUNCH(32, 16, 128, 8)
+        DGR_LAUNCH(16, 32, 128, 4)
+        DGR_LAUNCH(32, 32, 128, 4)
+    }
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;
 }
@@ -353,8 +430,10 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
 
 hipError_t launch_skinny(const Config& cfg, const LaunchArgs& a)
 {
-    if (a.dtype == kF16) return launch_t<_Float16>(cfg, a);
-    if (a.dtype == kBF16) return launch_t<__bf16>(cfg, a);
+    if (a.dtype == kF16) return launch_e<_Float16>(cfg, a);
+    if (a.dtype == kBF16) return launch_e<__bf16>(cfg, a);
+    if (a.dtype == kFP8E4M3) return launch_e<E4M3>(cfg, a);
+    if (a.dtype == kFP8E5M2) return launch_e<E5M2>(cfg, a);
     return hipErrorInvalidValue;
 }
 

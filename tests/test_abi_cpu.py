@@ -294,8 +294,14 @@ def test_few_rows_select_the_strip_kernel():
             assert n.startswith("skinny"), (M, N, K, n)
             info = dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb, M, N, K, dt))
             assert info["bm"] >= min(M, 32) or M > 64
-    # wide B from 33 rows up, many rows, fp32, 8-bit inputs, unaligned rows: not
+    # wide B from 33 rows up, many rows, fp32, unaligned rows: not
     for args in [(A, Bb, Cb, 64, 14336, 4096, 2), (A, Bb, Cb, 256, 4096, 4096, 2),
-                 (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4096, 3),
-                 (A, Bb, Cb, 16, 4096, 4092, 2)]:
+                 (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4092, 2)]:
         assert not name(*args).startswith("skinny"), args
+    # 8-bit inputs take the 8-bit strip configurations, up to 64 rows for N < 8192
+    for M, N, K in [(1, 4096, 4096), (16, 4096, 14336), (32, 14336, 4096), (64, 4096, 4096)]:
+        for dt in (3, 4):
+            info = dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb, M, N, K, dt))
+            assert info["name"].startswith("skinny8") and info["dtype_mask"] == 0x18, (M, N, K, info)
+    for M, N, K in [(64, 14336, 4096), (128, 4096, 4096), (16, 4096, 4088)]:
+        assert not name(A, Bb, Cb, M, N, K, 3).startswith("skinny"), (M, N, K)

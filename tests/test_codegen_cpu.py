@@ -166,3 +166,22 @@ def test_no_kernel_uses_scratch(kernels):
     # and move them to scratch memory
     for name, kn in kernels.items():
         assert kn.scratch == 0, (name, kn.scratch)
+
+
+def test_strip_kernel_uses_no_scratch_and_unscaled_8bit_mfma(tmp_path):
+    """The few-row kernel (all element types) keeps its register arrays in
+    registers, and its 8-bit MFMAs are the unscaled instruction (the
+    builtin is the scaled one with zero scales)."""
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    out = tmp_path / "skinny.s"
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_skinny.hip"),
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
+    assert len(sizes) >= 8 and all(x == 0 for x in sizes), sizes
+    assert "v_mfma_f32_16x16x128_f8f6f4" in text
+    assert "v_mfma_scale" not in text

@@ -29,8 +29,11 @@ def note(msg):
     sys.stdout.flush()
 
 
-def skinny_configs():
-    return [c for c in range(dg.gemm_config_count()) if dg.gemm_config_info(c)["name"].startswith("skinny")]
+def skinny_configs(eight=False):
+    """The few-row configurations for 16-bit (or, with eight, 8-bit) inputs."""
+    return [c for c in range(dg.gemm_config_count())
+            if dg.gemm_config_info(c)["name"].startswith("skinny")
+            and (dg.gemm_config_info(c)["dtype_mask"] == 0x18) == eight]
 
 
 def check(A, B, dtype, c):
@@ -42,23 +45,30 @@ def check(A, B, dtype, c):
     assert rep["ok"], rep
 
 
-@pytest.mark.parametrize("cid", range(15, 22))
+@pytest.mark.parametrize("cid", range(15, 26))
 def test_every_k_step_count(cid):
     if cid >= dg.gemm_config_count() or not dg.gemm_config_info(cid)["name"].startswith("skinny"):
         pytest.skip("not a few-row configuration")
     info = dg.gemm_config_info(cid)
+    eight = info["dtype_mask"] == 0x18
+    dtype = "fp8_e4m3" if eight else "bf16"
+    per16 = 16 if eight else 8                 # elements per 16 bytes
     waves = info["threads"] // 64
     per_step = info["bk"] * waves            # K covered by one K-step of every wavefront
     for steps in [1, 2, 6, 7, 8, 13, 14, 15, 16]:
-        K = steps * per_step - (24 if steps % 2 else 0)   # odd counts end with a ragged step
-        M, N = info["bm"] - 3, 3 * info["bn"] + 8
-        A, B = make_operands(M, N, K, "bf16", "normal", 500 + steps)
+        K = steps * per_step - (3 * per16 if steps % 2 else 0)   # odd counts end with a ragged step
+        M, N = info["bm"] - 3, 3 * info["bn"] + 2 * per16
+        A, B = make_operands(M, N, K, dtype, "normal", 500 + steps)
         a, b = A.cuda(), B.cuda()
         assert accepts(cid, a, b, M, N, K)
         note(f"[skinny] config {cid} {info['name']} K-steps/wavefront {steps} shape {(M, N, K)}")
         c = dg.gemm(a, b, config=cid)
         torch.cuda.synchronize()
-        check(A, B, "bf16", c)
+        if eight:
+            from test_gpu_fp8 import check as check8
+            check8(A, B, dtype, c)
+        else:
+            check(A, B, dtype, c)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -124,3 +134,36 @@ def test_few_row_shapes_in_the_selected_configuration(shape):
     note(f"[skinny] selected {dg.gemm_config_info(cid)['name']} for {shape}")
     assert dg.gemm_config_info(cid)["name"].startswith("skinny")
     check(A, B, "bf16", c)
+
+
+def test_8bit_few_rows_batched_guarded_and_selected():
+    from test_gpu_fp8 import check as check8
+    for dtype in ("fp8_e4m3", "fp8_e5m2"):
+        A, B = make_batched_operands(3, 24, 544, 1552, dtype, "normal", 640)
+        a, b = A.cuda(), B.cuda()
+        for cid in skinny_configs(eight=True):
+            note(f"[skinny] 8-bit batched {dtype} config {cid}")
+            c = dg.gemm_batched(a, b, config=cid)
+            torch.cuda.synchronize()
+            check8(A, B, dtype, c)
+    M, N, K = 21, 208, 3008
+    A, B = make_operands(M, N, K, "fp8_e4m3", "normal", 641)
+    guard = 2048
+    buf = torch.full((guard + M * N + guard,), 77.0, dtype=torch.bfloat16, device="cuda")
+    pattern = buf.clone()
+    out = buf[guard:guard + M * N].view(M, N)
+    for cid in skinny_configs(eight=True):
+        note(f"[skinny] 8-bit guards config {cid}")
+        dg.gemm(A.cuda(), B.cuda(), out=out, config=cid)
+        torch.cuda.synchronize()
+        assert torch.equal(buf[:guard], pattern[:guard]) and torch.equal(buf[guard + M * N:], pattern[guard + M * N:])
+        check8(A, B, "fp8_e4m3", out)
+    for M, N, K in [(16, 4096, 4096), (64, 4096, 4096), (32, 14336, 4096), (16, 4096, 14336)]:
+        A, B = make_operands(M, N, K, "fp8_e4m3", "normal", 642)
+        a, b = A.cuda(), B.cuda()
+        c = dg.gemm(a, b)
+        torch.cuda.synchronize()
+        cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, 3)
+        note(f"[skinny] 8-bit selected {dg.gemm_config_info(cid)['name']} for {(M, N, K)}")
+        assert dg.gemm_config_info(cid)["name"].startswith("skinny8")
+        check8(A, B, "fp8_e4m3", c)

@@ -26,8 +26,23 @@ def const(name):
 
 K_STAGES = const("kStages")
 K_LEAD_A = const("kLeadA")
-CONFIGS = [tuple(int(x) for x in m.groups())
-           for m in re.finditer(r"DGR_LAUNCH\((\d+), (\d+), (\d+), (\d+)\)", SRC)]
+def _launch_list(text):
+    return [tuple(int(x) for x in m.groups())
+            for m in re.finditer(r"DGR_LAUNCH\((\d+), (\d+), (\d+), (\d+)\)", text)]
+
+
+# (element bytes, rows, strip, K-step, wavefronts) of every instance the
+# launcher lists: 16-bit ones before "} else {", 8-bit ones after it
+_block = SRC[SRC.index("if constexpr (Elem<E>::BYTES == 2)"):SRC.index("#undef DGR_LAUNCH")]
+_two, _one = _block.split("} else {")
+CONFIGS = [(2,) + c for c in _launch_list(_two)] + [(1,) + c for c in _launch_list(_one)]
+
+
+def loads_per_step(es, bms, bn, bk):
+    """Direct-to-LDS B loads and 16-byte A loads of one K-step."""
+    ki = 32 if es == 2 else 128            # K per MFMA
+    frag = ki // 4 * es                    # fragment bytes per lane
+    return bk * bn * es // 1024, (bk // ki) * (bms // 16) * (frag // 16)
 
 
 def after_prologue(t, b_loads, a_loads):
@@ -79,14 +94,13 @@ def replay(per_wave, b_loads, a_loads):
 
 def test_source_constants_and_configs_found():
     assert K_STAGES == 7 and 1 <= K_LEAD_A <= K_STAGES
-    assert len(CONFIGS) >= 1
+    assert {c[0] for c in CONFIGS} == {1, 2}
 
 
 @pytest.mark.parametrize("cfg", CONFIGS)
 def test_every_wait_covers_its_b_loads(cfg):
-    bms, bn, bk, w = cfg
-    b_loads = bk * bn * 2 // 1024
-    a_loads = (bk // 32) * (bms // 16)
+    es, bms, bn, bk, w = cfg
+    b_loads, a_loads = loads_per_step(es, bms, bn, bk)
     assert K_STAGES * (b_loads + a_loads) <= 63        # the vmcnt field
     for per_wave in range(1, 41):
         waits = replay(per_wave, b_loads, a_loads)
