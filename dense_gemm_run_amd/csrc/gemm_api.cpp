@@ -66,6 +66,9 @@ const Entry kTable[] = {
     {{23, 32, 16, 128, 1, 512, 0x18, 1, 1, "skinny8_32x16x128"}, kSkinny},
     {{24, 16, 32, 128, 1, 256, 0x18, 1, 1, "skinny8_16x32x128"}, kSkinny},
     {{25, 32, 32, 128, 1, 256, 0x18, 1, 1, "skinny8_32x32x128"}, kSkinny},
+    // 8-bit tiles of 128 x 128 (two workgroups per CU)
+    {{26, 128, 128, 64, 4, 256, 0x18, 1, 1, "fp8_128x128x64"}, kFp8},
+    {{27, 128, 128, 128, 4, 256, 0x18, 1, 1, "fp8_128x128x128"}, kFp8},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -182,13 +185,17 @@ int select(const Problem& p)
     if (p.dtype == kF32) return 0;
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
-        if (p.M <= 64) {   // few rows: the strip kernel, as for 16-bit inputs
-            const bool wide = p.N >= 8192;
-            if (p.M <= 16) return wide ? 24 : 22;
-            if (p.M <= 32) return wide ? 25 : 23;
-            if (!wide) return 25;
+        if (p.M <= 64 && p.N < 8192) {
+            // few rows: the strip kernel (16-column strips up to 16 rows,
+            // 32 x 32 above; K >= 8192 keeps 16 columns for more strips)
+            if (p.M <= 16) return p.K >= 8192 ? 22 : 24;
+            return 25;
         }
-        return 13;
+        // 256 x 256 tiles once they cover half the CUs, else 128 x 128 (also
+        // for few rows of a wide B, whose 16-byte strip rows cost one cache
+        // line per lane)
+        const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+        return t256 >= 128 ? 13 : 26;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
     if (!accepts(kTable[6], p)) return 0;

@@ -9,11 +9,13 @@
 //
 // The structure is that of the 16x16x32 kernel (the tiled loop of
 // kernels-book chapter "Matrix Multiplication", section "Tiles": one
-// workgroup per 256 x 256 output tile, fp32 accumulators that live across
-// the whole K walk), with one-byte elements:
+// workgroup per BM x BN output tile, 256 x 256 or 128 x 128, fp32
+// accumulators that live across the whole K walk), with one-byte elements:
 //
-//  * Math: 4 wavefronts in a 2 x 2 grid, each owning 128 x 128 outputs as
-//    4 x 4 tiles of 32 x 32 (the 256 accumulator registers of a lane).  A
+//  * Math: 4 wavefronts in a 2 x 2 grid, each owning BM/2 x BN/2 outputs as
+//    tiles of 32 x 32 (4 x 4 of them, the 256 accumulator registers of a
+//    lane, at 256 x 256; 2 x 2 at 128 x 128, where two workgroups share a
+//    CU).  A
 //    64-deep K-slice is one MFMA per tile; a K-step of BK = 64 or 128 is one
 //    or two K-slices.  The MFMAs are inline assembly with the accumulator
 //    tied to the destination (and source C = 0 on the first K-slice), which
@@ -29,16 +31,18 @@
 //    16-byte pieces at or past K, rows past M and columns past N read zeros
 //    (the zero padding of chapter "Matrix Multiplication", section "The real
 //    tiled loop").
-//  * LDS layout: A [256][BK] with 16-byte pieces XOR-swizzled: a fragment
+//  * LDS layout: A [BM][BK] with 16-byte pieces XOR-swizzled: a fragment
 //    read has its four 16-lane groups take one piece each of rows 0-15,
 //    16-31, 0-15 and 16-31 of a tile.  Measured with the bank-conflict
 //    counter on that exact read, XOR (row/4) % 4 is conflict-free for 64-byte
 //    rows (BK = 64) where (row/2) % 4 costs a 2-way conflict, and XOR
-//    (row/2) % 8 is conflict-free for 128-byte rows.  B [BK][256] with
-//    piece p of row k stored at p ^ 2*(k%8): the 8-bit transpose read of a
-//    half-wavefront covers 8
-//    consecutive rows and one 32-byte column pair of each, and the swizzle
-//    puts those 8 pairs in 8 different 32-byte bank groups.
+//    (row/2) % 8 is conflict-free for 128-byte rows.  B [BK][BN]: the 8-bit
+//    transpose read of a half-wavefront covers 8 consecutive rows and one
+//    32-byte column pair of each, and the swizzle puts those 8 pairs in the
+//    8 different 32-byte bank groups of the 256 bytes the banks span.  With
+//    256-byte rows piece p of row k is stored at p ^ 2*(k%8); with 128-byte
+//    rows, two to a bank span, at p ^ 2*((k/2)%4), which separates the pairs
+//    of the 4 even (and the 4 odd) rows.
 //  * One barrier per K-step, half a K-slice before its end; the loads and
 //    LDS traffic of a K-step are spread over its MFMAs.
 //  * Epilogue: fp32 -> bf16 (round to nearest even), staged through LDS and
@@ -80,14 +84,16 @@ template <int BK> __device__ __forceinline__ int swz_a(int row)
 {
     return BK == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
 }
-__device__ __forceinline__ int swz_b(int k) { return 2 * (k & 7); }
+template <int BN> __device__ __forceinline__ int swz_b(int k)
+{
+    return BN == 256 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
+}
 
-template <int FMT, int BK>
-__global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
+template <int FMT, int BM, int BN, int BK>
+__global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_kernel(
     const unsigned char* A, const unsigned char* B, __bf16* C,
     int M, int N, int K, int group_m, Batch bt)
 {
-    constexpr int BM = 256, BN = 256;
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
     constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 tiles per wavefront
@@ -107,6 +113,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
     constexpr int NR = FM + FN;                  // operand fragments per K-slice
     constexpr int BAR = XS - NT / 2;             // MFMAs of a K-step before its barrier
     static_assert(BK == 64 || BK == 128, "K-step");
+    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile");
     static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
     static_assert((SB - 1) * B_BYTES < 65536, "LDS immediate offsets");
     __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
     for (int j = 0; j < B_LOADS; ++j) {
         const int byte = 1024 * (wave * B_LOADS + j) + lane * 16;
         const int k = byte / ROW_B;
-        const int piece = ((byte % ROW_B) / 16) ^ swz_b(k);
+        const int piece = ((byte % ROW_B) / 16) ^ swz_b<BN>(k);
         const int col = n0 + piece * 16;
         b_voff[j] = col < N ? (unsigned)k * (unsigned)N + (unsigned)col : kOOB;
     }
@@ -192,14 +199,14 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
     // group G = lane/16, lane 2r+q points at K row 32*(G/2) + 8h + r (+64 per
     // K-slice), bytes 8q .. 8q+7 of the 16 columns wn*WN + 32*bj + 16*(G%2)
     // .. +15; lane i of the group receives column i over those 8 rows, which
-    // are bytes 8h .. 8h+7 of its 32-byte operand.  The swizzle 2*(k%8) is
-    // 2r for every h and K-slice.
+    // are bytes 8h .. 8h+7 of its 32-byte operand.  The swizzle depends on
+    // k%8 = r alone, the same for every h and K-slice.
     int b_rd[FN];
 #pragma unroll
     for (int bj = 0; bj < FN; ++bj) {
         const int G = lane >> 4, r = (lane & 15) >> 1, q = lane & 1;
         const int piece = (wn * WN + 32 * bj + 16 * (G & 1)) / 16;
-        b_rd[bj] = (32 * (G >> 1) + r) * ROW_B + ((piece ^ swz_b(r)) * 16) + 8 * q;
+        b_rd[bj] = (32 * (G >> 1) + r) * ROW_B + ((piece ^ swz_b<BN>(r)) * 16) + 8 * q;
     }
     auto read_a = [&](int st, int sl, int bi) __attribute__((always_inline)) -> u32x8 {
         const lds_byte* base = a_stage(st) + bi * 32 * ROW_A;
@@ -332,21 +339,29 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_kernel(
 
     // ---- epilogue.  The last row of tiles was written by the most recent
     // MFMAs (16 passes each): wait them out before any accumulator is read;
-    // the other rows are at least FN MFMAs old.
-    static_assert(FN == 4, "the wait below lists the last row's tiles");
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
+    // the other rows are at least FN >= 2 MFMAs old.
+    static_assert(FN == 4 || FN == 2, "the wait below lists the last row's tiles");
+    if constexpr (FN == 4)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]));
     // All loads (the B stages' direct LDS writes included) have landed and
     // every wavefront is done with the stages before they are reused for C.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+    // Each wavefront stages its block through a stage of its own, at most one
+    // whole block (one pass) at a time.
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    constexpr int BLOCK = WM * WN * 2;
     if constexpr (SB == 4) {
-        store_c_block_32x32<__bf16, WM, WN, B_BYTES>(acc, b_stage(wave), lane, row0, col0, M, N, C);
+        store_c_block_32x32<__bf16, WM, WN, (B_BYTES < BLOCK ? B_BYTES : BLOCK)>(acc, b_stage(wave), lane,
+                                                                              row0, col0, M, N, C);
     } else {
         static_assert(A_BYTES == B_BYTES, "one C region per wavefront");
         lds_byte* cw = wave < 2 ? a_stage(wave) : b_stage(wave - 2);
-        store_c_block_32x32<__bf16, WM, WN, A_BYTES>(acc, cw, lane, row0, col0, M, N, C);
+        store_c_block_32x32<__bf16, WM, WN, (A_BYTES < BLOCK ? A_BYTES : BLOCK)>(acc, cw, lane, row0, col0,
+                                                                              M, N, C);
     }
 }
 
@@ -358,15 +373,19 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* A = static_cast<const unsigned char*>(a.A);
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
-    if (cfg.threads != 256 || cfg.bm != 256 || cfg.bn != 256) return hipErrorInvalidValue;
-    if (cfg.bk == 64)
-        hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64>), grid, block, 0, a.stream, A, B, C, a.M, a.N, a.K,
-                           cfg.group_m, a.batch);
-    else if (cfg.bk == 128)
-        hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128>), grid, block, 0, a.stream, A, B, C, a.M, a.N, a.K,
-                           cfg.group_m, a.batch);
+    if (cfg.threads != 256) return hipErrorInvalidValue;
+#define DGR_FP8(BM_, BN_, BK_)                                                                        \
+    else if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_)                                        \
+        hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_>), grid, block, 0, a.stream, A, B, C, a.M, \
+                           a.N, a.K, cfg.group_m, a.batch);
+    if (false) {}
+    DGR_FP8(256, 256, 64)
+    DGR_FP8(256, 256, 128)
+    DGR_FP8(128, 128, 64)
+    DGR_FP8(128, 128, 128)
     else
         return hipErrorInvalidValue;
+#undef DGR_FP8
     return hipGetLastError();
 }
 

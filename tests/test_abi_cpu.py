@@ -135,7 +135,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(22))
+@pytest.mark.parametrize("cid", range(32))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -299,9 +299,25 @@ def test_few_rows_select_the_strip_kernel():
                  (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4092, 2)]:
         assert not name(*args).startswith("skinny"), args
     # 8-bit inputs take the 8-bit strip configurations, up to 64 rows for N < 8192
-    for M, N, K in [(1, 4096, 4096), (16, 4096, 14336), (32, 14336, 4096), (64, 4096, 4096)]:
+    for M, N, K in [(1, 4096, 4096), (16, 4096, 14336), (32, 4096, 4096), (64, 4096, 4096)]:
         for dt in (3, 4):
             info = dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb, M, N, K, dt))
             assert info["name"].startswith("skinny8") and info["dtype_mask"] == 0x18, (M, N, K, info)
-    for M, N, K in [(64, 14336, 4096), (128, 4096, 4096), (16, 4096, 4088)]:
+    for M, N, K in [(16, 14336, 4096), (64, 14336, 4096), (128, 4096, 4096), (16, 4096, 4088)]:
         assert not name(A, Bb, Cb, M, N, K, 3).startswith("skinny"), (M, N, K)
+
+
+def test_8bit_tile_size_follows_the_tile_count():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
+    # fewer than 128 tiles of 256 x 256 (half the CUs): 128 x 128 tiles
+    for M, N, K in [(2048, 2048, 2048), (512, 4096, 4096), (128, 4096, 4096), (64, 14336, 4096),
+                    (2816, 2816, 1024)]:
+        assert name(A, Bb, Cb, M, N, K, 3).startswith("fp8_128x128"), (M, N, K)
+    for M, N, K in [(3072, 3072, 3072), (4096, 4096, 4096), (8192, 14336, 4096)]:
+        assert name(A, Bb, Cb, M, N, K, 4).startswith("fp8_256x256"), (M, N, K)
+    # the batch counts: 16 products of 1024^2 are 256 tiles of 256 x 256
+    cid = dg.gemm_select_config_batched(A, Bb, Cb, 16, 1024, 1024, 1024, 1024 * 1024, 1024 * 1024,
+                                        1024 * 1024, 3)
+    assert dg.gemm_config_info(cid)["name"].startswith("fp8_256x256")

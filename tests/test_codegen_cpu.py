@@ -27,9 +27,9 @@ FAMILIES = {
     "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)E",
                   # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32)
                   10, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
-    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)E",
-            # {e4m3, e5m2} x {64, 128}, all 256x256
-            4, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
+    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)E",
+            # {e4m3, e5m2} x {256x256, 128x128} x {64, 128}
+            8, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
 }
 
 
@@ -46,8 +46,7 @@ def compile_family(fam, tmp):
     for i, l in enumerate(lines):
         m = re.match(r"^(_Z\S*" + pat + r"\S*):", l)
         if m:
-            g = [int(x) for x in m.groups()[1:]]
-            bm, bn, bk = g if len(g) == 3 else (256, 256, g[0])
+            bm, bn, bk = [int(x) for x in m.groups()[1:]]
             end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
             found[m.group(1)] = Kernel(fam, bm, bn, bk, ebytes, mnem, kdepth, outs, lines[i:end])
     # per-kernel scratch use from the kernel descriptors

@@ -182,6 +182,35 @@ def test_fp8_workloads_sampled(name):
     assert rep["ok"], rep
 
 
+@pytest.mark.parametrize("shape", [(2048, 2048, 2048), (256, 14336, 4096), (64, 14336, 4096),
+                                   (1000, 3008, 1040)])
+def test_fp8_mid_sizes_in_the_selected_configuration(shape):
+    """Shapes with fewer than 128 tiles of 256 x 256 (the 128 x 128 tiles),
+    in the configuration gemm_run picks, on whole rows, whole columns and
+    random points."""
+    M, N, K = shape
+    A, B = make_operands(M, N, K, "fp8_e4m3", "normal", 700 + M)
+    a, b = A.cuda(), B.cuda()
+    c = dg.gemm(a, b)
+    torch.cuda.synchronize()
+    cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, 3)
+    note(f"[fp8] mid size {shape} config {dg.gemm_config_info(cid)['name']}")
+    assert dg.gemm_config_info(cid)["name"].startswith("fp8_128x128")
+    rng = np.random.default_rng(M)
+    rows = [0, M - 1, int(rng.integers(0, M))]
+    cols = [0, N - 1, int(rng.integers(0, N))]
+    pr = np.concatenate([np.full(N, r) for r in rows] + [np.arange(M) for _ in cols]
+                        + [rng.integers(0, M, 20000)])
+    pc = np.concatenate([np.arange(N) for _ in rows] + [np.full(M, c_) for c_ in cols]
+                        + [rng.integers(0, N, 20000)])
+    A64 = fp8.decode(fp8._bits(A), "e4m3")
+    B64 = fp8.decode(fp8._bits(B), "e4m3")
+    ref = gemm64.bits_to_f64(gemm64.round_to_bits(gemm64.gemm_points_f64(A64, B64, pr, pc), "bf16"), "bf16")
+    got = c[torch.from_numpy(pr).cuda(), torch.from_numpy(pc).cuda()].to("cpu", torch.float64).numpy()
+    rep = tolerance.compare(got, ref, "bf16", K, float(np.abs(A64).max()), float(np.abs(B64).max()))
+    assert rep["ok"], rep
+
+
 @pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2"])
 @pytest.mark.parametrize("shape", [(127, 255, 65), (264, 400, 144), (520, 784, 272), (1, 16, 16)])
 def test_fp8_masked_store_leaves_guards_untouched(dtype, shape):
