@@ -6,6 +6,10 @@ N(0,1)/sqrt(K), fp32 accumulation, fp16 output), with inputs already resident
 in HBM.  W untimed warm-up steps, then exactly K
 timed steps bracketed by a device synchronisation on both sides; the kernel
 time is taken with HIP events recorded on the stream the kernels run on.
+Without --warmup, W is as many steps as take half a second (at least 20):
+under sustained MFMA load the GPU runs at its power limit and its clock
+takes a few hundred launches of the 4096^3 product (~30 ms) to settle; the
+JSON line reports the W used.
 
 Prints one JSON line (stdout):
   metric/value/unit   GEMM TFLOP/s = 2MNK / time per step
@@ -203,8 +207,9 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed steps before the timed ones (default: half a second's worth, >= 20)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -270,9 +275,19 @@ def main(argv=None) -> int:
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+    else:
+        # until the clock has settled: at least 20 steps and half a second
+        args.warmup = 0
+        t_warm = time.perf_counter()
+        while args.warmup < 20 or time.perf_counter() - t_warm < 0.5:
+            for _ in range(10):
+                step()
+            args.warmup += 10
+            torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warm-up steps done")
 
     ev0 = torch.cuda.Event(enable_timing=True)
