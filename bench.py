@@ -9,7 +9,10 @@ time is taken with HIP events recorded on the stream the kernels run on.
 Without --warmup, W is as many steps as take half a second (at least 20):
 under sustained MFMA load the GPU runs at its power limit and its clock
 takes a few hundred launches of the 4096^3 product (~30 ms) to settle; the
-JSON line reports the W used.
+JSON line reports the W used.  With --graph G the timed steps are replayed
+from a HIP graph of G captured steps (K/G replays): for products that take
+only microseconds, a Python-side launch per step cannot keep the stream busy,
+and the graph measures the GPU's own rate.
 
 Prints one JSON line (stdout):
   metric/value/unit   GEMM TFLOP/s = 2MNK / time per step
@@ -212,6 +215,8 @@ def main(argv=None) -> int:
                    help="untimed steps before the timed ones (default: half a second's worth, >= 20)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
+    p.add_argument("--graph", type=int, default=0,
+                   help="time K steps as K/G replays of a HIP graph of G captured steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for scaling HBM counters)")
@@ -258,13 +263,27 @@ def main(argv=None) -> int:
     log(f"[bench] kernel configuration {cid} {cfg['name']}")
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    def step(st=stream):
         if w.batch > 1:
             dg.gemm_run_batched_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch, w.M,
-                                       w.N, w.K, *strides, code, cid, stream.cuda_stream)
+                                       w.N, w.K, *strides, code, cid, st.cuda_stream)
         else:
             dg.gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
-                               cid, stream.cuda_stream)
+                               cid, st.cuda_stream)
+
+    if args.graph:
+        if args.graph < 1 or args.steps % args.graph:
+            print("--graph G needs G >= 1 dividing --steps", file=sys.stderr)
+            return 2
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream(dev)
+            for _ in range(args.graph):
+                step(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] captured {args.graph} steps in a HIP graph")
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -295,8 +314,12 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    if args.graph:
+        for _ in range(args.steps // args.graph):
+            graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -334,6 +357,7 @@ def main(argv=None) -> int:
                    "kernel_config": cfg["name"], "parallelism": "single GPU"},
         "roofline": roofline,
         "wall_s_timed_region": round(wall, 4),
+        "launch": f"hip graph of {args.graph} steps" if args.graph else "one gemm_run call per step",
     }
     dg.gemm_destroy(h)
     if not args.no_cpu_baseline:

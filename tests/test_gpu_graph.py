@@ -1,0 +1,79 @@
+"""gemm_run inside a HIP graph (captured through torch's graph API on the
+caller's stream).  The launch path makes no allocation and no memset, so a
+captured product is one kernel node; every replay must give, bit for bit, what
+an eager call gives on the inputs as they are at that moment.  Between the
+replays the test does eager work of its own (rewriting A in place, an eager
+product, synchronisation), as a program around a graph would.
+"""
+import sys
+
+import pytest
+import torch
+
+import dense_gemm_run_amd as dg
+from dense_gemm_run_amd.inputs import make_batched_operands, make_operands
+
+pytestmark = pytest.mark.gpu
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# one shape per kernel family the selection reaches
+CASES = [(1000, 1000, 1000, "f16"),        # 16x16x32 kernel at 128 x 128
+         (2048, 2048, 1024, "bf16"),       # 16x16x32 kernel at 256 x 256
+         (16, 4096, 4096, "bf16"),         # few-row strip kernel
+         (4096, 4, 4096, "bf16"),          # matrix-vector kernel
+         (127, 255, 65, "f16"),            # generic kernel
+         (1024, 1024, 2048, "fp8_e4m3"),   # 8-bit kernel at 128 x 128
+         (32, 4096, 4096, "fp8_e5m2")]     # 8-bit strip kernel
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_every_replay_matches_the_eager_call(case):
+    M, N, K, dtype = case
+    note(f"[graph] {case}")
+    A, B = make_operands(M, N, K, dtype, "normal", 800 + M)
+    A2, _ = make_operands(M, N, K, dtype, "normal", 900 + M)
+    a, b = A.cuda(), B.cuda()
+    c = torch.empty((M, N), dtype=dg.out_dtype(a.dtype), device="cuda")
+    dg.gemm(a, b, out=c)                  # creates the handle outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dg.gemm(a, b, out=c)
+    sources = [A, A2, A, A2]
+    for r, src in enumerate(sources):
+        a.copy_(src.cuda())               # eager work between replays
+        torch.cuda.synchronize()
+        c.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = dg.gemm(a, b)
+        torch.cuda.synchronize()
+        same = torch.equal(c.view(torch.int16), eager.view(torch.int16))
+        note(f"  replay {r}: identical to the eager call: {same}")
+        assert same, (case, r)
+
+
+def test_batched_replays_match_the_eager_call():
+    batch, M, N, K = 4, 512, 768, 1024
+    A, B = make_batched_operands(batch, M, N, K, "bf16", "normal", 950)
+    a, b = A.cuda(), B.cuda()
+    c = torch.empty((batch, M, N), dtype=torch.bfloat16, device="cuda")
+    dg.gemm_batched(a, b, out=c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dg.gemm_batched(a, b, out=c)
+    for r in range(3):
+        a.mul_(-1.0)
+        torch.cuda.synchronize()
+        c.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = dg.gemm_batched(a, b)
+        torch.cuda.synchronize()
+        assert torch.equal(c.view(torch.int16), eager.view(torch.int16)), r
