@@ -239,7 +239,7 @@ def main(argv=None) -> int:
     args = p.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(the product shards by output rows or columns with no exchange between GPUs)",
               file=sys.stderr)
         return 2
