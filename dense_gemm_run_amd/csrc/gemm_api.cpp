@@ -69,6 +69,8 @@ const Entry kTable[] = {
     // 8-bit tiles of 128 x 128 (two workgroups per CU)
     {{26, 128, 128, 64, 4, 256, 0x18, 1, 1, "fp8_128x128x64"}, kFp8},
     {{27, 128, 128, 128, 4, 256, 0x18, 1, 1, "fp8_128x128x128"}, kFp8},
+    // 192 x 256 tiles: whole waves of CUs where 256 x 256 leaves a partial one
+    {{28, 192, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_192x256x32"}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -174,7 +176,10 @@ bool accepts(const Entry& e, const Problem& p)
 //  * at least 128 output tiles of 256 x 256 over the whole batch (half the
 //    256 CUs or more): the 16x16x32 kernel at 256 x 256.  At one wave of
 //    tiles it is 30-40 % faster than the 128 x 128 tile, and even at 144
-//    tiles (3072^3) it matches it;
+//    tiles (3072^3) it matches it.  Where its last wave of tiles is partial
+//    and 192 x 256 tiles fill fewer waves at lower cost (the wave model
+//    below), the same kernel at 192 x 256 (3072^3: 58.9 against 69.7 us;
+//    6144^3: 394 against 410);
 //  * otherwise the 16x16x32 kernel at 128 x 128, which gives 4x the tiles
 //    (2048^3: 842 TFLOP/s against 383 at 256 x 256).
 // The 32x32x16 configurations and the 256 x 128 tiles were never the fastest
@@ -210,7 +215,14 @@ int select(const Problem& p)
         if (!wide) return p.M <= 64 ? 19 : 20;
     }
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    return t256 >= 128 ? 6 : 12;
+    if (t256 < 128) return 12;
+    // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4
+    // of a 256 x 256 tile's work at ~94 % of its rate, so a wave of them costs
+    // ~0.8 of a wave of 256 x 256 tiles; it wins where 256 x 256 leaves a
+    // partial last wave (3072^2: 144 tiles, one wave of 192 x 256 tiles).
+    const int64_t t192 = ((p.M + 191) / 192) * ((p.N + 255) / 256) * p.batch;
+    const int64_t w256 = (t256 + 255) / 256, w192 = (t192 + 255) / 256;
+    return w192 * 80 < w256 * 95 ? 28 : 6;
 }
 
 gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream)

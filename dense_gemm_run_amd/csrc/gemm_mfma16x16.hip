@@ -8,7 +8,8 @@
 // with these differences:
 //
 //  * Math: 4 wavefronts in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs
-//    as 16x16 MFMA tiles (BM x BN = 256 x 256, 256 x 128 or 128 x 128).  Per unit of work the 16x16x32 instruction moves
+//    as 16x16 MFMA tiles (BM x BN = 256 x 256, 192 x 256, 256 x 128 or
+//    128 x 128).  Per unit of work the 16x16x32 instruction moves
 //    half the accumulator data of the 32x32x16 one; under MI355X's power
 //    limit this runs at a higher clock for the same issue rate.
 //  * The MFMAs are written as inline assembly with the accumulator operand
@@ -427,7 +428,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     __syncthreads();
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
     if constexpr (SB == 4) {
-        store_c_block<T, WM, WN, B_BYTES>(acc, b_stage(wave), lane, row0, col0, M, N, C);
+        // as many whole 16-row tile rows per pass as a B stage holds and WM
+        // divides into (64 of 128, 48 of 96)
+        constexpr int RP_MAX = B_BYTES / (WN * 2);
+        constexpr int RP = WM % RP_MAX == 0 ? RP_MAX : WM % 48 == 0 && RP_MAX >= 48 ? 48 : 16;
+        store_c_block<T, WM, WN, RP * WN * 2>(acc, b_stage(wave), lane, row0, col0, M, N, C);
     } else {
         constexpr int CW = A_BYTES < B_BYTES ? A_BYTES : B_BYTES;
         lds_byte* cw = wave < 2 ? a_stage(wave) : b_stage(wave - 2);
@@ -455,6 +460,7 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     DGR_LAUNCH(256, 256, 64)
     DGR_LAUNCH(256, 128, 64)
     DGR_LAUNCH(128, 128, 32)
+    DGR_LAUNCH(192, 256, 32)
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;
 }

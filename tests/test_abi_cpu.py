@@ -307,6 +307,22 @@ def test_few_rows_select_the_strip_kernel():
         assert not name(A, Bb, Cb, M, N, K, 3).startswith("skinny"), (M, N, K)
 
 
+def test_192_row_tiles_where_256_leaves_a_partial_wave():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
+    # 144 tiles of 256 x 256 -> one wave of 192 x 256; 576 (2.25 waves) -> 768 (3 whole waves)
+    for M, N, K in [(3072, 3072, 3072), (6144, 6144, 6144)]:
+        for dt in (1, 2):
+            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_192x256x32", (M, N, K)
+    # whole waves of 256 x 256 tiles keep them
+    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 12288, 4096), (8192, 4096, 14336),
+                    (8192, 14336, 4096), (5120, 5120, 5120)]:
+        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_256x256x32", (M, N, K)
+    info = dg.gemm_config_info(28)
+    assert (info["bm"], info["bn"], info["bk"]) == (192, 256, 32)
+
+
 def test_8bit_tile_size_follows_the_tile_count():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)

@@ -276,3 +276,21 @@ def test_full_size_workloads_sampled(name):
     assert not torch.isnan(C).any()
     rep = sampled_check(A, B, w.dtype, C, seed=w.seed)
     note(f"  {rep}")
+
+
+@pytest.mark.parametrize("shape", [(3072, 3072, 3072), (3000, 3064, 1000), (6144, 6144, 1024)])
+def test_partial_wave_shapes_in_the_192_row_tiles(shape):
+    """Shapes whose 256 x 256 tiles leave a partial last wave run 192 x 256
+    tiles (ragged in M and N for the second shape); sampled like the
+    full-size workloads."""
+    M, N, K = shape
+    note(f"[parity] 192-row tiles {shape}")
+    A, B = make_operands(M, N, K, "bf16", "normal", 40 + M)
+    a, b = A.cuda(), B.cuda()
+    C = torch.empty((M, N), dtype=a.dtype, device="cuda")
+    cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), C.data_ptr(), M, N, K, DT_CODE["bf16"])
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_192x256x32", cid
+    dg.gemm(a, b, out=C)
+    torch.cuda.synchronize()
+    rep = sampled_check(A, B, "bf16", C, seed=M)
+    note(f"  {rep}")
