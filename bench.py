@@ -172,18 +172,28 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
         a, b = A.to(dev), B.to(dev)
         code = dg.dtype_code(a.dtype)
         c = torch.empty((M, N), dtype=dg.out_dtype(a.dtype), device=dev)
-        chosen = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, code)
+        chosen, chosen_splits = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                                         M, N, K, code, 1 << 62)
         flops = 2.0 * M * N * K
         compulsory = (M * K + K * N) * a.element_size() + M * N * c.element_size()
 
-        def line(cid, name, us):
+        def line(cid, name, us, splits=1):
             print(json.dumps({"M": M, "N": N, "K": K, "dtype": dtype, "config": cid, "name": name,
-                              "selected": cid == chosen, "us": round(us, 2),
+                              "splits": splits,
+                              "selected": cid == chosen and splits == chosen_splits, "us": round(us, 2),
                               "tflops": round(flops / (us * 1e-6) / 1e12, 1),
                               "compulsory_gbps": round(compulsory / (us * 1e-6) / 1e9, 1)}),
                   flush=True)
 
-        def run(cid):
+        # workspace for up to 16 splits, on shapes small enough to split at all
+        ws_max = 16 * M * N * 4 if M * N <= (1 << 24) else 0
+        work = torch.empty(max(ws_max, 16), dtype=torch.uint8, device=dev)
+
+        def run(cid, splits=1):
+            if splits > 1:
+                return _lib.lib().gemm_run_ws_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), M,
+                                                     N, K, code, cid, splits, work.data_ptr(),
+                                                     ws_max, stream.cuda_stream)
             return _lib.lib().gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K,
                                               code, cid, stream.cuda_stream)
 
@@ -192,14 +202,25 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
         t_warm = time.perf_counter()
         while time.perf_counter() - t_warm < 0.3:
             for _ in range(10):
-                run(chosen)
+                run(chosen, chosen_splits)
             torch.cuda.synchronize()
         for cid in range(dg.gemm_config_count()):
             def run_cfg(cid=cid):
                 return run(cid)
             if run_cfg() != 0:      # this configuration refuses the shape
                 continue
-            line(cid, dg.gemm_config_info(cid)["name"], _time_us(run_cfg, iters, stream))
+            info = dg.gemm_config_info(cid)
+            line(cid, info["name"], _time_us(run_cfg, iters, stream))
+            # split K for the tile configurations on shapes with fewer tiles than CUs
+            tiles = -(-M // info["bm"]) * -(-N // info["bn"])
+            if ws_max and info["name"].startswith("mfma16x16") and tiles < 256:
+                for sp in (2, 4, 8, 16):
+                    if -(-K // info["bk"]) < 2 * sp:
+                        break
+                    def run_split(cid=cid, sp=sp):
+                        return run(cid, sp)
+                    if run_split() == 0:
+                        line(cid, f"{info['name']}_split{sp}", _time_us(run_split, iters, stream), sp)
         if vendor:
             if eight_bit:
                 bt = b.t().contiguous().t()
@@ -213,7 +234,7 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
                     vendor = False
             else:
                 line(None, "torch.matmul", _time_us(lambda: torch.matmul(a, b), iters, stream))
-        del a, b, c
+        del a, b, c, work
     dg.gemm_destroy(h)
     return 0
 
@@ -226,6 +247,8 @@ def main(argv=None) -> int:
                    help="untimed steps before the timed ones (default: half a second's worth, >= 20)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
+    p.add_argument("--splits", type=int, default=1,
+                   help="with --config: split K over this many workgroups per tile (gemm_run_ws_config)")
     p.add_argument("--graph", type=int, default=0,
                    help="time K steps as K/G replays of a HIP graph of G captured steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -263,21 +286,30 @@ def main(argv=None) -> int:
     code = dg.dtype_code(a.dtype)
     h = dg.gemm_create()
     strides = (w.M * w.K, w.K * w.N, w.M * w.N)
+    splits = 1
     if args.config is not None:
-        cid = args.config
+        cid, splits = args.config, args.splits
     elif w.batch > 1:
         cid = dg.gemm_select_config_batched(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch,
                                             w.M, w.N, w.K, *strides, code)
     else:
-        cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code)
+        # what gemm_run_ws picks with an ample workspace (split K where it helps)
+        cid, splits = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N,
+                                               w.K, code, 1 << 62)
     cfg = dg.gemm_config_info(cid)
-    log(f"[bench] kernel configuration {cid} {cfg['name']}")
+    kernel_name = cfg["name"] + (f"_split{splits}" if splits > 1 else "")
+    ws_bytes = splits * w.M * w.N * 4 if splits > 1 else 0
+    work = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    log(f"[bench] kernel configuration {cid} {kernel_name}")
     stream = torch.cuda.current_stream(dev)
 
     def step(st=stream):
         if w.batch > 1:
             dg.gemm_run_batched_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch, w.M,
                                        w.N, w.K, *strides, code, cid, st.cuda_stream)
+        elif splits > 1:
+            dg.gemm_run_ws_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
+                                  cid, splits, work.data_ptr(), ws_bytes, st.cuda_stream)
         else:
             dg.gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
                                cid, st.cuda_stream)
@@ -339,7 +371,7 @@ def main(argv=None) -> int:
 
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = traffic_from_profiles(cfg["name"], w.name)
+    traffic = traffic_from_profiles(kernel_name, w.name)
     compulsory = w.batch * ((w.M * w.K + w.K * w.N) * a.element_size() + w.M * w.N * c.element_size())
     if w.flops / compulsory < peak * 1e12 / (HBM_GBPS * 1e9):
         # below the ridge: the compulsory bytes, not the MFMAs, bound the step
@@ -365,7 +397,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "distribution": w.dist, "seed": w.seed,
-                   "kernel_config": cfg["name"], "parallelism": "single GPU"},
+                   "kernel_config": kernel_name, "parallelism": "single GPU"},
         "roofline": roofline,
         "wall_s_timed_region": round(wall, 4),
         "launch": f"hip graph of {args.graph} steps" if args.graph else "one gemm_run call per step",

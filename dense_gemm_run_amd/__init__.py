@@ -12,14 +12,16 @@ from __future__ import annotations
 from ._lib import (GEMM_BF16, GEMM_F16, GEMM_F32, GEMM_FP8_E4M3, GEMM_FP8_E5M2, GemmError, gemm_check_args,
                    gemm_check_args_batched, gemm_config_count, gemm_config_info, gemm_create,
                    gemm_destroy, gemm_run, gemm_run_batched, gemm_run_batched_config,
-                   gemm_run_config, gemm_select_config, gemm_select_config_batched,
-                   gemm_tile_of_block, gemm_tile_of_block_batched, status_string)
+                   gemm_run_config, gemm_run_ws, gemm_run_ws_config, gemm_select_config,
+                   gemm_select_config_batched, gemm_select_config_ws, gemm_tile_of_block,
+                   gemm_tile_of_block_batched, gemm_workspace_size, status_string)
 
 __all__ = ["gemm", "gemm_batched", "Gemm", "gemm_create", "gemm_run", "gemm_run_config",
            "gemm_run_batched", "gemm_run_batched_config", "gemm_destroy",
            "gemm_check_args", "gemm_check_args_batched", "gemm_config_count",
            "gemm_config_info", "gemm_select_config", "gemm_select_config_batched",
            "gemm_tile_of_block", "gemm_tile_of_block_batched", "status_string", "GemmError",
+           "gemm_workspace_size", "gemm_run_ws", "gemm_run_ws_config", "gemm_select_config_ws",
            "GEMM_F32", "GEMM_F16", "GEMM_BF16", "GEMM_FP8_E4M3", "GEMM_FP8_E5M2",
            "dtype_code", "out_dtype"]
 
@@ -62,7 +64,11 @@ class Gemm:
         except Exception:
             pass
 
-    def __call__(self, a, b, out=None, config: int | None = None):
+    def __call__(self, a, b, out=None, config: int | None = None, splits: int | None = None):
+        """C = a @ b.  Products that gemm_run_ws would split over K get their
+        workspace from torch's allocator on the current stream (stream-ordered,
+        so concurrent streams never share one).  ``config`` forces a kernel
+        configuration, and with it ``splits`` a split count."""
         import torch
         if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
             raise ValueError("gemm expects [M, K] @ [K, N]")
@@ -84,8 +90,19 @@ class Gemm:
         stream = torch.cuda.current_stream(self.device).cuda_stream
         with torch.cuda.device(self.device):
             if config is None:
-                gemm_run(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
-                         code, stream)
+                ws = gemm_workspace_size(M, N, K, code)
+                if ws > 0:
+                    work = torch.empty(ws, dtype=torch.uint8, device=self.device)
+                    gemm_run_ws(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                                code, work.data_ptr(), ws, stream)
+                else:
+                    gemm_run(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                             code, stream)
+            elif splits is not None and splits > 1:
+                ws = splits * M * N * 4
+                work = torch.empty(ws, dtype=torch.uint8, device=self.device)
+                gemm_run_ws_config(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N,
+                                   K, code, config, splits, work.data_ptr(), ws, stream)
             else:
                 gemm_run_config(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(),
                                 M, N, K, code, config, stream)
@@ -140,13 +157,13 @@ class Gemm:
 _default: dict[int, Gemm] = {}
 
 
-def gemm(a, b, out=None, config: int | None = None):
+def gemm(a, b, out=None, config: int | None = None, splits: int | None = None):
     """C = a @ b on a's device and the current stream (see module docstring)."""
     idx = a.device.index if a.device.index is not None else 0
     g = _default.get(idx)
     if g is None:
         g = _default[idx] = Gemm(idx)
-    return g(a, b, out=out, config=config)
+    return g(a, b, out=out, config=config, splits=splits)
 
 
 def gemm_batched(a, b, out=None, config: int | None = None):

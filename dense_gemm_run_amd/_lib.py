@@ -61,6 +61,12 @@ SIGNATURES = {
                                           ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "gemm_run_batched_config": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I64, _I64, _I64,
                                        _I64, _I32, _I32, _VP]),
+    "gemm_workspace_size": (_I64, [_I64, _I64, _I64, _I32]),
+    "gemm_run_ws": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _VP, _I64, _VP]),
+    "gemm_run_ws_config": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _I32, _I32, _VP, _I64,
+                                  _VP]),
+    "gemm_select_config_ws": (_I32, [_VP, _VP, _VP, _I64, _I64, _I64, _I32, _I64,
+                                     ctypes.POINTER(_I32)]),
 }
 
 _lib = None
@@ -181,3 +187,29 @@ def gemm_tile_of_block_batched(config_id: int, M: int, N: int, batch: int,
                                             ctypes.byref(tm), ctypes.byref(tn)),
            "gemm_tile_of_block_batched")
     return b.value, tm.value, tn.value
+
+
+def gemm_workspace_size(M: int, N: int, K: int, dtype: int) -> int:
+    """Workspace bytes gemm_run_ws uses for this product (0: none; -1: bad sizes)."""
+    return lib().gemm_workspace_size(M, N, K, dtype)
+
+
+def gemm_run_ws(h, A: int, B: int, C: int, M: int, N: int, K: int, dtype: int,
+                workspace: int, workspace_bytes: int, stream=None) -> None:
+    _check(lib().gemm_run_ws(h, A, B, C, M, N, K, dtype, workspace, workspace_bytes, stream),
+           "gemm_run_ws")
+
+
+def gemm_run_ws_config(h, A: int, B: int, C: int, M: int, N: int, K: int, dtype: int,
+                       config_id: int, splits: int, workspace: int, workspace_bytes: int,
+                       stream=None) -> None:
+    _check(lib().gemm_run_ws_config(h, A, B, C, M, N, K, dtype, config_id, splits, workspace,
+                                    workspace_bytes, stream), "gemm_run_ws_config")
+
+
+def gemm_select_config_ws(A: int, B: int, C: int, M: int, N: int, K: int, dtype: int,
+                          workspace_bytes: int) -> tuple[int, int]:
+    """(configuration, split count) gemm_run_ws would use; (-1, 1) on bad arguments."""
+    s = _I32(1)
+    cid = lib().gemm_select_config_ws(A, B, C, M, N, K, dtype, workspace_bytes, ctypes.byref(s))
+    return cid, s.value

@@ -225,7 +225,61 @@ int select(const Problem& p)
     return w192 * 80 < w256 * 95 ? 28 : 6;
 }
 
-gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream)
+// ---- split K (gemm_run_ws)
+
+// Split count actually launched for `splits` requested: lowered until no
+// split is left without K-steps of bk.
+int effective_splits(int splits, int64_t K, int bk)
+{
+    const int64_t steps = (K + bk - 1) / bk;
+    if (splits <= 1 || steps <= 1) return 1;
+    const int64_t q = (steps + splits - 1) / splits;
+    return (int)((steps + q - 1) / q);
+}
+
+constexpr int kSplitConfig = 12;   // the 16x16x32 kernel at 128 x 128 tiles
+
+// The choice of gemm_run_ws: a configuration and a split count (1: none).
+// fp16/bf16 products of one matrix with K >= 2048 (64 K-steps) whose
+// 128 x 128 tiles number at most 160 split K over the 16x16x32 kernel at
+// 128 x 128, so that tiles * splits comes near 256 workgroups, with at least
+// 16 K-steps (512 of K) per split.  Up to 8 rows stay on the strip kernel.
+// (Sweep, bf16: 256 x 4096 x 4096 in 19.6 us with 4 splits against 31.9 in
+// one pass; 16 x 4096 x 14336 22.6 with 8 against 38.0 on the strip kernel;
+// 1024^3 14.4 with 2 against 10.7, hence the K floor.)
+int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
+{
+    splits = 1;
+    const int c = select(p);
+    if (p.batch != 1 || (p.dtype != kF16 && p.dtype != kBF16) || p.M == 0 || p.N == 0) return c;
+    if (!accepts(kTable[kSplitConfig], p) || kTable[c].kind == kGemv) return c;
+    if (kTable[c].kind == kSkinny && p.M <= 8) return c;
+    const int64_t steps = (p.K + 31) / 32;
+    const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    if (steps < 64 || t128 > 160) return c;
+    int s = (int)((256 + t128 / 2) / t128);
+    if (s > 16) s = 16;
+    while (s > 1 && steps < 16 * (int64_t)s) --s;
+    s = effective_splits(s, p.K, 32);
+    if (s < 2 || (int64_t)s * p.M * p.N * 4 > ws_bytes) return c;
+    splits = s;
+    return kSplitConfig;
+}
+
+// Workspace argument checks (after check_args).
+gemm_status_t check_ws(const Problem& p, const void* ws, int64_t ws_bytes)
+{
+    if (ws_bytes < 0 || (!ws && ws_bytes > 0)) return GEMM_ERR_INVALID_VALUE;
+    if (ws && (reinterpret_cast<uintptr_t>(ws) & 15u)) return GEMM_ERR_INVALID_VALUE;
+    const int64_t si = in_bytes(p.dtype), so = out_bytes(p.dtype);
+    if (overlaps(ws, ws_bytes, p.A, p.M * p.K * si) || overlaps(ws, ws_bytes, p.B, p.K * p.N * si) ||
+        overlaps(ws, ws_bytes, p.C, p.M * p.N * so))
+        return GEMM_ERR_ALIASING;
+    return GEMM_OK;
+}
+
+gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream, int splits = 1,
+                     void* ws = nullptr)
 {
     if (!h) return GEMM_ERR_INVALID_VALUE;
     int cur = -1;
@@ -234,11 +288,16 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
     if (p.M == 0 || p.N == 0 || p.batch == 0) return GEMM_OK;
     LaunchArgs la{p.A, p.B, p.C, (int)p.M, (int)p.N, (int)p.K, p.dtype, static_cast<hipStream_t>(stream),
                   Batch{(int)p.batch, p.sa, p.sb, p.sc}};
+    la.splits = splits;
+    la.ws = static_cast<float*>(ws);
     hipError_t err = hipSuccess;
     switch (e.kind) {
     case kGeneric: err = launch_generic(e.cfg, la); break;
     case kMfma32x32: err = launch_mfma32x32(e.cfg, la); break;
-    case kMfma16x16: err = launch_mfma16x16(e.cfg, la); break;
+    case kMfma16x16:
+        err = launch_mfma16x16(e.cfg, la);
+        if (err == hipSuccess && splits > 1) err = launch_reduce_splits(la);
+        break;
     case kGemv: err = launch_gemv(e.cfg, la); break;
     case kFp8: err = launch_fp8(e.cfg, la); break;
     case kSkinny: err = launch_skinny(e.cfg, la); break;
@@ -251,6 +310,34 @@ gemm_status_t run(gemm_handle_t h, const Problem& p, void* stream)
     const gemm_status_t st = check_args(p);
     if (st != GEMM_OK) return st;
     return launch(kTable[select(p)], h, p, stream);
+}
+
+gemm_status_t run_ws(gemm_handle_t h, const Problem& p, void* ws, int64_t ws_bytes, void* stream)
+{
+    gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GEMM_OK) return st;
+    int splits = 1;
+    const int c = select_ws(p, ws ? ws_bytes : 0, splits);
+    return launch(kTable[c], h, p, stream, splits, ws);
+}
+
+gemm_status_t run_ws_config(gemm_handle_t h, const Problem& p, int32_t config_id, int32_t splits, void* ws,
+                            int64_t ws_bytes, void* stream)
+{
+    gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    if ((st = check_ws(p, ws, ws_bytes)) != GEMM_OK) return st;
+    if (config_id < 0 || config_id >= kTableSize || splits < 1 || splits > 64) return GEMM_ERR_INVALID_VALUE;
+    const Entry& e = kTable[config_id];
+    if (!accepts(e, p)) return GEMM_ERR_CONFIG_MISMATCH;
+    int s = 1;
+    if (splits > 1) {
+        if (e.kind != kMfma16x16 || p.batch != 1) return GEMM_ERR_CONFIG_MISMATCH;
+        s = effective_splits(splits, p.K, e.cfg.bk);
+        if (s > 1 && (int64_t)s * p.M * p.N * 4 > ws_bytes) return GEMM_ERR_INVALID_VALUE;
+    }
+    return launch(e, h, p, stream, s, ws);
 }
 
 gemm_status_t run_config(gemm_handle_t h, const Problem& p, int32_t config_id, void* stream)
@@ -394,6 +481,44 @@ gemm_status_t gemm_run(gemm_handle_t h, const void* A, const void* B, void* C,
                        int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream)
 {
     return run(h, single(A, B, C, M, N, K, dtype), stream);
+}
+
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t dtype)
+{
+    // any distinct, far apart, 16-byte aligned addresses: the choice looks
+    // only at alignment
+    const uintptr_t base = (uintptr_t)1 << 44;
+    const Problem p = single(reinterpret_cast<const void*>(base), reinterpret_cast<const void*>(2 * base),
+                             reinterpret_cast<void*>(3 * base), M, N, K, dtype);
+    if (check_args(p) != GEMM_OK) return -1;
+    int splits = 1;
+    select_ws(p, INT64_MAX, splits);
+    return splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+}
+
+gemm_status_t gemm_run_ws(gemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                          int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream)
+{
+    return run_ws(h, single(A, B, C, M, N, K, dtype), workspace, workspace_bytes, stream);
+}
+
+gemm_status_t gemm_run_ws_config(gemm_handle_t h, const void* A, const void* B, void* C, int64_t M,
+                                 int64_t N, int64_t K, int32_t dtype, int32_t config_id, int32_t splits,
+                                 void* workspace, int64_t workspace_bytes, void* stream)
+{
+    return run_ws_config(h, single(A, B, C, M, N, K, dtype), config_id, splits, workspace, workspace_bytes,
+                         stream);
+}
+
+int32_t gemm_select_config_ws(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+                              int32_t dtype, int64_t workspace_bytes, int32_t* splits)
+{
+    const Problem p = single(A, B, const_cast<void*>(C), M, N, K, dtype);
+    if (check_args(p) != GEMM_OK || workspace_bytes < 0) return -1;
+    int s = 1;
+    const int c = select_ws(p, workspace_bytes, s);
+    if (splits) *splits = s;
+    return c;
 }
 
 gemm_status_t gemm_run_batched(gemm_handle_t h, const void* A, const void* B, void* C, int64_t batch,

@@ -83,6 +83,10 @@ struct LaunchArgs {
     int dtype;
     hipStream_t stream;
     Batch batch;
+    // split K (one product only): `splits` workgroups per tile, each writing
+    // fp32 sums to its M x N slice of `ws`; 1 = the single-pass kernels
+    int splits = 1;
+    float* ws = nullptr;
 };
 
 // Kernel launchers; each returns the hipError_t of the launch.
@@ -92,5 +96,7 @@ hipError_t launch_mfma16x16(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_gemv(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_fp8(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_skinny(const Config& cfg, const LaunchArgs& a);
+// Second pass of split K: C = the rounded sum of the `splits` slices of ws.
+hipError_t launch_reduce_splits(const LaunchArgs& a);
 
 }  // namespace dgr

@@ -46,6 +46,13 @@
 //    The epilogue rounds to the output type (round to nearest even), stages
 //    the wavefront's block through LDS and writes whole row segments with
 //    16-byte stores, skipping rows >= M and columns >= N.
+//  * Split K (SPLIT): for products with too few tiles to fill the CUs, the
+//    grid holds `splits` workgroups per tile; split s walks K-steps
+//    s*Q .. (s+1)*Q-1 (Q = ceil(K-steps / splits)) and writes its fp32 sums,
+//    unrounded, to its own M x N slice of a workspace; a second kernel adds
+//    the slices in split order and rounds once (the blocked K-loop of lesson
+//    "Matrix multiplication", section "Tiles are small rectangles of work":
+//    the per-block contributions are summed, here by different workgroups).
 #include "gemm_internal.h"
 #include "gemm_device.h"
 
@@ -140,10 +147,10 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
     }
 }
 
-template <typename T, int BM, int BN, int BK>
+template <typename T, int BM, int BN, int BK, bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const T* A, const T* B, T* C,
-    int M, int N, int K, int group_m, Batch bt)
+    int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
 {
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
@@ -178,11 +185,21 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
-    A += b * bt.sa;
-    B += b * bt.sb;
-    C += b * bt.sc;
+    // with split K the batch axis of the tile order is the split (one product)
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, SPLIT ? splits : bt.count, group_m, true, b, tm, tn);
+    if constexpr (!SPLIT) {
+        A += b * bt.sa;
+        B += b * bt.sb;
+        C += b * bt.sc;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
+    // K range of this workgroup: [kb, ke)
+    int kb = 0, ke = K;
+    if constexpr (SPLIT) {
+        const int q = cdiv_i(cdiv_i(K, BK), splits) * BK;
+        kb = b * q;
+        ke = kb + q < K ? kb + q : K;
+    }
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -223,8 +240,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     u32x4 stg[LEAD][A_LOADS];
     // A rows of the K-step at k0 -> register slot `slot`, load j.
     auto load_a = [&](int slot, int k0_in, int j) __attribute__((always_inline)) {
-        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
-        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
+        const unsigned off = a_kp[j] < ke - k0 ? a_voff[j] : kOOB;
         stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0 * 2, 0));
     };
     // Register slot `slot`, load j -> A stage `st`.
@@ -234,11 +251,11 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     };
     // B rows of the K-step at k0, load j -> B stage `st` (direct to LDS).
     auto load_b = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
-        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
-        const int krem = K - k0;
+        const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
+        const int krem = ke - k0;
         const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
         const __amdgpu_buffer_rsrc_t rbk =
-            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
+            make_rsrc(B + (size_t)(k0 < ke ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
         // (copied to a local: clang's host pass drops the kernel stub when a
         // captured array element is passed straight to a buffer builtin)
         const unsigned off = b_voff[j];
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
 
     // K-steps, rounded up to the LEAD-step unroll and at least one round:
     // the extra steps multiply the zeros their loads brought in.
-    const int nk = cdiv_i(cdiv_i(K, BK), LEAD) * LEAD;
+    const int nk = cdiv_i(cdiv_i(ke - kb, BK), LEAD) * LEAD;
     kstep(0, 0, true);
 #pragma unroll
     for (int q = 1; q < LEAD; ++q) kstep(q, q, false);
@@ -425,8 +442,22 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // every wavefront is done with the stages before they are reused for C:
     // each wavefront stages its block through one stage of its own.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __syncthreads();
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
+    if constexpr (SPLIT) {
+        // fp32 sums of this split, unrounded: lane l of tile (bi, bj) holds 4
+        // consecutive columns of one row, one 16-byte store (N is a multiple
+        // of 8, so the 4 columns are wholly inside or outside)
+        float* P = ws + (size_t)b * M * N;
+        const int r = row0 + (lane & 15), c = col0 + 4 * (lane >> 4);
+#pragma unroll
+        for (int bi = 0; bi < FM; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < FN; ++bj)
+                if (r + 16 * bi < M && c + 16 * bj < N)
+                    *(f32x4*)(P + (size_t)(r + 16 * bi) * N + c + 16 * bj) = acc[bi][bj];
+        return;
+    }
+    __syncthreads();
     if constexpr (SB == 4) {
         // as many whole 16-row tile rows per pass as a B stage holds and WM
         // divides into (64 of 128, 48 of 96)
@@ -449,11 +480,15 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
-#define DGR_LAUNCH(BM_, BN_, BK_)                                                                        \
-    if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                              \
-        hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_>), grid, block, 0, a.stream, A, B, C, \
-                           a.M, a.N, a.K, cfg.group_m, a.batch);                                        \
-        return hipGetLastError();                                                                       \
+#define DGR_LAUNCH(BM_, BN_, BK_)                                                                          \
+    if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                                \
+        if (a.splits > 1)                                                                                 \
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_, true>), dim3(tiles * a.splits), block, \
+                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits); \
+        else                                                                                              \
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_, false>), grid, block, 0, a.stream, A, B, \
+                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);                          \
+        return hipGetLastError();                                                                         \
     }
     DGR_LAUNCH(256, 256, 32)
     DGR_LAUNCH(256, 128, 32)

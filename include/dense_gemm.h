@@ -120,6 +120,41 @@ gemm_status_t gemm_run_batched(gemm_handle_t h, const void* A, const void* B, vo
                                int64_t stride_a, int64_t stride_b, int64_t stride_c,
                                int32_t dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Split K with a caller-provided workspace.
+ *
+ * A product with few output tiles and a long K (a few hundred rows times a
+ * few thousand columns, say) leaves most CUs idle when each tile is one
+ * workgroup.  gemm_run_ws may split K over several workgroups per tile: each
+ * writes its fp32 sums, unrounded, to its own M x N slice of the workspace,
+ * and a second kernel adds the slices in split order and rounds once (the
+ * blocked K-loop of lesson "Matrix multiplication", section "Tiles are small
+ * rectangles of work", with the per-block contributions summed across
+ * workgroups).  The result is bitwise the same on every call for a given
+ * configuration and split count, and meets gemm_run's accuracy (fp32 sums,
+ * one rounding).  Only fp16/bf16 products of one matrix split.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of workspace gemm_run_ws uses for this product when A, B and C are
+ * 16-byte aligned and the workspace is large enough (0: it runs as gemm_run
+ * and needs none).  -1 for negative sizes or an unknown dtype. */
+int64_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t dtype);
+
+/* gemm_run with `workspace` available as scratch:
+ *   workspace        device memory on the handle's device, 16-byte aligned,
+ *                    owned by the caller, overlapping none of A, B and C;
+ *                    NULL when workspace_bytes is 0.
+ *   workspace_bytes  its size; when the split this product would use needs
+ *                    more (gemm_workspace_size), the call runs as gemm_run.
+ * The workspace's contents are overwritten and have no meaning afterwards;
+ * calls that may run at the same time (other streams) need distinct
+ * workspaces.  Errors as gemm_run, plus GEMM_ERR_INVALID_VALUE for a negative
+ * workspace_bytes, a NULL workspace with a nonzero size, or a misaligned
+ * workspace, and GEMM_ERR_ALIASING when it overlaps A, B or C. */
+gemm_status_t gemm_run_ws(gemm_handle_t h, const void* A, const void* B, void* C,
+                          int64_t M, int64_t N, int64_t K, int32_t dtype,
+                          void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Release a handle.  NULL is accepted and ignored.  No work may still be
  * using the handle (enqueued work does not refer to it). */
 gemm_status_t gemm_destroy(gemm_handle_t h);
@@ -194,6 +229,24 @@ gemm_status_t gemm_tile_of_block_batched(int32_t id, int64_t M, int64_t N, int64
 gemm_status_t gemm_run_config(gemm_handle_t h, const void* A, const void* B, void* C,
                               int64_t M, int64_t N, int64_t K, int32_t dtype,
                               int32_t config_id, void* stream);
+
+/* The configuration and split count gemm_run_ws would use with
+ * workspace_bytes of workspace (*splits = 1 when it does not split); -1 when
+ * the arguments are invalid.  splits may be NULL. */
+int32_t gemm_select_config_ws(const void* A, const void* B, const void* C,
+                              int64_t M, int64_t N, int64_t K, int32_t dtype,
+                              int64_t workspace_bytes, int32_t* splits);
+
+/* gemm_run_ws with a forced configuration and split count.  splits = 1 is
+ * gemm_run_config.  splits in 2 .. 64 needs a 16x16x32 tile configuration
+ * (GEMM_ERR_CONFIG_MISMATCH otherwise) and splits*M*N*4 bytes of workspace
+ * (GEMM_ERR_INVALID_VALUE otherwise); the count actually used is lowered
+ * until no split is left without K-steps (K-steps of the configuration's
+ * bk).  Other errors as gemm_run_ws. */
+gemm_status_t gemm_run_ws_config(gemm_handle_t h, const void* A, const void* B, void* C,
+                                 int64_t M, int64_t N, int64_t K, int32_t dtype,
+                                 int32_t config_id, int32_t splits,
+                                 void* workspace, int64_t workspace_bytes, void* stream);
 
 /* gemm_run_batched with a forced configuration (alignment also covers the
  * strides: with batch > 1 they must be multiples of 16 bytes). */

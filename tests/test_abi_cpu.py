@@ -337,3 +337,63 @@ def test_8bit_tile_size_follows_the_tile_count():
     cid = dg.gemm_select_config_batched(A, Bb, Cb, 16, 1024, 1024, 1024, 1024 * 1024, 1024 * 1024,
                                         1024 * 1024, 3)
     assert dg.gemm_config_info(cid)["name"].startswith("fp8_256x256")
+
+
+# ---------------------------------------------------------------- split K with a workspace
+def test_workspace_sizes_follow_the_split_rule():
+    L = _lib.lib()
+    # 256 x 4096: 64 tiles of 128 x 128 -> 4 splits of 32 K-steps
+    assert L.gemm_workspace_size(256, 4096, 4096, 2) == 4 * 256 * 4096 * 4
+    # 64 x 14336: 112 tiles -> 2 splits
+    assert L.gemm_workspace_size(64, 14336, 4096, 1) == 2 * 64 * 14336 * 4
+    # 16 rows: 32 tiles -> 8 splits; 512 x 4096: 128 tiles -> 2
+    assert L.gemm_workspace_size(16, 4096, 4096, 2) == 8 * 16 * 4096 * 4
+    assert L.gemm_workspace_size(512, 4096, 4096, 2) == 2 * 512 * 4096 * 4
+    # enough tiles, up to 8 rows (the strip kernel), GEMV, fp32, 8-bit, K < 2048, K = 0: no split
+    for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2), (8, 4096, 4096, 2),
+                 (1, 4096, 4096, 1), (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
+                 (1024, 1024, 1024, 2), (256, 4096, 2016, 2), (256, 4096, 0, 2), (0, 4096, 4096, 2),
+                 (256, 4096, 4092, 2)]:
+        assert L.gemm_workspace_size(*args) == 0, args
+    # the split count never leaves a split without K-steps, and each has >= 16 of them
+    for M, N, K in [(128, 1024, 4096), (256, 512, 8192), (256, 4096, 2048), (100, 200, 30000)]:
+        ws = L.gemm_workspace_size(M, N, K, 2)
+        s = ws // (M * N * 4)
+        assert ws == 0 or (2 <= s <= 16 and -(-K // 32) >= 16 * s), (M, N, K, s)
+    assert L.gemm_workspace_size(-1, 4, 4, 2) == -1
+    assert L.gemm_workspace_size(4, 4, 4, 9) == -1
+
+
+def test_select_config_ws_falls_back_when_the_workspace_is_short():
+    need = dg.gemm_workspace_size(256, 4096, 4096, 2)
+    cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need)
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32" and s == 4
+    cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need - 1)
+    assert s == 1 and cid == dg.gemm_select_config(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2)
+    # misaligned A: the generic kernel, no split
+    cid, s = dg.gemm_select_config_ws(A + 2, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need)
+    assert (cid, s) == (0, 1)
+    assert dg.gemm_select_config_ws(A, B, C, -1, 4, 4, 2, need)[0] == -1
+
+
+def test_workspace_argument_errors():
+    L = _lib.lib()
+    M, N, K = 256, 4096, 4096
+    Bb, Cb = A + (1 << 30), A + (1 << 31)
+    W = A + (1 << 33)
+    need = 4 * M * N * 4
+    run = lambda *a: L.gemm_run_ws(None, A, Bb, Cb, M, N, K, 2, *a, None)
+    assert run(W, -1) == INVALID
+    assert run(None, 64) == INVALID
+    assert run(W + 8, need) == INVALID                 # not 16-byte aligned
+    assert run(Cb + 1024, need) == ALIAS               # overlaps C
+    assert run(A, need) == ALIAS                       # overlaps A
+    assert run(W, need) == INVALID                     # valid arguments, but no handle
+    cfg = lambda cid, s, w, nb: L.gemm_run_ws_config(None, A, Bb, Cb, M, N, K, 2, cid, s, w, nb, None)
+    assert cfg(12, 0, W, need) == INVALID
+    assert cfg(12, 65, W, need) == INVALID
+    assert cfg(0, 2, W, need) == MISMATCH               # the generic kernel does not split
+    assert cfg(15, 2, W, need) == MISMATCH              # nor does the strip kernel
+    assert cfg(12, 4, W, need - 1) == INVALID           # workspace too small for 4 splits
+    assert cfg(12, 4, W, need) == INVALID               # valid, but no handle
+    assert cfg(99, 2, W, need) == INVALID

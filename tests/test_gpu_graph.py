@@ -1,6 +1,7 @@
 """gemm_run inside a HIP graph (captured through torch's graph API on the
 caller's stream).  The launch path makes no allocation and no memset, so a
-captured product is one kernel node; every replay must give, bit for bit, what
+captured product is one kernel node (two for a product split over K, whose
+workspace comes from the graph's memory pool); every replay must give, bit for bit, what
 an eager call gives on the inputs as they are at that moment.  Between the
 replays the test does eager work of its own (rewriting A in place, an eager
 product, synchronisation), as a program around a graph would.
@@ -28,7 +29,8 @@ CASES = [(1000, 1000, 1000, "f16"),        # 16x16x32 kernel at 128 x 128
          (4096, 4, 4096, "bf16"),          # matrix-vector kernel
          (127, 255, 65, "f16"),            # generic kernel
          (1024, 1024, 2048, "fp8_e4m3"),   # 8-bit kernel at 128 x 128
-         (32, 4096, 4096, "fp8_e5m2")]     # 8-bit strip kernel
+         (32, 4096, 4096, "fp8_e5m2"),     # 8-bit strip kernel
+         (256, 4096, 4096, "bf16")]        # split K: partial sums in a workspace, then the sum
 
 
 @pytest.mark.parametrize("case", CASES)
