@@ -213,7 +213,7 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
             line(cid, info["name"], _time_us(run_cfg, iters, stream))
             # split K for the tile configurations on shapes with fewer tiles than CUs
             tiles = -(-M // info["bm"]) * -(-N // info["bn"])
-            if ws_max and info["name"].startswith("mfma16x16") and tiles < 256:
+            if ws_max and info["name"].startswith(("mfma16x16", "fp8_")) and tiles < 256:
                 for sp in (2, 4, 8, 16):
                     if -(-K // info["bk"]) < 2 * sp:
                         break

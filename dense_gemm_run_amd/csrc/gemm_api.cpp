@@ -237,33 +237,61 @@ int effective_splits(int splits, int64_t K, int bk)
     return (int)((steps + q - 1) / q);
 }
 
-constexpr int kSplitConfig = 12;   // the 16x16x32 kernel at 128 x 128 tiles
+constexpr int kSplitConfig = 12;     // the 16x16x32 kernel at 128 x 128 tiles
+constexpr int kSplitConfig8 = 26;    // the 8-bit kernel at 128 x 128 x 64
+
+// Split count for `t128` tiles of 128 x 128 and `steps` K-steps: near 256
+// workgroups in all, at most 16 splits, at least 16 K-steps per split, and
+// none without K-steps.
+int split_count(int64_t t128, int64_t steps, int64_t K, int bk)
+{
+    int s = (int)((256 + t128 / 2) / t128);
+    if (s > 16) s = 16;
+    while (s > 1 && steps < 16 * (int64_t)s) --s;
+    return effective_splits(s, K, bk);
+}
 
 // The choice of gemm_run_ws: a configuration and a split count (1: none).
-// fp16/bf16 products of one matrix with K >= 2048 (64 K-steps) whose
-// 128 x 128 tiles number at most 160 split K over the 16x16x32 kernel at
-// 128 x 128, so that tiles * splits comes near 256 workgroups, with at least
-// 16 K-steps (512 of K) per split.  Up to 8 rows stay on the strip kernel.
-// (Sweep, bf16: 256 x 4096 x 4096 in 19.6 us with 4 splits against 31.9 in
-// one pass; 16 x 4096 x 14336 22.6 with 8 against 38.0 on the strip kernel;
-// 1024^3 14.4 with 2 against 10.7, hence the K floor.)
+// Products of one matrix only; the numbers are from the shape sweep.
+//  * fp16/bf16 with K >= 2048 (64 K-steps) and at most 160 tiles of
+//    128 x 128: the 16x16x32 kernel at 128 x 128 with split_count splits;
+//    up to 8 rows stay on the strip kernel.  (256 x 4096 x 4096: 19.6 us
+//    with 4 splits against 31.9 in one pass; 16 x 4096 x 14336: 22.6 with 8
+//    against 38.0 on the strip kernel; 1024^3: 14.4 with 2 against 10.7,
+//    hence the K floor.)
+//  * 8-bit inputs, up to 128 rows, K >= 2048: the 8-bit kernel at
+//    128 x 128 x 64, split likewise; up to 16 rows with K < 8192 stay on
+//    the strip kernel.  Beyond 128 rows the fp32 partial sums (4 bytes per
+//    output against 1-byte inputs) cost more than the split gains.
+//    (64 x 4096 x 14336: 17.0 us with 8 splits against 38.4 on the strip
+//    kernel; 256 x 4096 x 4096: 16.5 in one pass, 17.6 with 2 splits.)
 int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
 {
     splits = 1;
     const int c = select(p);
-    if (p.batch != 1 || (p.dtype != kF16 && p.dtype != kBF16) || p.M == 0 || p.N == 0) return c;
-    if (!accepts(kTable[kSplitConfig], p) || kTable[c].kind == kGemv) return c;
-    if (kTable[c].kind == kSkinny && p.M <= 8) return c;
-    const int64_t steps = (p.K + 31) / 32;
+    if (p.batch != 1 || p.M == 0 || p.N == 0) return c;
     const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-    if (steps < 64 || t128 > 160) return c;
-    int s = (int)((256 + t128 / 2) / t128);
-    if (s > 16) s = 16;
-    while (s > 1 && steps < 16 * (int64_t)s) --s;
-    s = effective_splits(s, p.K, 32);
+    int cfg = -1, s = 1;
+    if (p.dtype == kF16 || p.dtype == kBF16) {
+        if (!accepts(kTable[kSplitConfig], p) || kTable[c].kind == kGemv) return c;
+        if (kTable[c].kind == kSkinny && p.M <= 8) return c;
+        const int64_t steps = (p.K + 31) / 32;
+        if (steps < 64 || t128 > 160) return c;
+        cfg = kSplitConfig;
+        s = split_count(t128, steps, p.K, 32);
+    } else if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
+        if (!accepts(kTable[kSplitConfig8], p) || p.M > 128) return c;
+        if (kTable[c].kind == kSkinny && p.M <= 16 && p.K < 8192) return c;
+        const int64_t steps = (p.K + 63) / 64;
+        if (steps < 32) return c;
+        cfg = kSplitConfig8;
+        s = split_count(t128, steps, p.K, 64);
+    } else {
+        return c;
+    }
     if (s < 2 || (int64_t)s * p.M * p.N * 4 > ws_bytes) return c;
     splits = s;
-    return kSplitConfig;
+    return cfg;
 }
 
 // Workspace argument checks (after check_args).
@@ -299,7 +327,10 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
         if (err == hipSuccess && splits > 1) err = launch_reduce_splits(la);
         break;
     case kGemv: err = launch_gemv(e.cfg, la); break;
-    case kFp8: err = launch_fp8(e.cfg, la); break;
+    case kFp8:
+        err = launch_fp8(e.cfg, la);
+        if (err == hipSuccess && splits > 1) err = launch_reduce_splits(la);
+        break;
     case kSkinny: err = launch_skinny(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
@@ -333,7 +364,7 @@ gemm_status_t run_ws_config(gemm_handle_t h, const Problem& p, int32_t config_id
     if (!accepts(e, p)) return GEMM_ERR_CONFIG_MISMATCH;
     int s = 1;
     if (splits > 1) {
-        if (e.kind != kMfma16x16 || p.batch != 1) return GEMM_ERR_CONFIG_MISMATCH;
+        if ((e.kind != kMfma16x16 && e.kind != kFp8) || p.batch != 1) return GEMM_ERR_CONFIG_MISMATCH;
         s = effective_splits(splits, p.K, e.cfg.bk);
         if (s > 1 && (int64_t)s * p.M * p.N * 4 > ws_bytes) return GEMM_ERR_INVALID_VALUE;
     }

@@ -47,6 +47,10 @@
 //    LDS traffic of a K-step are spread over its MFMAs.
 //  * Epilogue: fp32 -> bf16 (round to nearest even), staged through LDS and
 //    written as whole row segments, skipping rows >= M and columns >= N.
+//  * Split K (SPLIT): as in the 16x16x32 kernel, `splits` workgroups per
+//    tile walk disjoint ranges of K-steps and write their fp32 sums,
+//    unrounded, to their own M x N slice of a workspace; a second kernel adds
+//    the slices in split order and rounds once to bf16.
 #include "gemm_internal.h"
 #include "gemm_device.h"
 
@@ -89,10 +93,10 @@ template <int BN> __device__ __forceinline__ int swz_b(int k)
     return BN == 256 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
 }
 
-template <int FMT, int BM, int BN, int BK>
+template <int FMT, int BM, int BN, int BK, bool SPLIT>
 __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_kernel(
     const unsigned char* A, const unsigned char* B, __bf16* C,
-    int M, int N, int K, int group_m, Batch bt)
+    int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
 {
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
@@ -124,11 +128,21 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
-    A += b * bt.sa;
-    B += b * bt.sb;
-    C += b * bt.sc;
+    // with split K the batch axis of the tile order is the split (one product)
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, SPLIT ? splits : bt.count, group_m, true, b, tm, tn);
+    if constexpr (!SPLIT) {
+        A += b * bt.sa;
+        B += b * bt.sb;
+        C += b * bt.sc;
+    }
     const int m0 = tm * BM, n0 = tn * BN;
+    // K range of this workgroup: [kb, ke)
+    int kb = 0, ke = K;
+    if constexpr (SPLIT) {
+        const int q = cdiv_i(cdiv_i(K, BK), splits) * BK;
+        kb = b * q;
+        ke = kb + q < K ? kb + q : K;
+    }
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -164,8 +178,8 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
 
     u32x4 stg[LEAD][A_LOADS];
     auto load_a = [&](int slot, int k0_in, int j) __attribute__((always_inline)) {
-        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
-        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
+        const unsigned off = a_kp[j] < ke - k0 ? a_voff[j] : kOOB;
         stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0, 0));
     };
     auto store_a = [&](int st, int slot, int j) __attribute__((always_inline)) {
@@ -173,11 +187,11 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
         *(u32x4 __attribute__((address_space(3)))*)p = stg[slot][j];
     };
     auto load_b = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
-        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
-        const int krem = K - k0;
+        const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
+        const int krem = ke - k0;
         const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
         const __amdgpu_buffer_rsrc_t rbk =
-            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N);
+            make_rsrc(B + (size_t)(k0 < ke ? k0 : 0) * N, (unsigned)rows * (unsigned)N);
         const unsigned off = b_voff[j];
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rbk, (void __attribute__((address_space(3)))*)(b_stage(st) + (wave * B_LOADS + j) * 1024), 16,
@@ -328,7 +342,7 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
 
     // K-steps, rounded up to the LEAD-step unroll: the extra steps multiply
     // the zeros their loads brought in.
-    const int nk = cdiv_i(cdiv_i(K, BK), LEAD) * LEAD;
+    const int nk = cdiv_i(cdiv_i(ke - kb, BK), LEAD) * LEAD;
     kstep(0, 0, true);
 #pragma unroll
     for (int q = 1; q < LEAD; ++q) kstep(q, q, false);
@@ -349,6 +363,28 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     // All loads (the B stages' direct LDS writes included) have landed and
     // every wavefront is done with the stages before they are reused for C.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (SPLIT) {
+        // fp32 sums of this split, unrounded: lane l of tile (bi, bj) holds
+        // row 32*bi + l%32, columns 32*bj + 8g + 4*(l/32) .. +3 in registers
+        // 4g .. 4g+3: one 16-byte store per g (N is a multiple of 16)
+        float* P = ws + (size_t)b * M * N;
+        const int r = m0 + wm * WM + (lane & 31), c = n0 + wn * WN + 4 * (lane >> 5);
+#pragma unroll
+        for (int bi = 0; bi < FM; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < FN; ++bj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    if (r + 32 * bi < M && c + 32 * bj + 8 * g < N) {
+                        f32x4 v;
+                        v[0] = acc[bi][bj][4 * g];
+                        v[1] = acc[bi][bj][4 * g + 1];
+                        v[2] = acc[bi][bj][4 * g + 2];
+                        v[3] = acc[bi][bj][4 * g + 3];
+                        *(f32x4*)(P + (size_t)(r + 32 * bi) * N + c + 32 * bj + 8 * g) = v;
+                    }
+        return;
+    }
     __syncthreads();
     // Each wavefront stages its block through a stage of its own, at most one
     // whole block (one pass) at a time.
@@ -374,10 +410,15 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
-#define DGR_FP8(BM_, BN_, BK_)                                                                        \
-    else if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_)                                        \
-        hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_>), grid, block, 0, a.stream, A, B, C, a.M, \
-                           a.N, a.K, cfg.group_m, a.batch);
+#define DGR_FP8(BM_, BN_, BK_)                                                                            \
+    else if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                          \
+        if (a.splits > 1)                                                                                \
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_, true>), dim3(tiles * a.splits), block, 0, \
+                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);  \
+        else                                                                                             \
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_, false>), grid, block, 0, a.stream, A, B, C, \
+                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);                            \
+    }
     if (false) {}
     DGR_FP8(256, 256, 64)
     DGR_FP8(256, 256, 128)

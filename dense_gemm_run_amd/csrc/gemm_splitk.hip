@@ -1,6 +1,6 @@
 // Second pass of the split-K schedule: C = round(sum over s of P[s]), where
 // P[s] is split s's M x N slice of fp32 sums in the workspace (written by the
-// split variant of the 16x16x32 kernel).  The slices are added in split order
+// split variants of the 16x16x32 and 8-bit kernels).  The slices are added in split order
 // in fp32, so a configuration and split count give one bitwise result, and
 // the sum is rounded once to the output type (round to nearest even), as the
 // single-pass epilogue rounds its accumulator.  Each thread takes 8
@@ -44,7 +44,7 @@ hipError_t launch_reduce_splits(const LaunchArgs& a)
     if (a.dtype == kF16)
         hipLaunchKernelGGL(reduce_splits_kernel<_Float16>, grid, block, 0, a.stream, a.ws,
                            static_cast<_Float16*>(a.C), mn, a.splits);
-    else if (a.dtype == kBF16)
+    else if (a.dtype == kBF16 || a.dtype == kFP8E4M3 || a.dtype == kFP8E5M2)   // 8-bit inputs: bf16 C
         hipLaunchKernelGGL(reduce_splits_kernel<__bf16>, grid, block, 0, a.stream, a.ws,
                            static_cast<__bf16*>(a.C), mn, a.splits);
     else

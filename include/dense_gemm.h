@@ -132,7 +132,8 @@ gemm_status_t gemm_run_batched(gemm_handle_t h, const void* A, const void* B, vo
  * rectangles of work", with the per-block contributions summed across
  * workgroups).  The result is bitwise the same on every call for a given
  * configuration and split count, and meets gemm_run's accuracy (fp32 sums,
- * one rounding).  Only fp16/bf16 products of one matrix split.
+ * one rounding).  Only products of one matrix split: fp16/bf16 ones, and
+ * 8-bit ones of up to 128 rows (their C is bf16 as always).
  * ------------------------------------------------------------------------- */
 
 /* Bytes of workspace gemm_run_ws uses for this product when A, B and C are
@@ -238,7 +239,8 @@ int32_t gemm_select_config_ws(const void* A, const void* B, const void* C,
                               int64_t workspace_bytes, int32_t* splits);
 
 /* gemm_run_ws with a forced configuration and split count.  splits = 1 is
- * gemm_run_config.  splits in 2 .. 64 needs a 16x16x32 tile configuration
+ * gemm_run_config.  splits in 2 .. 64 needs a tile configuration of the
+ * 16x16x32 or the 8-bit kernel
  * (GEMM_ERR_CONFIG_MISMATCH otherwise) and splits*M*N*4 bytes of workspace
  * (GEMM_ERR_INVALID_VALUE otherwise); the count actually used is lowered
  * until no split is left without K-steps (K-steps of the configuration's

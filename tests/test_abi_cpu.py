@@ -349,9 +349,15 @@ def test_workspace_sizes_follow_the_split_rule():
     # 16 rows: 32 tiles -> 8 splits; 512 x 4096: 128 tiles -> 2
     assert L.gemm_workspace_size(16, 4096, 4096, 2) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(512, 4096, 4096, 2) == 2 * 512 * 4096 * 4
-    # enough tiles, up to 8 rows (the strip kernel), GEMV, fp32, 8-bit, K < 2048, K = 0: no split
+    # 8-bit inputs up to 128 rows: 32 tiles, 64 K-steps of 64 -> 4 splits; K = 14336 -> 8
+    assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
+    assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
+    assert L.gemm_workspace_size(16, 14336, 4096, 3) == 2 * 16 * 14336 * 4
+    # enough tiles, up to 8 rows (the strip kernel), GEMV, fp32, K < 2048, K = 0, and 8-bit
+    # inputs beyond 128 rows or up to 16 rows with K < 8192: no split
     for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2), (8, 4096, 4096, 2),
                  (1, 4096, 4096, 1), (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
+                 (16, 4096, 4096, 3), (129, 4096, 4096, 3), (64, 4096, 1024, 4),
                  (1024, 1024, 1024, 2), (256, 4096, 2016, 2), (256, 4096, 0, 2), (0, 4096, 4096, 2),
                  (256, 4096, 4092, 2)]:
         assert L.gemm_workspace_size(*args) == 0, args
@@ -394,6 +400,7 @@ def test_workspace_argument_errors():
     assert cfg(12, 65, W, need) == INVALID
     assert cfg(0, 2, W, need) == MISMATCH               # the generic kernel does not split
     assert cfg(15, 2, W, need) == MISMATCH              # nor does the strip kernel
+    assert cfg(22, 2, W, need) == MISMATCH              # nor the 8-bit strip kernel
     assert cfg(12, 4, W, need - 1) == INVALID           # workspace too small for 4 splits
     assert cfg(12, 4, W, need) == INVALID               # valid, but no handle
     assert cfg(99, 2, W, need) == INVALID

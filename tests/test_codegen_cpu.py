@@ -28,9 +28,9 @@ FAMILIES = {
                   # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32 + 192x256x32)
                   # x {one pass, split K}
                   24, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
-    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)E()",
-            # {e4m3, e5m2} x {256x256, 128x128} x {64, 128}
-            8, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
+    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)E",
+            # {e4m3, e5m2} x {256x256, 128x128} x {64, 128} x {one pass, split K}
+            16, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
 }
 
 

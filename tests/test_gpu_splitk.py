@@ -129,3 +129,45 @@ def test_a_short_workspace_runs_the_single_pass_schedule():
     assert torch.equal(c_short.view(torch.int16), c_plain.view(torch.int16))
     sampled_check(A, B, "bf16", c_ws, seed=1)
     sampled_check(A, B, "bf16", c_short, seed=2)
+
+
+@pytest.mark.parametrize("dtype", ["fp8_e4m3", "fp8_e5m2"])
+@pytest.mark.parametrize("shape", [(300, 528, 1040), (64, 272, 4112), (130, 256, 2064)])
+def test_8bit_tile_configurations_at_every_split_count(dtype, shape):
+    from test_gpu_fp8 import check as check8
+    M, N, K = shape
+    A, B = make_operands(M, N, K, dtype, "normal", 1600 + M)
+    a, b = A.cuda(), B.cuda()
+    for cid in range(dg.gemm_config_count()):
+        info = dg.gemm_config_info(cid)
+        if not info["name"].startswith("fp8_") or not accepts(cid, a, b, M, N, K):
+            continue
+        for s in (2, 3, 7, 16):
+            note(f"[splitk] config {cid} {info['name']} splits {s} {dtype} {shape}")
+            c = dg.gemm(a, b, config=cid, splits=s)
+            torch.cuda.synchronize()
+            check8(A, B, dtype, c)
+
+
+@pytest.mark.parametrize("shape", [(64, 4096, 14336), (16, 14336, 4096), (100, 4096, 4096)])
+def test_selected_8bit_split_shapes_sampled(shape):
+    from oracle import fp8, tolerance
+    M, N, K = shape
+    A, B = make_operands(M, N, K, "fp8_e4m3", "normal", 1700 + M)
+    a, b = A.cuda(), B.cuda()
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    need = dg.gemm_workspace_size(M, N, K, 3)
+    cid, s = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, 3, need)
+    note(f"[splitk] selected {dg.gemm_config_info(cid)['name']} x {s} for 8-bit {shape}")
+    assert s > 1 and dg.gemm_config_info(cid)["name"].startswith("fp8_128x128")
+    dg.gemm(a, b, out=c)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M)
+    pr = np.concatenate([np.full(N, 0), np.full(N, M - 1), np.arange(M), rng.integers(0, M, 20000)])
+    pc = np.concatenate([np.arange(N), np.arange(N), np.full(M, N - 1), rng.integers(0, N, 20000)])
+    A64 = fp8.decode(fp8._bits(A), "e4m3")
+    B64 = fp8.decode(fp8._bits(B), "e4m3")
+    ref = gemm64.bits_to_f64(gemm64.round_to_bits(gemm64.gemm_points_f64(A64, B64, pr, pc), "bf16"), "bf16")
+    got = c[torch.from_numpy(pr).cuda(), torch.from_numpy(pc).cuda()].to("cpu", torch.float64).numpy()
+    rep = tolerance.compare(got, ref, "bf16", K, float(np.abs(A64).max()), float(np.abs(B64).max()))
+    assert rep["ok"], rep
