@@ -69,17 +69,21 @@ def kernel_source_digest(kernel_cfg: str) -> str:
     """sha256 (16 hex digits) of what configuration ``kernel_cfg`` runs: its
     kernel file, the shared headers, and its own entry of the configuration
     table (tile, K-step, workgroup size and order, as the library reports
-    them)."""
+    them).  A name ending in _split<s> (split K) adds the reduction's source
+    and the split count."""
     import dense_gemm_run_amd as dg
-    fam = next(f for p, f in KERNEL_FILES.items() if kernel_cfg.startswith(p))
+    base, _, split = kernel_cfg.partition("_split")
+    fam = next(f for p, f in KERNEL_FILES.items() if base.startswith(p))
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dense_gemm_run_amd", "csrc")
-    for f in sorted([fam] + SHARED_FILES):
+    for f in sorted([fam] + SHARED_FILES + (["gemm_splitk.hip"] if split else [])):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     info = next(dg.gemm_config_info(i) for i in range(dg.gemm_config_count())
-                if dg.gemm_config_info(i)["name"] == kernel_cfg)
+                if dg.gemm_config_info(i)["name"] == base)
     h.update(json.dumps({k: info[k] for k in sorted(info) if k != "id"}).encode())
+    if split:
+        h.update(b"splits=" + split.encode())
     return h.hexdigest()[:16]
 
 
