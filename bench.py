@@ -122,14 +122,20 @@ def cpu_baseline(A, B, target_s: float = 12.0) -> dict:
     probe_rows = max(1, min(M, threads))
     t_probe, _ = gemm64.time_rows_f64(A64, B64, 0, probe_rows, threads)
     rows = int(min(M, max(probe_rows, probe_rows * target_s / max(t_probe, 1e-6))))
-    rows = max(threads, rows - rows % threads) if rows >= threads else rows
+    if rows < M:   # a block of rows: whole rounds of rows over the threads
+        rows = max(threads, rows - rows % threads) if rows >= threads else rows
     t, _ = gemm64.time_rows_f64(A64, B64, 0, rows, threads)
     flops = 2.0 * rows * N * K
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product"
-                      f"{' (the first of the batch of %d)' % batch if batch > 1 else ''} "
-                      f"({rows / M / batch:.4f} of the work), fp64 three-loop oracle, "
-                      f"{t:.2f} s on {threads} threads"}
+    out = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"rows 0..{rows - 1} of the {M}x{N}x{K} product"
+                     f"{' (the first of the batch of %d)' % batch if batch > 1 else ''} "
+                     f"({rows / M / batch:.4f} of the work), fp64 three-loop oracle, "
+                     f"{t:.2f} s on {threads} threads"}
+    if rows == M and batch == 1 and t < 0.05:
+        # a product this small is also timed on one thread (median of 5)
+        reps = sorted(gemm64.time_rows_f64(A64, B64, 0, M, 1)[0] for _ in range(5))
+        out["single_thread_s"] = reps[2]
+    return out
 
 
 SWEEP_SQUARE = [512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192]
@@ -256,6 +262,9 @@ def main(argv=None) -> int:
     p.add_argument("--graph", type=int, default=0,
                    help="time K steps as K/G replays of a HIP graph of G captured steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cold", action="store_true",
+                   help="also time the steps rotating over copies of A and B that together exceed "
+                        "twice the 256 MB Infinity Cache (reported as 'cold')")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for scaling HBM counters)")
     p.add_argument("--sweep", choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2"], default=None,
@@ -307,7 +316,7 @@ def main(argv=None) -> int:
     log(f"[bench] kernel configuration {cid} {kernel_name}")
     stream = torch.cuda.current_stream(dev)
 
-    def step(st=stream):
+    def step(st=stream, a=a, b=b):
         if w.batch > 1:
             dg.gemm_run_batched_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch, w.M,
                                        w.N, w.K, *strides, code, cid, st.cuda_stream)
@@ -406,6 +415,27 @@ def main(argv=None) -> int:
         "wall_s_timed_region": round(wall, 4),
         "launch": f"hip graph of {args.graph} steps" if args.graph else "one gemm_run call per step",
     }
+    if args.cold:
+        # the same product on copies of A and B that together exceed twice the
+        # Infinity Cache, one copy per step in turn, so every step starts with
+        # its inputs in HBM only
+        set_bytes = a.numel() * a.element_size() + b.numel() * b.element_size()
+        sets = max(2, -(-2 * 256 * 2**20 // set_bytes))
+        copies = [(a.clone(), b.clone()) for _ in range(sets)]
+        for i in range(2 * sets):
+            step(stream, *copies[i % sets])
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(stream, *copies[i % sets])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_cold = ev0.elapsed_time(ev1) / args.steps
+        out["cold"] = {"value": round(w.flops / (ms_cold * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                       "ms_per_step": round(ms_cold, 5), "buffer_sets": sets,
+                       "rotated_bytes": sets * set_bytes}
+        log(f"[bench] cold: {ms_cold * 1e3:.1f} us/step over {sets} copies of A and B")
+        del copies
     dg.gemm_destroy(h)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a block of rows")
