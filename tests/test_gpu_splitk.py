@@ -171,3 +171,18 @@ def test_selected_8bit_split_shapes_sampled(shape):
     got = c[torch.from_numpy(pr).cuda(), torch.from_numpy(pc).cuda()].to("cpu", torch.float64).numpy()
     rep = tolerance.compare(got, ref, "bf16", K, float(np.abs(A64).max()), float(np.abs(B64).max()))
     assert rep["ok"], rep
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_long_k_single_pass_and_split(dtype):
+    """K = 65536: 2048 K-steps of 32 in one workgroup (the K loop's counters
+    and buffer offsets far from their first round), and the same product
+    split 16 ways; a K that is not a multiple of 32 ends mid-step."""
+    for M, N, K in [(136, 264, 65536), (128, 256, 40008)]:
+        A, B = make_operands(M, N, K, dtype, "normal", 1800 + K % 97)
+        a, b = A.cuda(), B.cuda()
+        for cid, s in [(12, 1), (6, 1), (12, 16), (28, 5)]:
+            note(f"[splitk] long K {dtype} {(M, N, K)} config {cid} splits {s}")
+            c = dg.gemm(a, b, config=cid, splits=s)
+            torch.cuda.synchronize()
+            check_full(A, B, dtype, c)
