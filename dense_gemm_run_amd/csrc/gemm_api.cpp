@@ -71,6 +71,10 @@ const Entry kTable[] = {
     {{27, 128, 128, 128, 4, 256, 0x18, 1, 1, "fp8_128x128x128"}, kFp8},
     // 192 x 256 tiles: whole waves of CUs where 256 x 256 leaves a partial one
     {{28, 192, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_192x256x32"}, kMfma16x16},
+    // the 16x16x32 kernel with A loaded direct to LDS too (one ring for A and B)
+    {{29, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x32_adma", 1}, kMfma16x16},
+    {{30, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_128x128x32_adma", 1}, kMfma16x16},
+    {{31, 192, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_192x256x32_adma", 1}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -181,7 +185,10 @@ bool accepts(const Entry& e, const Problem& p)
 //    below), the same kernel at 192 x 256 (3072^3: 58.9 against 69.7 us;
 //    6144^3: 394 against 410);
 //  * otherwise the 16x16x32 kernel at 128 x 128, which gives 4x the tiles
-//    (2048^3: 842 TFLOP/s against 383 at 256 x 256).
+//    (2048^3: 842 TFLOP/s against 383 at 256 x 256);
+//  * each of these tiled choices in its variant with A loaded direct to
+//    LDS (configs 29-31) unless A and B together overflow the Infinity Cache
+//    (see the end of select).
 // The 32x32x16 configurations and the 256 x 128 tiles were never the fastest
 // in the sweep and stay available through gemm_run_config.
 int select(const Problem& p)
@@ -215,14 +222,21 @@ int select(const Problem& p)
         if (!wide) return p.M <= 64 ? 19 : 20;
     }
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    if (t256 < 128) return 12;
+    if (t256 < 128) return 30;
     // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4
     // of a 256 x 256 tile's work at ~94 % of its rate, so a wave of them costs
     // ~0.8 of a wave of 256 x 256 tiles; it wins where 256 x 256 leaves a
     // partial last wave (3072^2: 144 tiles, one wave of 192 x 256 tiles).
     const int64_t t192 = ((p.M + 191) / 192) * ((p.N + 255) / 256) * p.batch;
     const int64_t w256 = (t256 + 255) / 256, w192 = (t192 + 255) / 256;
-    return w192 * 80 < w256 * 95 ? 28 : 6;
+    const bool rows192 = w192 * 80 < w256 * 95;
+    // A direct to LDS (one ring with B) unless the operands overflow the
+    // 256 MB Infinity Cache: then loads come from HBM and A's register path,
+    // which covers half a K-step more latency, was faster
+    // (8192 x 4096 x 14336: 1352 against 1310 TFLOP/s; 4096^3: 1245 against
+    // 1281-1284 the other way round)
+    const bool adma = (p.M * p.K + p.K * p.N) * in_bytes(p.dtype) * p.batch <= ((int64_t)256 << 20);
+    return rows192 ? (adma ? 31 : 28) : (adma ? 29 : 6);
 }
 
 // ---- split K (gemm_run_ws)
@@ -364,7 +378,8 @@ gemm_status_t run_ws_config(gemm_handle_t h, const Problem& p, int32_t config_id
     if (!accepts(e, p)) return GEMM_ERR_CONFIG_MISMATCH;
     int s = 1;
     if (splits > 1) {
-        if ((e.kind != kMfma16x16 && e.kind != kFp8) || p.batch != 1) return GEMM_ERR_CONFIG_MISMATCH;
+        if ((e.kind != kMfma16x16 && e.kind != kFp8) || e.cfg.sched != 0 || p.batch != 1)
+            return GEMM_ERR_CONFIG_MISMATCH;
         s = effective_splits(splits, p.K, e.cfg.bk);
         if (s > 1 && (int64_t)s * p.M * p.N * 4 > ws_bytes) return GEMM_ERR_INVALID_VALUE;
     }

@@ -66,6 +66,7 @@ struct Config {
     int32_t needs_vec_align;
     int32_t xcd_remap;
     const char* name;
+    int32_t sched;   // pipeline variant of the kernel family (0: its default)
 };
 
 // The batch a launch covers: `count` products, matrix b of A (B, C) starting

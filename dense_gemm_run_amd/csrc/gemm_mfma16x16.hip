@@ -147,7 +147,7 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
     }
 }
 
-template <typename T, int BM, int BN, int BK, bool SPLIT>
+template <typename T, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
 __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const T* A, const T* B, T* C,
     int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
@@ -177,11 +177,20 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // Every stage is an LDS object of its own: the compiler tracks the
     // direct-to-LDS loads per object, so reading one B stage does not wait
     // for the loads still landing in the others.
-    __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb2[SB > 2 ? B_BYTES : 1], sb3[SB > 2 ? B_BYTES : 1];
-    auto a_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sa0 : sa1); };
-    auto b_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+    // ADMA: A also goes global -> LDS directly, into the same ring as B; each
+    // ring stage is one LDS object holding A (first) and B of one K-step.
+    static_assert(!ADMA || (SB == 4 && LEAD == 4 && !SPLIT), "direct A loads: 32-deep K-steps, one pass");
+    constexpr int SA_BYTES = ADMA ? 1 : A_BYTES;
+    constexpr int SB_BYTES = ADMA ? A_BYTES + B_BYTES : B_BYTES;
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[SA_BYTES], sa1[SA_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[SB_BYTES], sb1[SB_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb2[SB > 2 ? SB_BYTES : 1], sb3[SB > 2 ? SB_BYTES : 1];
+    auto b_obj = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+    auto a_stage = [&](int st) __attribute__((always_inline)) {
+        if constexpr (ADMA) return b_obj(st);
+        else return (lds_byte*)(st == 0 ? sa0 : sa1);
+    };
+    auto b_stage = [&](int st) __attribute__((always_inline)) { return b_obj(st) + (ADMA ? A_BYTES : 0); };
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
@@ -243,6 +252,15 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
         const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
         const unsigned off = a_kp[j] < ke - k0 ? a_voff[j] : kOOB;
         stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0 * 2, 0));
+    };
+    // ADMA: A rows of the K-step at k0, load j -> A part of ring stage `st`
+    // (direct to LDS, at the place store_a gives the same piece).
+    auto load_a_lds = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
+        const unsigned off = a_kp[j] < ke - k0 ? a_voff[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (void __attribute__((address_space(3)))*)(a_stage(st) + (wave * A_LOADS + j) * 1024), 16,
+            off, k0 * 2, 0, 0);
     };
     // Register slot `slot`, load j -> A stage `st`.
     auto store_a = [&](int st, int slot, int j) __attribute__((always_inline)) {
@@ -319,9 +337,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // still be in flight.
 #pragma unroll
     for (int g = -LEAD; g < 0; ++g) {
-        if (g + LEAD >= 0)
+        if (g + LEAD >= 0) {
 #pragma unroll
-            for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * BK, j);
+            for (int j = 0; j < A_LOADS; ++j) {
+                if constexpr (ADMA) load_a_lds(g + LEAD, (g + LEAD) * BK, j);
+                else load_a(g + LEAD, (g + LEAD) * BK, j);
+            }
+        }
         asm volatile("" ::: "memory");
         if (g + SB >= 0)
 #pragma unroll
@@ -329,8 +351,10 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
         asm volatile("" ::: "memory");
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 1) * LOADS));   // group -SB (B of K-step 0) landed
+    if constexpr (!ADMA) {
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
+        for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -360,9 +384,13 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // loops rather than one with a branch: the compiler only unrolls loops
     // below a size limit, and everything here must unroll.)
     auto kslice = [&](const int q, int it, const int sl, const bool first) __attribute__((always_inline)) {
-        const int sta = q & 1, stb = q % SB, set = (q * NS + sl) & 1;
-        constexpr int NOPS1 = 2 * A_LOADS;
-        constexpr int NOPS2 = B_LOADS + NR;
+        // ADMA: A shares B's ring (stage it % SB); its loads of K-step it+SB
+        // go after the barrier with B's
+        const int sta = ADMA ? q % SB : q & 1, stb = q % SB, set = (q * NS + sl) & 1;
+        const int sta_next = ADMA ? (q + 1) % SB : sta ^ 1;
+        constexpr int NOPS1 = ADMA ? 0 : 2 * A_LOADS;
+        constexpr int LD2 = ADMA ? A_LOADS + B_LOADS : B_LOADS;   // loads after the barrier
+        constexpr int NOPS2 = LD2 + NR;
         auto mfma = [&](int xx) __attribute__((always_inline)) {
             if (first && sl == 0)
                 Mfma16x16<T>::first(acc[xx / FN][xx % FN], fb[set][xx % FN], fa[set][xx / FN]);
@@ -379,12 +407,14 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
                 for (int o = op_lo(xx, NR, NT); o < op_lo(xx + 1, NR, NT); ++o)
                     read_frag(set ^ 1, sta, stb, sl + 1, o);
             }
+            if constexpr (NOPS1 > 0) {
 #pragma unroll
-            for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
-                if (o < A_LOADS)
-                    store_a(sta ^ 1, (q + 1) % LEAD, o);
-                else
-                    load_a(q, (it + LEAD) * BK, o - A_LOADS);
+                for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
+                    if (o < A_LOADS)
+                        store_a(sta ^ 1, (q + 1) % LEAD, o);
+                    else
+                        load_a(q, (it + LEAD) * BK, o - A_LOADS);
+                }
             }
         }
         if (lo < BAR && BAR <= hi) {
@@ -393,8 +423,9 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
             // any (it may otherwise move loads whose results are needed only
             // steps later).
             asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS + A_LOADS));
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
+            // ADMA: groups it-2 and it-1 were issued after K-step it+1's
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS + (ADMA ? 0 : A_LOADS)));
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes (and reads) done
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
@@ -403,10 +434,12 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
             mfma(x - lo);
 #pragma unroll
             for (int o = op_lo(x - BAR, NOPS2, XS - BAR); o < op_lo(x + 1 - BAR, NOPS2, XS - BAR); ++o) {
-                if (o < B_LOADS)
-                    load_b(stb, (it + SB) * BK, o);
+                if (ADMA && o < A_LOADS)
+                    load_a_lds(stb, (it + SB) * BK, o);
+                else if (o < LD2)
+                    load_b(stb, (it + SB) * BK, o - (ADMA ? A_LOADS : 0));
                 else
-                    read_frag(((q + 1) * NS) & 1, sta ^ 1, (q + 1) % SB, 0, o - B_LOADS);
+                    read_frag(((q + 1) * NS) & 1, sta_next, (q + 1) % SB, 0, o - LD2);
             }
         }
     };
@@ -480,6 +513,21 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
+    if (cfg.sched == 1) {   // A direct to LDS as well; one pass only
+        if (a.splits > 1) return hipErrorInvalidValue;
+        if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 32)
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 256, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
+                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, false, true>), grid, block, 0, a.stream, A, B,
+                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 32)
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 192, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
+                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
 #define DGR_LAUNCH(BM_, BN_, BK_)                                                                          \
     if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                                \
         if (a.splits > 1)                                                                                 \

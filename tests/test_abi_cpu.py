@@ -314,11 +314,16 @@ def test_192_row_tiles_where_256_leaves_a_partial_wave():
     # 144 tiles of 256 x 256 -> one wave of 192 x 256; 576 (2.25 waves) -> 768 (3 whole waves)
     for M, N, K in [(3072, 3072, 3072), (6144, 6144, 6144)]:
         for dt in (1, 2):
-            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_192x256x32", (M, N, K)
+            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_192x256x32_adma", (M, N, K)
     # whole waves of 256 x 256 tiles keep them
-    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 12288, 4096), (8192, 4096, 14336),
-                    (8192, 14336, 4096), (5120, 5120, 5120)]:
-        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_256x256x32", (M, N, K)
+    for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 12288, 4096), (8192, 14336, 4096),
+                    (5120, 5120, 5120)]:
+        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_256x256x32_adma", (M, N, K)
+    # operands beyond the 256 MB Infinity Cache: A through registers
+    assert name(A, Bb, Cb, 8192, 4096, 14336, 2) == "mfma16x16_256x256x32"
+    assert name(A, Bb, Cb, 6144, 6144, 16384, 2) == "mfma16x16_192x256x32"
+    # fewer than 128 tiles: 128 x 128, A direct to LDS
+    assert name(A, Bb, Cb, 2048, 2048, 2048, 1) == "mfma16x16_128x128x32_adma"
     info = dg.gemm_config_info(28)
     assert (info["bm"], info["bn"], info["bk"]) == (192, 256, 32)
 

@@ -24,11 +24,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # source file, kernel-name pattern (-> bm, bn, bk), instances, element bytes,
 # MFMA mnemonic, K depth of one MFMA, outputs of one MFMA
 FAMILIES = {
-    "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)ELb(\d)E",
+    "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E",
                   # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32 + 192x256x32)
-                  # x {one pass, split K}
-                  24, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
-    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)E",
+                  # x {one pass, split K}, + {256x256x32, 128x128x32, 192x256x32} with A
+                  # direct to LDS
+                  30, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
+    "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)E()",
             # {e4m3, e5m2} x {256x256, 128x128} x {64, 128} x {one pass, split K}
             16, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
 }
@@ -51,6 +52,7 @@ def compile_family(fam, tmp):
             end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
             found[m.group(1)] = Kernel(fam, bm, bn, bk, ebytes, mnem, kdepth, outs, lines[i:end])
             found[m.group(1)].split = m.group(5) == '1'
+            found[m.group(1)].adma = m.group(6) == '1'
     # per-kernel scratch use from the kernel descriptors
     for i, l in enumerate(lines):
         m = re.match(r"^\s*\.amdhsa_kernel (\S+)", l)
@@ -75,6 +77,7 @@ class Kernel:
         self.sb = 4 if bk * ebytes == 64 else 2           # B stages
         self.scratch = None
         self.split = False  # split-K instance: fp32 partials, no LDS epilogue
+        self.adma = False   # A direct to LDS too, in B's ring
 
 
 @pytest.fixture(scope="module")
@@ -111,7 +114,10 @@ def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels)
     for name, kn in kernels.items():
         a_loads, b_loads, lead, sb, body = kn.a_loads, kn.b_loads, kn.lead, kn.sb, kn.body
         loads = a_loads + b_loads
-        count = (sb - 2) * loads + a_loads
+        # the B loads of K-step it+1 were followed by groups it+2-SB .. it-1
+        # and the A loads of group it (none when A goes direct to LDS after
+        # the barrier, with B)
+        count = (sb - 2) * loads + (0 if kn.adma else a_loads)
         ev = events(body)
         bars = [i for i, e in enumerate(ev) if e == "B"]
         # prologue, the peeled K-steps, the K-steps of the loop body, epilogue
@@ -123,7 +129,7 @@ def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels)
         pro = [e for e in ev[:bars[0]] if e in ("g", "L")]
         expect = []
         for g in range(-lead, 0):
-            expect += ["g"] * a_loads + (["L"] * b_loads if g + sb >= 0 else [])
+            expect += ["L" if kn.adma else "g"] * a_loads + (["L"] * b_loads if g + sb >= 0 else [])
         assert pro == expect, (name, pro)
         pro_waits = [e[1] for e in ev[:bars[0]] if isinstance(e, tuple)]
         # before the prologue barrier at most the loads issued after the B
@@ -132,11 +138,16 @@ def test_every_k_step_issues_its_loads_in_order_before_the_counted_wait(kernels)
         assert pro_waits and pro_waits[-1] <= (sb - 1) * loads, (name, pro_waits)
         # a K-step issues its A loads before its barrier and its B loads
         # after it, so between two barriers: B loads of the previous step,
-        # then A loads of this one
+        # then A loads of this one (A direct to LDS: A then B of the previous
+        # step, all after its barrier)
         for k in range(2 * lead):
             seg = ev[bars[k] + 1:bars[k + 1]]
             got = [e for e in seg if e in ("g", "L")]
-            assert got == (["L"] * b_loads if k else []) + ["g"] * a_loads, (name, k, got)
+            if kn.adma:
+                want = ["L"] * (a_loads + b_loads) if k else []
+            else:
+                want = (["L"] * b_loads if k else []) + ["g"] * a_loads
+            assert got == want, (name, k, got)
             # the last vmcnt wait before the barrier is the counted one (the
             # compiler adds stricter waits of its own for register data)
             waits = [e[1] for e in seg if isinstance(e, tuple)]

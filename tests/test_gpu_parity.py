@@ -289,7 +289,7 @@ def test_partial_wave_shapes_in_the_192_row_tiles(shape):
     a, b = A.cuda(), B.cuda()
     C = torch.empty((M, N), dtype=a.dtype, device="cuda")
     cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), C.data_ptr(), M, N, K, DT_CODE["bf16"])
-    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_192x256x32", cid
+    assert dg.gemm_config_info(cid)["name"].startswith("mfma16x16_192x256x32"), cid
     dg.gemm(a, b, out=C)
     torch.cuda.synchronize()
     rep = sampled_check(A, B, "bf16", C, seed=M)

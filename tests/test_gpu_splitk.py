@@ -30,8 +30,11 @@ def note(msg):
 
 
 def tile_configs():
+    """The 16x16x32 tile configurations that split K (the variants with A
+    direct to LDS run in one pass only)."""
     return [c for c in range(dg.gemm_config_count())
-            if dg.gemm_config_info(c)["name"].startswith("mfma16x16")]
+            if dg.gemm_config_info(c)["name"].startswith("mfma16x16")
+            and not dg.gemm_config_info(c)["name"].endswith("_adma")]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -69,6 +72,17 @@ def test_selected_split_shapes_sampled(shape):
     torch.cuda.synchronize()
     rep = sampled_check(A, B, "bf16", c, seed=M)
     note(f"  {rep}")
+
+
+def test_configurations_without_a_split_form_refuse_splits():
+    M, N, K = 256, 1024, 4096
+    A, B = make_operands(M, N, K, "bf16", "normal", 1350)
+    a, b = A.cuda(), B.cuda()
+    for cid in range(dg.gemm_config_count()):
+        if dg.gemm_config_info(cid)["name"].endswith("_adma"):
+            with pytest.raises(dg.GemmError) as e:
+                dg.gemm(a, b, config=cid, splits=4)
+            assert e.value.name == "GEMM_ERR_CONFIG_MISMATCH"
 
 
 def test_split_results_are_bitwise_repeatable():
