@@ -75,6 +75,9 @@ const Entry kTable[] = {
     {{29, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x32_adma", 1}, kMfma16x16},
     {{30, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_128x128x32_adma", 1}, kMfma16x16},
     {{31, 192, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_192x256x32_adma", 1}, kMfma16x16},
+    // the 8-bit kernel with A loaded direct to LDS
+    {{32, 256, 256, 64, 4, 256, 0x18, 1, 1, "fp8_256x256x64_adma", 1}, kFp8},
+    {{33, 128, 128, 64, 4, 256, 0x18, 1, 1, "fp8_128x128x64_adma", 1}, kFp8},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -205,9 +208,12 @@ int select(const Problem& p)
         }
         // 256 x 256 tiles once they cover half the CUs, else 128 x 128 (also
         // for few rows of a wide B, whose 16-byte strip rows cost one cache
-        // line per lane)
+        // line per lane).  A goes direct to LDS except for a partial single
+        // wave of 256 x 256 tiles (sustained, E4M3: 8192^3 2881 against 2793
+        // TFLOP/s, 512 x 4096 x 4096 15.6 against 17.1 us; 3072^3 34.8
+        // against 33.4 us the other way round).
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-        return t256 >= 128 ? 13 : 26;
+        return t256 >= 256 ? 32 : t256 >= 128 ? 13 : 33;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
     if (!accepts(kTable[6], p)) return 0;

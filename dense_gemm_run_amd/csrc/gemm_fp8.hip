@@ -47,6 +47,10 @@
 //    LDS traffic of a K-step are spread over its MFMAs.
 //  * Epilogue: fp32 -> bf16 (round to nearest even), staged through LDS and
 //    written as whole row segments, skipping rows >= M and columns >= N.
+//  * A direct to LDS (ADMA, K-step 64): as in the 16x16x32 kernel, A's
+//    16-byte pieces go global -> LDS at the places the register path writes
+//    them, into the stage of B's ring for the same K-step (one LDS object per
+//    stage), issued after the barrier with B's.
 //  * Split K (SPLIT): as in the 16x16x32 kernel, `splits` workgroups per
 //    tile walk disjoint ranges of K-steps and write their fp32 sums,
 //    unrounded, to their own M x N slice of a workspace; a second kernel adds
@@ -93,7 +97,7 @@ template <int BN> __device__ __forceinline__ int swz_b(int k)
     return BN == 256 ? 2 * (k & 7) : 2 * ((k >> 1) & 3);
 }
 
-template <int FMT, int BM, int BN, int BK, bool SPLIT>
+template <int FMT, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
 __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_kernel(
     const unsigned char* A, const unsigned char* B, __bf16* C,
     int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
@@ -120,11 +124,18 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile");
     static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
     static_assert((SB - 1) * B_BYTES < 65536, "LDS immediate offsets");
-    __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char sb2[SB > 2 ? B_BYTES : 1], sb3[SB > 2 ? B_BYTES : 1];
-    auto a_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sa0 : sa1); };
-    auto b_stage = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+    static_assert(!ADMA || (SB == 4 && LEAD == 4 && !SPLIT), "direct A loads: 64-deep K-steps, one pass");
+    constexpr int SA_BYTES = ADMA ? 1 : A_BYTES;
+    constexpr int SB_BYTES = ADMA ? A_BYTES + B_BYTES : B_BYTES;
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[SA_BYTES], sa1[SA_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[SB_BYTES], sb1[SB_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb2[SB > 2 ? SB_BYTES : 1], sb3[SB > 2 ? SB_BYTES : 1];
+    auto b_obj = [&](int st) __attribute__((always_inline)) { return (lds_byte*)(st == 0 ? sb0 : st == 1 ? sb1 : st == 2 ? sb2 : sb3); };
+    auto a_stage = [&](int st) __attribute__((always_inline)) {
+        if constexpr (ADMA) return b_obj(st);
+        else return (lds_byte*)(st == 0 ? sa0 : sa1);
+    };
+    auto b_stage = [&](int st) __attribute__((always_inline)) { return b_obj(st) + (ADMA ? A_BYTES : 0); };
 
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
@@ -181,6 +192,13 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
         const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
         const unsigned off = a_kp[j] < ke - k0 ? a_voff[j] : kOOB;
         stg[slot][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, k0, 0));
+    };
+    auto load_a_lds = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(kb + k0_in);
+        const unsigned off = a_kp[j] < ke - k0 ? a_voff[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (void __attribute__((address_space(3)))*)(a_stage(st) + (wave * A_LOADS + j) * 1024), 16,
+            off, k0, 0, 0);
     };
     auto store_a = [&](int st, int slot, int j) __attribute__((always_inline)) {
         lds_byte* p = a_stage(st) + (wave * A_LOADS + j) * 1024 + lane * 16;
@@ -260,9 +278,13 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     // still be in flight.
 #pragma unroll
     for (int g = -LEAD; g < 0; ++g) {
-        if (g + LEAD >= 0)
+        if (g + LEAD >= 0) {
 #pragma unroll
-            for (int j = 0; j < A_LOADS; ++j) load_a(g + LEAD, (g + LEAD) * BK, j);
+            for (int j = 0; j < A_LOADS; ++j) {
+                if constexpr (ADMA) load_a_lds(g + LEAD, (g + LEAD) * BK, j);
+                else load_a(g + LEAD, (g + LEAD) * BK, j);
+            }
+        }
         asm volatile("" ::: "memory");
         if (g + SB >= 0)
 #pragma unroll
@@ -270,8 +292,10 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
         asm volatile("" ::: "memory");
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 1) * LOADS));   // group -SB (B of K-step 0) landed
+    if constexpr (!ADMA) {
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
+        for (int j = 0; j < A_LOADS; ++j) store_a(0, 0, j);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -289,9 +313,11 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
 
     auto kslice = [&](const int q, int it, const int sl, const bool first) __attribute__((always_inline)) {
-        const int sta = q & 1, stb = q % SB, set = (q * NS + sl) & 1;
-        constexpr int NOPS1 = 2 * A_LOADS;
-        constexpr int NOPS2 = B_LOADS + NR;
+        const int sta = ADMA ? q % SB : q & 1, stb = q % SB, set = (q * NS + sl) & 1;
+        const int sta_next = ADMA ? (q + 1) % SB : sta ^ 1;
+        constexpr int NOPS1 = ADMA ? 0 : 2 * A_LOADS;
+        constexpr int LD2 = ADMA ? A_LOADS + B_LOADS : B_LOADS;   // loads after the barrier
+        constexpr int NOPS2 = LD2 + NR;
         auto mfma = [&](int xx) __attribute__((always_inline)) {
             if (first && sl == 0)
                 MfmaFp8<FMT>::first(acc[xx / FN][xx % FN], fb[set][xx % FN], fa[set][xx / FN]);
@@ -308,18 +334,20 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
                 for (int o = op_lo(xx, NR, NT); o < op_lo(xx + 1, NR, NT); ++o)
                     read_frag(set ^ 1, sta, stb, sl + 1, o);
             }
+            if constexpr (NOPS1 > 0) {
 #pragma unroll
-            for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
-                if (o < A_LOADS)
-                    store_a(sta ^ 1, (q + 1) % LEAD, o);
-                else
-                    load_a(q, (it + LEAD) * BK, o - A_LOADS);
+                for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
+                    if (o < A_LOADS)
+                        store_a(sta ^ 1, (q + 1) % LEAD, o);
+                    else
+                        load_a(q, (it + LEAD) * BK, o - A_LOADS);
+                }
             }
         }
         if (lo < BAR && BAR <= hi) {
             asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS + A_LOADS));
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes done
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm((SB - 2) * LOADS + (ADMA ? 0 : A_LOADS)));
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's A writes (and reads) done
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         }
@@ -328,10 +356,12 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
             mfma(x - lo);
 #pragma unroll
             for (int o = op_lo(x - BAR, NOPS2, XS - BAR); o < op_lo(x + 1 - BAR, NOPS2, XS - BAR); ++o) {
-                if (o < B_LOADS)
-                    load_b(stb, (it + SB) * BK, o);
+                if (ADMA && o < A_LOADS)
+                    load_a_lds(stb, (it + SB) * BK, o);
+                else if (o < LD2)
+                    load_b(stb, (it + SB) * BK, o - (ADMA ? A_LOADS : 0));
                 else
-                    read_frag(((q + 1) * NS) & 1, sta ^ 1, (q + 1) % SB, 0, o - B_LOADS);
+                    read_frag(((q + 1) * NS) & 1, sta_next, (q + 1) % SB, 0, o - LD2);
             }
         }
     };
@@ -410,6 +440,18 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
+    if (cfg.sched == 1) {   // A direct to LDS as well; one pass only
+        if (a.splits > 1) return hipErrorInvalidValue;
+        if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 64)
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 256, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
+                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
+                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
 #define DGR_FP8(BM_, BN_, BK_)                                                                            \
     else if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                          \
         if (a.splits > 1)                                                                                \

@@ -338,6 +338,10 @@ def test_8bit_tile_size_follows_the_tile_count():
         assert name(A, Bb, Cb, M, N, K, 3).startswith("fp8_128x128"), (M, N, K)
     for M, N, K in [(3072, 3072, 3072), (4096, 4096, 4096), (8192, 14336, 4096)]:
         assert name(A, Bb, Cb, M, N, K, 4).startswith("fp8_256x256"), (M, N, K)
+    # A direct to LDS except for a partial single wave of 256 x 256 tiles
+    assert name(A, Bb, Cb, 4096, 4096, 4096, 3) == "fp8_256x256x64_adma"
+    assert name(A, Bb, Cb, 3072, 3072, 3072, 3) == "fp8_256x256x64"
+    assert name(A, Bb, Cb, 2048, 2048, 2048, 3) == "fp8_128x128x64_adma"
     # the batch counts: 16 products of 1024^2 are 256 tiles of 256 x 256
     cid = dg.gemm_select_config_batched(A, Bb, Cb, 16, 1024, 1024, 1024, 1024 * 1024, 1024 * 1024,
                                         1024 * 1024, 3)
