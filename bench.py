@@ -65,9 +65,18 @@ KERNEL_FILES = {"mfma16x16": "gemm_mfma16x16.hip", "mfma32x32": "gemm_mfma32x32.
 SHARED_FILES = ["gemm_device.h", "gemm_internal.h"]
 
 
+def _code_only(src: bytes) -> bytes:
+    """Source text without comments and blank lines, so that a digest follows
+    the code, not its commentary."""
+    import re
+    text = re.sub(rb"/\*.*?\*/", b"", src, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b"", text)
+    return b"\n".join(l.rstrip() for l in text.split(b"\n") if l.strip())
+
+
 def kernel_source_digest(kernel_cfg: str) -> str:
-    """sha256 (16 hex digits) of what configuration ``kernel_cfg`` runs: its
-    kernel file, the shared headers, and its own entry of the configuration
+    """sha256 (16 hex digits) of what configuration ``kernel_cfg`` runs: the
+    code (comments aside) of its kernel file and the shared headers, and its own entry of the configuration
     table (tile, K-step, workgroup size and order, as the library reports
     them).  A name ending in _split<s> (split K) adds the reduction's source
     and the split count."""
@@ -78,7 +87,7 @@ def kernel_source_digest(kernel_cfg: str) -> str:
     csrc = os.path.join(ROOT, "dense_gemm_run_amd", "csrc")
     for f in sorted([fam] + SHARED_FILES + (["gemm_splitk.hip"] if split else [])):
         with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+            h.update(f.encode() + b"\0" + _code_only(fh.read()))
     info = next(dg.gemm_config_info(i) for i in range(dg.gemm_config_count())
                 if dg.gemm_config_info(i)["name"] == base)
     h.update(json.dumps({k: info[k] for k in sorted(info) if k != "id"}).encode())

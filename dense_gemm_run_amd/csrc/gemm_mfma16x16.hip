@@ -30,6 +30,12 @@
 //    it.  Out-of-range 16-byte pieces read zeros, as in the 32x32 kernel (the
 //    zero padding of chapter "Matrix Multiplication", section "The real
 //    tiled loop").
+//  * ADMA variant: A also goes global -> LDS directly, each lane fetching the
+//    piece the swizzled layout puts at its slot, into the ring stage of B's
+//    K-step (one LDS object per stage holds A and B); A and B of K-step
+//    it+SB are issued after K-step it's barrier.  No register staging and no
+//    A writes; it is the faster choice wherever the operands stay in the
+//    Infinity Cache.
 //  * LDS layout: A [BM][32] with 16-byte pieces XOR-swizzled by (row/2)%4
 //    (the layout that measured free of bank conflicts for this read); B
 //    [32][BN] with 16-byte pieces XOR-swizzled by an even
