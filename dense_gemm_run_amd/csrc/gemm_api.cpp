@@ -258,7 +258,7 @@ int effective_splits(int splits, int64_t K, int bk)
 }
 
 constexpr int kSplitConfig = 12;     // the 16x16x32 kernel at 128 x 128 tiles
-constexpr int kSplitConfig8 = 26;    // the 8-bit kernel at 128 x 128 x 64
+constexpr int kSplitConfig8 = 33;    // the 8-bit kernel at 128 x 128 x 64, A direct to LDS
 
 // Split count for `t128` tiles of 128 x 128 and `steps` K-steps: near 256
 // workgroups in all, at most 16 splits, at least 16 K-steps per split, and
@@ -280,7 +280,8 @@ int split_count(int64_t t128, int64_t steps, int64_t K, int bk)
 //    against 38.0 on the strip kernel; 1024^3: 14.4 with 2 against 10.7,
 //    hence the K floor.)
 //  * 8-bit inputs, up to 128 rows, K >= 2048: the 8-bit kernel at
-//    128 x 128 x 64, split likewise; up to 16 rows with K < 8192 stay on
+//    128 x 128 x 64 with A direct to LDS (1-6 % faster split than with A
+//    through registers), split likewise; up to 16 rows with K < 8192 stay on
 //    the strip kernel.  Beyond 128 rows the fp32 partial sums (4 bytes per
 //    output against 1-byte inputs) cost more than the split gains.
 //    (64 x 4096 x 14336: 17.0 us with 8 splits against 38.4 on the strip
@@ -384,7 +385,10 @@ gemm_status_t run_ws_config(gemm_handle_t h, const Problem& p, int32_t config_id
     if (!accepts(e, p)) return GEMM_ERR_CONFIG_MISMATCH;
     int s = 1;
     if (splits > 1) {
-        if ((e.kind != kMfma16x16 && e.kind != kFp8) || e.cfg.sched != 0 || p.batch != 1)
+        // split forms: every tile configuration with A through registers, and
+        // the 128 x 128 ones with A direct to LDS
+        const bool adma128 = e.cfg.sched == 1 && e.cfg.bm == 128 && e.cfg.bn == 128;
+        if ((e.kind != kMfma16x16 && e.kind != kFp8) || (e.cfg.sched != 0 && !adma128) || p.batch != 1)
             return GEMM_ERR_CONFIG_MISMATCH;
         s = effective_splits(splits, p.K, e.cfg.bk);
         if (s > 1 && (int64_t)s * p.M * p.N * 4 > ws_bytes) return GEMM_ERR_INVALID_VALUE;

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile");
     static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
     static_assert((SB - 1) * B_BYTES < 65536, "LDS immediate offsets");
-    static_assert(!ADMA || (SB == 4 && LEAD == 4 && !SPLIT), "direct A loads: 64-deep K-steps, one pass");
+    static_assert(!ADMA || (SB == 4 && LEAD == 4), "direct A loads: 64-deep K-steps");
     constexpr int SA_BYTES = ADMA ? 1 : A_BYTES;
     constexpr int SB_BYTES = ADMA ? A_BYTES + B_BYTES : B_BYTES;
     __shared__ __attribute__((aligned(1024))) unsigned char sa0[SA_BYTES], sa1[SA_BYTES];
@@ -440,8 +440,13 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
-    if (cfg.sched == 1) {   // A direct to LDS as well; one pass only
-        if (a.splits > 1) return hipErrorInvalidValue;
+    if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 only
+        if (a.splits > 1) {
+            if (cfg.bm != 128 || cfg.bn != 128 || cfg.bk != 64) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, true, true>), dim3(tiles * a.splits), block, 0,
+                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            return hipGetLastError();
+        }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 256, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
                                a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // for the loads still landing in the others.
     // ADMA: A also goes global -> LDS directly, into the same ring as B; each
     // ring stage is one LDS object holding A (first) and B of one K-step.
-    static_assert(!ADMA || (SB == 4 && LEAD == 4 && !SPLIT), "direct A loads: 32-deep K-steps, one pass");
+    static_assert(!ADMA || (SB == 4 && LEAD == 4), "direct A loads: 32-deep K-steps");
     constexpr int SA_BYTES = ADMA ? 1 : A_BYTES;
     constexpr int SB_BYTES = ADMA ? A_BYTES + B_BYTES : B_BYTES;
     __shared__ __attribute__((aligned(1024))) unsigned char sa0[SA_BYTES], sa1[SA_BYTES];
@@ -519,8 +519,13 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
-    if (cfg.sched == 1) {   // A direct to LDS as well; one pass only
-        if (a.splits > 1) return hipErrorInvalidValue;
+    if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 only
+        if (a.splits > 1) {
+            if (cfg.bm != 128 || cfg.bn != 128 || cfg.bk != 32) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, true, true>), dim3(tiles * a.splits), block,
+                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            return hipGetLastError();
+        }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 256, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
                                C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);

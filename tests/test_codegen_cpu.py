@@ -27,12 +27,13 @@ FAMILIES = {
     "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E",
                   # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32 + 192x256x32)
                   # x {one pass, split K}, + {256x256x32, 128x128x32, 192x256x32} with A
-                  # direct to LDS
-                  30, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
+                  # direct to LDS, + 128x128x32 split with A direct to LDS
+                  32, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
     "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E",
             # {e4m3, e5m2} x ({256x256, 128x128} x {64, 128} x {one pass, split K}
-            #                 + {256x256, 128x128} x 64 with A direct to LDS)
-            20, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
+            #                 + {256x256, 128x128} x 64 with A direct to LDS
+            #                 + 128x128x64 split with A direct to LDS)
+            22, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
 }
 
 

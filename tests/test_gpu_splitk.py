@@ -29,12 +29,17 @@ def note(msg):
     sys.stdout.flush()
 
 
+def splits_k(name):
+    """Whether a tile configuration has a split form: all with A through
+    registers, and the 128 x 128 ones with A direct to LDS."""
+    return not name.endswith("_adma") or "_128x128x" in name
+
+
 def tile_configs():
-    """The 16x16x32 tile configurations that split K (the variants with A
-    direct to LDS run in one pass only)."""
+    """The 16x16x32 tile configurations that split K."""
     return [c for c in range(dg.gemm_config_count())
             if dg.gemm_config_info(c)["name"].startswith("mfma16x16")
-            and not dg.gemm_config_info(c)["name"].endswith("_adma")]
+            and splits_k(dg.gemm_config_info(c)["name"])]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -79,7 +84,8 @@ def test_configurations_without_a_split_form_refuse_splits():
     A, B = make_operands(M, N, K, "bf16", "normal", 1350)
     a, b = A.cuda(), B.cuda()
     for cid in range(dg.gemm_config_count()):
-        if dg.gemm_config_info(cid)["name"].endswith("_adma"):
+        name = dg.gemm_config_info(cid)["name"]
+        if name.startswith("mfma16x16") and not splits_k(name):
             with pytest.raises(dg.GemmError) as e:
                 dg.gemm(a, b, config=cid, splits=4)
             assert e.value.name == "GEMM_ERR_CONFIG_MISMATCH"
@@ -154,7 +160,7 @@ def test_8bit_tile_configurations_at_every_split_count(dtype, shape):
     a, b = A.cuda(), B.cuda()
     for cid in range(dg.gemm_config_count()):
         info = dg.gemm_config_info(cid)
-        if (not info["name"].startswith("fp8_") or info["name"].endswith("_adma")
+        if (not info["name"].startswith("fp8_") or not splits_k(info["name"])
                 or not accepts(cid, a, b, M, N, K)):
             continue
         for s in (2, 3, 7, 16):
