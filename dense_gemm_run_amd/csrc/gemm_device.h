@@ -102,7 +102,8 @@ __device__ __forceinline__ void store_c_block_32x32(const f32x16 (&acc)[WM / 32]
             u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
             if ((r / PR) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
             const int row = row0 + pass * RP + r;
-            if (row < M && col < N) *(u32x4*)(C + (size_t)row * N + col) = v;
+            // non-temporal: C is not read again (see the 16x16 epilogue)
+            if (row < M && col < N) __builtin_nontemporal_store(v, (u32x4*)(C + (size_t)row * N + col));
         }
     }
 }

@@ -148,7 +148,10 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
             const int p = q ^ ((r / W) & (PR - 1));
             const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
             const int row = row0 + pass * RP + r;
-            if (row < M && col < N) *(u32x4*)(C + (size_t)row * N + col) = v;
+            // non-temporal: C is not read again, and streaming it past the
+            // caches leaves them to the A and B tiles other workgroups still
+            // need (bf16 8192^3: 760 against 787 us)
+            if (row < M && col < N) __builtin_nontemporal_store(v, (u32x4*)(C + (size_t)row * N + col));
         }
     }
 }

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* ws, T* 
         u32x2 o;
         o[0] = pack2<T>(acc[0], acc[1]);
         o[1] = pack2<T>(acc[2], acc[3]);
-        *(u32x2*)(C + i) = o;
+        __builtin_nontemporal_store(o, (u32x2*)(C + i));   // C is not read again
     }
 }
 
