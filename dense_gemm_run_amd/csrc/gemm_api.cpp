@@ -78,6 +78,9 @@ const Entry kTable[] = {
     // the 8-bit kernel with A loaded direct to LDS
     {{32, 256, 256, 64, 4, 256, 0x18, 1, 1, "fp8_256x256x64_adma", 1}, kFp8},
     {{33, 128, 128, 64, 4, 256, 0x18, 1, 1, "fp8_128x128x64_adma", 1}, kFp8},
+    // matrix-vector with the wavefronts of a workgroup splitting K (bm = R)
+    {{34, 4, 4, 512, 1, 256, 0x6, 1, 0, "gemv_kslice_4rows", 1}, kGemv},
+    {{35, 8, 4, 512, 1, 256, 0x6, 1, 0, "gemv_kslice_8rows", 1}, kGemv},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -215,7 +218,17 @@ int select(const Problem& p)
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
         return t256 >= 256 ? 32 : t256 >= 128 ? 13 : 33;
     }
-    if (p.N <= 4 && accepts(kTable[10], p)) return p.M * p.batch >= 16 * 256 * 4 ? 11 : 10;
+    if (p.N <= 4 && accepts(kTable[10], p)) {
+        // Timed on bf16 shapes with M 2K-28K, K 2K-14K, N 1-4.  A K-slice
+        // wavefront step covers 2048 (U = 4) or 1024 (U = 2) K positions, so
+        // below K = 4096 some of the four wavefronts would idle: there the
+        // rows are split instead.  From K = 4096 the K-slice kernels lead:
+        // 4 rows per workgroup, or 8 with 3-4 columns (more outputs per
+        // wavefront against fewer loads of B) once A is tall or K short.
+        if (p.K < 4096) return 10;
+        if (p.N >= 3 && (p.M * p.batch >= 8192 || p.K <= 4096)) return 35;
+        return 34;
+    }
     if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
     if (p.M <= 128) {
