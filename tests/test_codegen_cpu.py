@@ -202,3 +202,47 @@ def test_strip_kernel_uses_no_scratch_and_unscaled_8bit_mfma(tmp_path):
     assert len(sizes) >= 8 and all(x == 0 for x in sizes), sizes
     assert "v_mfma_f32_16x16x128_f8f6f4" in text
     assert "v_mfma_scale" not in text
+
+
+def test_matrix_vector_kernel_structure(tmp_path):
+    """The matrix-vector kernel (every element type, column count, rows per
+    wavefront and schedule): each K step issues all of its U*(R+N) 16-byte
+    loads (U chunks of R rows of A and N pieces of B) before its first wait
+    for them, its products are exactly U*R*4*N two-element dot products on
+    whole 32-bit words of A (no single-word loads of a piece), the
+    cross-lane reduction selects with masks rather than with a lane-dependent
+    array index (no chain of compares), and nothing spills."""
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    out = tmp_path / "gemv.s"
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_gemv.hip"),
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = out.read_text().split("\n")
+    pat = r"^(_Z\S*gemv_kernelI(DF16_|DF16b)Li(\d)ELi(\d+)ELi(\d+)ELb(\d)E\S*):"
+    seen = []
+    for i, l in enumerate(lines):
+        m = re.match(pat, l)
+        if not m:
+            continue
+        nv, rows, u = int(m.group(3)), int(m.group(4)), int(m.group(5))
+        end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+        body = [x.strip() for x in lines[i:end]]
+        name = m.group(1)
+        seen.append((m.group(2), nv, rows, u, m.group(6)))
+        insts = [x for x in body if x and not x.startswith((";", ".")) and not x.endswith(":")]
+        ops = [x.split()[0] for x in insts]
+        first_load = ops.index("buffer_load_dwordx4")
+        first_wait = next(k for k in range(first_load, len(ops))
+                          if ops[k] == "s_waitcnt" and "vmcnt" in insts[k])
+        loads_before = ops[:first_wait].count("buffer_load_dwordx4")
+        assert loads_before >= u * (rows + nv), (name, loads_before, u * (rows + nv))
+        assert "buffer_load_dword" not in ops, name
+        dots = sum(op.startswith("v_dot2") for op in ops)
+        assert dots == u * rows * 4 * nv, (name, dots)
+        assert sum(op.startswith("v_cmp_eq_u32") for op in ops) < 16, name
+    assert len(seen) == 2 * 4 * 4, seen
+    sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", "\n".join(lines))]
+    assert len(sizes) == 32 and all(x == 0 for x in sizes), sizes
