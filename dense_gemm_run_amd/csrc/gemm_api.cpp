@@ -209,6 +209,10 @@ int select(const Problem& p)
             if (p.M <= 16) return p.K >= 8192 ? 22 : 24;
             return 25;
         }
+        // at most 4 K-steps of 64: 128 x 128 tiles with A through registers,
+        // for the same reason as the 16-bit short-K rule below (E4M3,
+        // 64 x 2048^2, 8192^2, 8 x 4096^2: 12-22 % faster at K = 64-256)
+        if (p.K <= 256) return 26;
         // 256 x 256 tiles once they cover half the CUs, else 128 x 128 (also
         // for few rows of a wide B, whose 16-byte strip rows cost one cache
         // line per lane).  A goes direct to LDS except for a partial single
@@ -240,6 +244,12 @@ int select(const Problem& p)
         if (p.M <= 32) return wide ? 19 : 16;
         if (!wide) return p.M <= 64 ? 19 : 20;
     }
+    // At most 8 K-steps of 32: a workgroup is mostly its prologue and its C
+    // stores, and the 128 x 128 tile with A through registers (several
+    // workgroups per CU) overlaps one's stores with another's loads (bf16,
+    // 64 x 2048^2 and 8192^2 and 8 x 4096^2: 9-17 % faster than 256 x 256 at
+    // K = 64-128, 0-6 % at 256, slower from 512)
+    if (p.K <= 256) return 12;
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
     if (t256 < 128) return 30;
     // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4

@@ -413,3 +413,25 @@ def test_workspace_argument_errors():
     assert cfg(12, 4, W, need - 1) == INVALID           # workspace too small for 4 splits
     assert cfg(12, 4, W, need) == INVALID               # valid, but no handle
     assert cfg(99, 2, W, need) == INVALID
+
+
+def test_short_k_selects_128x128_tiles_with_a_through_registers():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
+    # at most 8 K-steps of 32 (16-bit) or 4 of 64 (8-bit)
+    for M, N, K in [(8192, 8192, 64), (8192, 8192, 256), (4096, 4096, 128), (2048, 2048, 208)]:
+        for dt in (1, 2):
+            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_128x128x32", (M, N, K, dt)
+        for dt in (3, 4):
+            assert name(A, Bb, Cb, M, N, K, dt) == "fp8_128x128x64", (M, N, K, dt)
+    cid = dg.gemm_select_config_batched(A, Bb, Cb, 64, 2048, 2048, 128, 2048 * 128, 128 * 2048,
+                                        2048 * 2048, 2)
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32"
+    # from K = 264 on, the tile-count rules again
+    assert name(A, Bb, Cb, 8192, 8192, 264, 2) == "mfma16x16_256x256x32_adma"
+    assert name(A, Bb, Cb, 8192, 8192, 512, 3) == "fp8_256x256x64_adma"
+    # few rows keep the strip kernels, few columns the vector kernel
+    assert name(A, Bb, Cb, 16, 4096, 128, 2).startswith("skinny")
+    assert name(A, Bb, Cb, 16, 4096, 128, 3).startswith("skinny8")
+    assert name(A, Bb, Cb, 4096, 1, 128, 2).startswith("gemv")
