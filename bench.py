@@ -151,6 +151,10 @@ SWEEP_SQUARE = [512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192]
 SWEEP_SKINNY = [(m, 4096, 4096) for m in (1, 4, 8, 16, 32, 64, 128, 256, 512)] + \
                [(m, 14336, 4096) for m in (16, 64, 256)] + [(16, 4096, 14336), (64, 4096, 14336)]
 SWEEP_PREFILL = [(8192, 12288, 4096), (8192, 4096, 4096), (8192, 14336, 4096), (8192, 4096, 14336)]
+SWEEP_SHORT_K = [(2048, 2048, 64), (8192, 8192, 128), (4096, 4096, 256)]
+# few columns (decode GEMV); 16-bit inputs only: the 8-bit path has no such kernel,
+# and the vendor's 8-bit call takes only multiples of 16
+SWEEP_FEW_COLUMNS = [(14336, 1, 4096), (4096, 1, 14336), (4096, 2, 4096), (12288, 4, 4096)]
 
 
 def _time_us(fn, iters, stream) -> float:
@@ -184,7 +188,9 @@ def sweep(dtype: str, iters: int, vendor: bool = False) -> int:
     torch.cuda.set_device(dev)
     h = dg.gemm_create()
     eight_bit = dtype.startswith("fp8")
-    shapes = [(n, n, n) for n in SWEEP_SQUARE] + SWEEP_SKINNY + SWEEP_PREFILL
+    shapes = [(n, n, n) for n in SWEEP_SQUARE] + SWEEP_SKINNY + SWEEP_PREFILL + SWEEP_SHORT_K
+    if not eight_bit:
+        shapes += SWEEP_FEW_COLUMNS
     stream = torch.cuda.current_stream(dev)
     for M, N, K in shapes:
         A, B = make_operands(M, N, K, dtype, "normal" if eight_bit else "normal_sqrtk", 100)
