@@ -95,3 +95,27 @@ def test_gemv_workloads_whole(name):
     dg.gemm(a, b, out=C)
     torch.cuda.synchronize()
     note(f"  {check(A, B, w.dtype, C)}")
+
+
+@pytest.mark.parametrize("shape", [(3, 300, 4, 4104), (3, 3000, 3, 4096), (2, 777, 1, 8200)])
+def test_gemv_batched_at_long_k_every_configuration(shape):
+    """Batches whose K reaches the K-split schedules (wavefronts splitting K,
+    partial sums added in LDS): the selected configuration and every other
+    vector configuration, each matrix of the batch against the oracle; K not
+    a multiple of the 512-element chunk, M not a multiple of the rows per
+    workgroup."""
+    batch, M, N, K = shape
+    A, B = make_batched_operands(batch, M, N, K, "bf16", "decode", 60 + M)
+    a, b = A.cuda(), B.cuda()
+    sel = dg.gemm_select_config_batched(a.data_ptr(), b.data_ptr(), a.data_ptr() + (1 << 40), batch, M,
+                                        N, K, M * K, K * N, M * N, DT_CODE["bf16"])
+    assert sel in GEMV_CONFIGS and dg.gemm_config_info(sel)["name"].startswith("gemv_kslice"), sel
+    ref, _ = gemm64.reference_batched(A, B, "bf16")
+    for cid in GEMV_CONFIGS + [None]:
+        note(f"[gemv] batched config {cid} {shape}")
+        c = dg.gemm_batched(a, b, config=cid)
+        torch.cuda.synchronize()
+        got = c.to("cpu", torch.float64).numpy()
+        for i in range(batch):
+            rep = tolerance.compare(got[i], ref[i], "bf16", K, float(A.abs().max()), float(B.abs().max()))
+            assert rep["ok"], (cid, i, rep)
