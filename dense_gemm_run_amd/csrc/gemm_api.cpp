@@ -81,6 +81,9 @@ const Entry kTable[] = {
     // matrix-vector with the wavefronts of a workgroup splitting K (bm = R)
     {{34, 4, 4, 512, 1, 256, 0x6, 1, 0, "gemv_kslice_4rows", 1}, kGemv},
     {{35, 8, 4, 512, 1, 256, 0x6, 1, 0, "gemv_kslice_8rows", 1}, kGemv},
+    // the 16x16 kernel at 64 x 128: few rows with split K
+    {{36, 64, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_64x128x32"}, kMfma16x16},
+    {{37, 64, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_64x128x32_adma", 1}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -281,6 +284,7 @@ int effective_splits(int splits, int64_t K, int bk)
 }
 
 constexpr int kSplitConfig = 12;     // the 16x16x32 kernel at 128 x 128 tiles
+constexpr int kSplitConfigFew = 37;  // the 16x16x32 kernel at 64 x 128, A direct to LDS
 constexpr int kSplitConfig8 = 33;    // the 8-bit kernel at 128 x 128 x 64, A direct to LDS
 
 // Split count for `t128` tiles of 128 x 128 and `steps` K-steps: near 256
@@ -296,12 +300,18 @@ int split_count(int64_t t128, int64_t steps, int64_t K, int bk)
 
 // The choice of gemm_run_ws: a configuration and a split count (1: none).
 // Products of one matrix only; the numbers are from the shape sweep.
-//  * fp16/bf16 with K >= 2048 (64 K-steps) and at most 160 tiles of
-//    128 x 128: the 16x16x32 kernel at 128 x 128 with split_count splits;
-//    up to 8 rows stay on the strip kernel.  (256 x 4096 x 4096: 19.6 us
-//    with 4 splits against 31.9 in one pass; 16 x 4096 x 14336: 22.6 with 8
-//    against 38.0 on the strip kernel; 1024^3: 14.4 with 2 against 10.7,
-//    hence the K floor.)
+//  * fp16/bf16 with K >= 2048 (64 K-steps) and at most 160 tiles: the
+//    16x16x32 kernel with split_count splits, on 64 x 128 tiles with A
+//    direct to LDS up to 256 rows (a quarter of the MFMAs of a 128-row tile
+//    on rows past M, and room for more workgroups per CU), else on 128 x 128
+//    tiles.  (256 x 4096 x 4096: 19.6
+//    us with 4 splits against 31.9 in one pass; 16 x 4096 x 14336: 22.6
+//    with 8 against 38.0 on the strip kernel; 1024^3: 14.4 with 2 against
+//    10.7, hence the K floor.  64 x 128 against 128 x 128 tiles, 16-256 rows
+//    x 1024-14336 x 2048-14336: 2-15 % faster, e.g. 16 x 4096 x 4096 7.9
+//    against 8.9 us, 128 x 4096 x 4096 14.0 against 15.5.  Against the strip
+//    kernel for 1-8 rows: 7.0-7.3 against 8.9-11.0 us at 4096 x 4096, 20.2
+//    against 34.3 at 8 x 4096 x 14336.)
 //  * 8-bit inputs, up to 128 rows, K >= 2048: the 8-bit kernel at
 //    128 x 128 x 64 with A direct to LDS (1-6 % faster split than with A
 //    through registers), split likewise; up to 16 rows with K < 8192 stay on
@@ -318,11 +328,12 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
     int cfg = -1, s = 1;
     if (p.dtype == kF16 || p.dtype == kBF16) {
         if (!accepts(kTable[kSplitConfig], p) || kTable[c].kind == kGemv) return c;
-        if (kTable[c].kind == kSkinny && p.M <= 8) return c;
         const int64_t steps = (p.K + 31) / 32;
-        if (steps < 64 || t128 > 160) return c;
-        cfg = kSplitConfig;
-        s = split_count(t128, steps, p.K, 32);
+        const bool few = p.M <= 256;
+        const int64_t t = few ? ((p.M + 63) / 64) * ((p.N + 127) / 128) : t128;
+        if (steps < 64 || t > 160) return c;
+        cfg = few ? kSplitConfigFew : kSplitConfig;
+        s = split_count(t, steps, p.K, 32);
     } else if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[kSplitConfig8], p) || p.M > 128) return c;
         if (kTable[c].kind == kSkinny && p.M <= 16 && p.K < 8192) return c;
@@ -410,7 +421,7 @@ gemm_status_t run_ws_config(gemm_handle_t h, const Problem& p, int32_t config_id
     if (splits > 1) {
         // split forms: every tile configuration with A through registers, and
         // the 128 x 128 ones with A direct to LDS
-        const bool adma128 = e.cfg.sched == 1 && e.cfg.bm == 128 && e.cfg.bn == 128;
+        const bool adma128 = e.cfg.sched == 1 && e.cfg.bm <= 128 && e.cfg.bn == 128;
         if ((e.kind != kMfma16x16 && e.kind != kFp8) || (e.cfg.sched != 0 && !adma128) || p.batch != 1)
             return GEMM_ERR_CONFIG_MISMATCH;
         s = effective_splits(splits, p.K, e.cfg.bk);

@@ -8,8 +8,8 @@
 // with these differences:
 //
 //  * Math: 4 wavefronts in a 2 x 2 grid, each owning (BM/2) x (BN/2) outputs
-//    as 16x16 MFMA tiles (BM x BN = 256 x 256, 192 x 256, 256 x 128 or
-//    128 x 128).  Per unit of work the 16x16x32 instruction moves
+//    as 16x16 MFMA tiles (BM x BN = 256 x 256, 192 x 256, 256 x 128,
+//    128 x 128 or 64 x 128).  Per unit of work the 16x16x32 instruction moves
 //    half the accumulator data of the 32x32x16 one; under MI355X's power
 //    limit this runs at a higher clock for the same issue rate.
 //  * The MFMAs are written as inline assembly with the accumulator operand
@@ -524,9 +524,14 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     if (cfg.threads != 256) return hipErrorInvalidValue;
     if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 only
         if (a.splits > 1) {
-            if (cfg.bm != 128 || cfg.bn != 128 || cfg.bk != 32) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, true, true>), dim3(tiles * a.splits), block,
-                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)
+                hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, true, true>), dim3(tiles * a.splits),
+                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 32)
+                hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 64, 128, 32, true, true>), dim3(tiles * a.splits),
+                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            else
+                return hipErrorInvalidValue;
             return hipGetLastError();
         }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 32)
@@ -537,6 +542,9 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
                                C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
         else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 192, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
+                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 32)
+            hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 64, 128, 32, false, true>), grid, block, 0, a.stream, A, B,
                                C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
         else
             return hipErrorInvalidValue;
@@ -558,6 +566,7 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     DGR_LAUNCH(256, 128, 64)
     DGR_LAUNCH(128, 128, 32)
     DGR_LAUNCH(192, 256, 32)
+    DGR_LAUNCH(64, 128, 32)
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;
 }

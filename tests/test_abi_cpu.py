@@ -351,21 +351,25 @@ def test_8bit_tile_size_follows_the_tile_count():
 # ---------------------------------------------------------------- split K with a workspace
 def test_workspace_sizes_follow_the_split_rule():
     L = _lib.lib()
-    # 256 x 4096: 64 tiles of 128 x 128 -> 4 splits of 32 K-steps
-    assert L.gemm_workspace_size(256, 4096, 4096, 2) == 4 * 256 * 4096 * 4
-    # 64 x 14336: 112 tiles -> 2 splits
+    # up to 256 rows the tiles are 64 x 128: 256 x 4096 is 128 of them -> 2 splits
+    assert L.gemm_workspace_size(256, 4096, 4096, 2) == 2 * 256 * 4096 * 4
+    # 128 x 4096: 64 tiles -> 4 splits; 64 x 14336: 112 tiles -> 2 splits
+    assert L.gemm_workspace_size(128, 4096, 4096, 2) == 4 * 128 * 4096 * 4
     assert L.gemm_workspace_size(64, 14336, 4096, 1) == 2 * 64 * 14336 * 4
-    # 16 rows: 32 tiles -> 8 splits; 512 x 4096: 128 tiles -> 2
+    # 16 rows: 32 tiles -> 8 splits; beyond 256 rows 128 x 128 tiles: 512 x 4096 is 128 -> 2
     assert L.gemm_workspace_size(16, 4096, 4096, 2) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(512, 4096, 4096, 2) == 2 * 512 * 4096 * 4
     # 8-bit inputs up to 128 rows: 32 tiles, 64 K-steps of 64 -> 4 splits; K = 14336 -> 8
     assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
     assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(16, 14336, 4096, 3) == 2 * 16 * 14336 * 4
-    # enough tiles, up to 8 rows (the strip kernel), GEMV, fp32, K < 2048, K = 0, and 8-bit
-    # inputs beyond 128 rows or up to 16 rows with K < 8192: no split
-    for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2), (8, 4096, 4096, 2),
-                 (1, 4096, 4096, 1), (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
+    # 1 to 8 rows split too (8 splits of the 32 tiles of 64 x 128)
+    assert L.gemm_workspace_size(8, 4096, 4096, 2) == 8 * 8 * 4096 * 4
+    assert L.gemm_workspace_size(1, 4096, 4096, 1) == 8 * 1 * 4096 * 4
+    # enough tiles, GEMV, fp32, K < 2048, K = 0, and 8-bit inputs beyond 128 rows or up to
+    # 16 rows with K < 8192: no split
+    for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2),
+                 (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
                  (16, 4096, 4096, 3), (129, 4096, 4096, 3), (64, 4096, 1024, 4),
                  (1024, 1024, 1024, 2), (256, 4096, 2016, 2), (256, 4096, 0, 2), (0, 4096, 4096, 2),
                  (256, 4096, 4092, 2)]:
@@ -382,7 +386,11 @@ def test_workspace_sizes_follow_the_split_rule():
 def test_select_config_ws_falls_back_when_the_workspace_is_short():
     need = dg.gemm_workspace_size(256, 4096, 4096, 2)
     cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need)
-    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32" and s == 4
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_64x128x32_adma" and s == 2
+    # beyond 256 rows: 128 x 128 tiles
+    need512 = dg.gemm_workspace_size(512, 4096, 4096, 2)
+    cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 512, 4096, 4096, 2, need512)
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32" and s == 2
     cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need - 1)
     assert s == 1 and cid == dg.gemm_select_config(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2)
     # misaligned A: the generic kernel, no split

@@ -25,10 +25,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # MFMA mnemonic, K depth of one MFMA, outputs of one MFMA
 FAMILIES = {
     "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_kernel\S*?Li(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E",
-                  # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32 + 192x256x32)
-                  # x {one pass, split K}, + {256x256x32, 128x128x32, 192x256x32} with A
-                  # direct to LDS, + 128x128x32 split with A direct to LDS
-                  32, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
+                  # {f16, bf16} x ({256x256, 256x128} x {32, 64} + 128x128x32 + 192x256x32
+                  # + 64x128x32) x {one pass, split K}, + {256x256x32, 128x128x32,
+                  # 192x256x32, 64x128x32} with A direct to LDS, + {128x128x32, 64x128x32}
+                  # split with A direct to LDS
+                  40, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
     "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E",
             # {e4m3, e5m2} x ({256x256, 128x128} x {64, 128} x {one pass, split K}
             #                 + {256x256, 128x128} x 64 with A direct to LDS
