@@ -84,6 +84,8 @@ const Entry kTable[] = {
     // the 16x16 kernel at 64 x 128: few rows with split K
     {{36, 64, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_64x128x32"}, kMfma16x16},
     {{37, 64, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_64x128x32_adma", 1}, kMfma16x16},
+    // the 8-bit kernel at 64 x 128 x 64, A direct to LDS: few rows with split K
+    {{38, 64, 128, 64, 4, 256, 0x18, 1, 1, "fp8_64x128x64_adma", 1}, kFp8},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -285,16 +287,16 @@ int effective_splits(int splits, int64_t K, int bk)
 
 constexpr int kSplitConfig = 12;     // the 16x16x32 kernel at 128 x 128 tiles
 constexpr int kSplitConfigFew = 37;  // the 16x16x32 kernel at 64 x 128, A direct to LDS
-constexpr int kSplitConfig8 = 33;    // the 8-bit kernel at 128 x 128 x 64, A direct to LDS
+constexpr int kSplitConfig8 = 38;    // the 8-bit kernel at 64 x 128 x 64, A direct to LDS
 
-// Split count for `t128` tiles of 128 x 128 and `steps` K-steps: near 256
-// workgroups in all, at most 16 splits, at least 16 K-steps per split, and
-// none without K-steps.
-int split_count(int64_t t128, int64_t steps, int64_t K, int bk)
+// Split count for `tiles` tiles and `steps` K-steps: near 256 workgroups in
+// all, at most 16 splits, at least `min_steps` K-steps per split, and none
+// without K-steps.
+int split_count(int64_t tiles, int64_t steps, int64_t K, int bk, int min_steps = 16)
 {
-    int s = (int)((256 + t128 / 2) / t128);
+    int s = (int)((256 + tiles / 2) / tiles);
     if (s > 16) s = 16;
-    while (s > 1 && steps < 16 * (int64_t)s) --s;
+    while (s > 1 && steps < min_steps * (int64_t)s) --s;
     return effective_splits(s, K, bk);
 }
 
@@ -313,11 +315,13 @@ int split_count(int64_t t128, int64_t steps, int64_t K, int bk)
 //    kernel for 1-8 rows: 7.0-7.3 against 8.9-11.0 us at 4096 x 4096, 20.2
 //    against 34.3 at 8 x 4096 x 14336.)
 //  * 8-bit inputs, up to 128 rows, K >= 2048: the 8-bit kernel at
-//    128 x 128 x 64 with A direct to LDS (1-6 % faster split than with A
-//    through registers), split likewise; up to 16 rows with K < 8192 stay on
-//    the strip kernel.  Beyond 128 rows the fp32 partial sums (4 bytes per
-//    output against 1-byte inputs) cost more than the split gains.
-//    (64 x 4096 x 14336: 17.0 us with 8 splits against 38.4 on the strip
+//    64 x 128 x 64 with A direct to LDS, split likewise, with at least 16
+//    K-steps of 64 per split up to 64 rows and 32 above (the fp32 partial
+//    sums, 4 bytes per output against 1-byte inputs, weigh more with more
+//    rows).  Beyond 128 rows they cost more than the split gains.  (E4M3,
+//    against the 128 x 128 split: 16-128 rows x 4096 x 4096 6.6-9.7 us
+//    against 7.6-13.4, 1-5 % faster with N or K = 14336; 64 x 4096 x 14336:
+//    17.0 us with 8 splits on 128 x 128 tiles against 38.4 on the strip
 //    kernel; 256 x 4096 x 4096: 16.5 in one pass, 17.6 with 2 splits.)
 int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
 {
@@ -336,11 +340,10 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
         s = split_count(t, steps, p.K, 32);
     } else if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[kSplitConfig8], p) || p.M > 128) return c;
-        if (kTable[c].kind == kSkinny && p.M <= 16 && p.K < 8192) return c;
         const int64_t steps = (p.K + 63) / 64;
         if (steps < 32) return c;
         cfg = kSplitConfig8;
-        s = split_count(t128, steps, p.K, 64);
+        s = split_count(((p.M + 63) / 64) * ((p.N + 127) / 128), steps, p.K, 64, p.M > 64 ? 32 : 16);
     } else {
         return c;
     }

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     constexpr int NR = FM + FN;                  // operand fragments per K-slice
     constexpr int BAR = XS - NT / 2;             // MFMAs of a K-step before its barrier
     static_assert(BK == 64 || BK == 128, "K-step");
-    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128), "tile");
+    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 128 && ADMA), "tile");
     static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
     static_assert((SB - 1) * B_BYTES < 65536, "LDS immediate offsets");
     static_assert(!ADMA || (SB == 4 && LEAD == 4), "direct A loads: 64-deep K-steps");
@@ -440,11 +440,16 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
-    if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 only
+    if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 and 64 x 128 only
         if (a.splits > 1) {
-            if (cfg.bm != 128 || cfg.bn != 128 || cfg.bk != 64) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, true, true>), dim3(tiles * a.splits), block, 0,
-                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
+                hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, true, true>), dim3(tiles * a.splits), block,
+                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
+                hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, true, true>), dim3(tiles * a.splits), block,
+                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+            else
+                return hipErrorInvalidValue;
             return hipGetLastError();
         }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 64)
@@ -452,6 +457,9 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
                                a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
         else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
+                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
                                a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
         else
             return hipErrorInvalidValue;

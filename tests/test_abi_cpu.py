@@ -363,14 +363,17 @@ def test_workspace_sizes_follow_the_split_rule():
     assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
     assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(16, 14336, 4096, 3) == 2 * 16 * 14336 * 4
+    # 8-bit tiles are 64 x 128: 16 rows of 4096 columns are 32 tiles -> 4 splits (64 K-steps);
+    # beyond 64 rows each split keeps at least 32 K-steps: 128 x 4096 x 4096 -> 2
+    assert L.gemm_workspace_size(16, 4096, 4096, 3) == 4 * 16 * 4096 * 4
+    assert L.gemm_workspace_size(128, 4096, 4096, 3) == 2 * 128 * 4096 * 4
     # 1 to 8 rows split too (8 splits of the 32 tiles of 64 x 128)
     assert L.gemm_workspace_size(8, 4096, 4096, 2) == 8 * 8 * 4096 * 4
     assert L.gemm_workspace_size(1, 4096, 4096, 1) == 8 * 1 * 4096 * 4
-    # enough tiles, GEMV, fp32, K < 2048, K = 0, and 8-bit inputs beyond 128 rows or up to
-    # 16 rows with K < 8192: no split
+    # enough tiles, GEMV, fp32, K < 2048, K = 0, and 8-bit inputs beyond 128 rows: no split
     for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2),
                  (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
-                 (16, 4096, 4096, 3), (129, 4096, 4096, 3), (64, 4096, 1024, 4),
+                 (129, 4096, 4096, 3), (64, 4096, 1024, 4),
                  (1024, 1024, 1024, 2), (256, 4096, 2016, 2), (256, 4096, 0, 2), (0, 4096, 4096, 2),
                  (256, 4096, 4092, 2)]:
         assert L.gemm_workspace_size(*args) == 0, args

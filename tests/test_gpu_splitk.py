@@ -180,7 +180,7 @@ def test_selected_8bit_split_shapes_sampled(shape):
     need = dg.gemm_workspace_size(M, N, K, 3)
     cid, s = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, 3, need)
     note(f"[splitk] selected {dg.gemm_config_info(cid)['name']} x {s} for 8-bit {shape}")
-    assert s > 1 and dg.gemm_config_info(cid)["name"].startswith("fp8_128x128")
+    assert s > 1 and dg.gemm_config_info(cid)["name"].startswith("fp8_64x128")
     dg.gemm(a, b, out=c)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M)
