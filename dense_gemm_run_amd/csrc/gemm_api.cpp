@@ -255,6 +255,13 @@ int select(const Problem& p)
     // 64 x 2048^2 and 8192^2 and 8 x 4096^2: 9-17 % faster than 256 x 256 at
     // K = 64-128, 0-6 % at 256, slower from 512)
     if (p.K <= 256) return 12;
+    if (p.M <= 128) {
+        // 33-128 rows of a wide B: 64 x 128 tiles with A direct to LDS while
+        // they fit one wave of workgroups (bf16, 40-128 rows x 8192-14336: 9-28
+        // % faster than 128 x 128 tiles; 128 x 28672, 448 tiles: 23 % slower)
+        const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
+        if (t64 <= 256) return 37;
+    }
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
     if (t256 < 128) return 30;
     // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4

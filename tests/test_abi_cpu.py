@@ -446,3 +446,15 @@ def test_short_k_selects_128x128_tiles_with_a_through_registers():
     assert name(A, Bb, Cb, 16, 4096, 128, 2).startswith("skinny")
     assert name(A, Bb, Cb, 16, 4096, 128, 3).startswith("skinny8")
     assert name(A, Bb, Cb, 4096, 1, 128, 2).startswith("gemv")
+
+
+def test_wide_few_rows_select_64x128_tiles_while_they_fit_one_wave():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
+    for M, N, K in [(40, 14336, 4096), (128, 14336, 4096), (64, 8192, 4096), (128, 8192, 8192)]:
+        for dt in (1, 2):
+            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_64x128x32_adma", (M, N, K, dt)
+    # 448 tiles of 64 x 128: back to 128 x 128; up to 32 rows the strip kernels keep wide B
+    assert name(A, Bb, Cb, 128, 28672, 4096, 2) == "mfma16x16_128x128x32_adma"
+    assert name(A, Bb, Cb, 32, 14336, 4096, 2).startswith("skinny")
