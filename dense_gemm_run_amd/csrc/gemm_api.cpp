@@ -255,15 +255,15 @@ int select(const Problem& p)
     // 64 x 2048^2 and 8192^2 and 8 x 4096^2: 9-17 % faster than 256 x 256 at
     // K = 64-128, 0-6 % at 256, slower from 512)
     if (p.K <= 256) return 12;
-    if (p.M <= 128) {
-        // 33-128 rows of a wide B: 64 x 128 tiles with A direct to LDS while
-        // they fit one wave of workgroups (bf16, 40-128 rows x 8192-14336: 9-28
-        // % faster than 128 x 128 tiles; 128 x 28672, 448 tiles: 23 % slower)
-        const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
-        if (t64 <= 256) return 37;
-    }
+    // Few tiles: 64 x 128 tiles with A direct to LDS while they fit one wave
+    // of workgroups, else 128 x 128 (bf16, one pass: 40-128 rows of a wide B
+    // 9-28 % faster than on 128 x 128 tiles, 512^3-1024^3 17-21 %,
+    // 512 x 4096 x 4096 11 % faster than the 128 x 128 tiles split in two;
+    // 1536^3 and 128 x 28672, 288 and 448 tiles of 64 x 128, slower)
+    const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
+    if (p.M <= 128 && t64 <= 256) return 37;
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    if (t256 < 128) return 30;
+    if (t256 < 128) return t64 <= 256 ? 37 : 30;
     // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4
     // of a 256 x 256 tile's work at ~94 % of its rate, so a wave of them costs
     // ~0.8 of a wave of 256 x 256 tiles; it wins where 256 x 256 leaves a
@@ -292,7 +292,6 @@ int effective_splits(int splits, int64_t K, int bk)
     return (int)((steps + q - 1) / q);
 }
 
-constexpr int kSplitConfig = 12;     // the 16x16x32 kernel at 128 x 128 tiles
 constexpr int kSplitConfigFew = 37;  // the 16x16x32 kernel at 64 x 128, A direct to LDS
 constexpr int kSplitConfig8 = 38;    // the 8-bit kernel at 64 x 128 x 64, A direct to LDS
 
@@ -309,11 +308,10 @@ int split_count(int64_t tiles, int64_t steps, int64_t K, int bk, int min_steps =
 
 // The choice of gemm_run_ws: a configuration and a split count (1: none).
 // Products of one matrix only; the numbers are from the shape sweep.
-//  * fp16/bf16 with K >= 2048 (64 K-steps) and at most 160 tiles: the
-//    16x16x32 kernel with split_count splits, on 64 x 128 tiles with A
-//    direct to LDS up to 256 rows (a quarter of the MFMAs of a 128-row tile
-//    on rows past M, and room for more workgroups per CU), else on 128 x 128
-//    tiles.  (256 x 4096 x 4096: 19.6
+//  * fp16/bf16 with K >= 2048 (64 K-steps) and at most 160 tiles of
+//    64 x 128: the 16x16x32 kernel at 64 x 128 with A direct to LDS with
+//    split_count splits (a quarter of the MFMAs of a 128-row tile on rows
+//    past M, and room for more workgroups per CU).  (256 x 4096 x 4096: 19.6
 //    us with 4 splits against 31.9 in one pass; 16 x 4096 x 14336: 22.6
 //    with 8 against 38.0 on the strip kernel; 1024^3: 14.4 with 2 against
 //    10.7, hence the K floor.  64 x 128 against 128 x 128 tiles, 16-256 rows
@@ -335,15 +333,13 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
     splits = 1;
     const int c = select(p);
     if (p.batch != 1 || p.M == 0 || p.N == 0) return c;
-    const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     int cfg = -1, s = 1;
     if (p.dtype == kF16 || p.dtype == kBF16) {
-        if (!accepts(kTable[kSplitConfig], p) || kTable[c].kind == kGemv) return c;
+        if (!accepts(kTable[kSplitConfigFew], p) || kTable[c].kind == kGemv) return c;
         const int64_t steps = (p.K + 31) / 32;
-        const bool few = p.M <= 256;
-        const int64_t t = few ? ((p.M + 63) / 64) * ((p.N + 127) / 128) : t128;
+        const int64_t t = ((p.M + 63) / 64) * ((p.N + 127) / 128);
         if (steps < 64 || t > 160) return c;
-        cfg = few ? kSplitConfigFew : kSplitConfig;
+        cfg = kSplitConfigFew;
         s = split_count(t, steps, p.K, 32);
     } else if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[kSplitConfig8], p) || p.M > 128) return c;

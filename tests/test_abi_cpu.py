@@ -356,9 +356,11 @@ def test_workspace_sizes_follow_the_split_rule():
     # 128 x 4096: 64 tiles -> 4 splits; 64 x 14336: 112 tiles -> 2 splits
     assert L.gemm_workspace_size(128, 4096, 4096, 2) == 4 * 128 * 4096 * 4
     assert L.gemm_workspace_size(64, 14336, 4096, 1) == 2 * 64 * 14336 * 4
-    # 16 rows: 32 tiles -> 8 splits; beyond 256 rows 128 x 128 tiles: 512 x 4096 is 128 -> 2
+    # 16 rows: 32 tiles -> 8 splits; 512 x 4096 is 256 tiles, one wave: no split;
+    # 1024 x 1024 x 16384: 128 tiles -> 2 splits of 256 K-steps
     assert L.gemm_workspace_size(16, 4096, 4096, 2) == 8 * 16 * 4096 * 4
-    assert L.gemm_workspace_size(512, 4096, 4096, 2) == 2 * 512 * 4096 * 4
+    assert L.gemm_workspace_size(512, 4096, 4096, 2) == 0
+    assert L.gemm_workspace_size(1024, 1024, 16384, 2) == 2 * 1024 * 1024 * 4
     # 8-bit inputs up to 128 rows: 32 tiles, 64 K-steps of 64 -> 4 splits; K = 14336 -> 8
     assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
     assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
@@ -390,10 +392,9 @@ def test_select_config_ws_falls_back_when_the_workspace_is_short():
     need = dg.gemm_workspace_size(256, 4096, 4096, 2)
     cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need)
     assert dg.gemm_config_info(cid)["name"] == "mfma16x16_64x128x32_adma" and s == 2
-    # beyond 256 rows: 128 x 128 tiles
-    need512 = dg.gemm_workspace_size(512, 4096, 4096, 2)
-    cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 512, 4096, 4096, 2, need512)
-    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32" and s == 2
+    # one wave of 64 x 128 tiles: one pass on them
+    cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 512, 4096, 4096, 2, 1 << 40)
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_64x128x32_adma" and s == 1
     cid, s = dg.gemm_select_config_ws(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2, need - 1)
     assert s == 1 and cid == dg.gemm_select_config(A, A + (1 << 30), A + (1 << 31), 256, 4096, 4096, 2)
     # misaligned A: the generic kernel, no split
@@ -458,3 +459,15 @@ def test_wide_few_rows_select_64x128_tiles_while_they_fit_one_wave():
     # 448 tiles of 64 x 128: back to 128 x 128; up to 32 rows the strip kernels keep wide B
     assert name(A, Bb, Cb, 128, 28672, 4096, 2) == "mfma16x16_128x128x32_adma"
     assert name(A, Bb, Cb, 32, 14336, 4096, 2).startswith("skinny")
+
+
+def test_few_tiles_select_64x128_tiles_while_they_fit_one_wave():
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
+    for n in (512, 768, 1024):
+        assert name(A, Bb, Cb, n, n, n, 2) == "mfma16x16_64x128x32_adma", n
+    assert name(A, Bb, Cb, 512, 4096, 4096, 1) == "mfma16x16_64x128x32_adma"
+    # 288 and 512 tiles of 64 x 128: 128 x 128
+    for n in (1536, 2048):
+        assert name(A, Bb, Cb, n, n, n, 2) == "mfma16x16_128x128x32_adma", n

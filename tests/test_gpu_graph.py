@@ -24,7 +24,7 @@ def note(msg):
 
 # one shape per kernel family the selection reaches (with a workspace, as
 # gemm() runs them), and the strip kernels forced by name
-CASES = [(1000, 1000, 1000, "f16", None),        # 16x16x32 kernel at 128 x 128
+CASES = [(1000, 1000, 1000, "f16", None),        # 16x16x32 kernel at 64 x 128
          (2048, 2048, 1024, "bf16", None),       # 16x16x32 kernel at 256 x 256
          (16, 4096, 4096, "bf16", None),         # split K on 64 x 128 tiles
          (16, 4096, 4096, "bf16", "skinny_16x16x32"),   # few-row strip kernel
