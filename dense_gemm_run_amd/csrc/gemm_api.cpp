@@ -224,8 +224,12 @@ int select(const Problem& p)
         // wave of 256 x 256 tiles (sustained, E4M3: 8192^3 2881 against 2793
         // TFLOP/s, 512 x 4096 x 4096 15.6 against 17.1 us; 3072^3 34.8
         // against 33.4 us the other way round).
+        // Fewer than 128 of them: 64 x 128 tiles with A direct to LDS while
+        // they fit one wave (E4M3, one pass: 512^3-1024^3 11-21 % faster than
+        // on 128 x 128 tiles, 256 x 4096 x 4096 28 %; 1536^3 slower).
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-        return t256 >= 256 ? 32 : t256 >= 128 ? 13 : 33;
+        const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
+        return t256 >= 256 ? 32 : t256 >= 128 ? 13 : t64 <= 256 ? 38 : 33;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) {
         // Timed on bf16 shapes with M 2K-28K, K 2K-14K, N 1-4.  A K-slice

@@ -332,9 +332,11 @@ def test_8bit_tile_size_follows_the_tile_count():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
-    # fewer than 128 tiles of 256 x 256 (half the CUs): 128 x 128 tiles
-    for M, N, K in [(2048, 2048, 2048), (512, 4096, 4096), (128, 4096, 4096), (64, 14336, 4096),
-                    (2816, 2816, 1024)]:
+    # fewer than 128 tiles of 256 x 256 (half the CUs): 64 x 128 tiles while they fit one
+    # wave, else 128 x 128
+    for M, N, K in [(512, 4096, 4096), (128, 4096, 4096), (64, 14336, 4096), (1024, 1024, 1024)]:
+        assert name(A, Bb, Cb, M, N, K, 3) == "fp8_64x128x64_adma", (M, N, K)
+    for M, N, K in [(2048, 2048, 2048), (1536, 1536, 1536), (2816, 2816, 1024)]:
         assert name(A, Bb, Cb, M, N, K, 3).startswith("fp8_128x128"), (M, N, K)
     for M, N, K in [(3072, 3072, 3072), (4096, 4096, 4096), (8192, 14336, 4096)]:
         assert name(A, Bb, Cb, M, N, K, 4).startswith("fp8_256x256"), (M, N, K)

@@ -30,7 +30,7 @@ CASES = [(1000, 1000, 1000, "f16", None),        # 16x16x32 kernel at 64 x 128
          (16, 4096, 4096, "bf16", "skinny_16x16x32"),   # few-row strip kernel
          (4096, 4, 4096, "bf16", None),          # matrix-vector kernel (K split over wavefronts)
          (127, 255, 65, "f16", None),            # generic kernel
-         (1024, 1024, 2048, "fp8_e4m3", None),   # 8-bit kernel at 128 x 128
+         (1024, 1024, 2048, "fp8_e4m3", None),   # 8-bit kernel at 64 x 128
          (32, 4096, 4096, "fp8_e5m2", None),     # 8-bit split K on 64 x 128 tiles
          (32, 4096, 4096, "fp8_e5m2", "skinny8_32x32x128"),   # 8-bit strip kernel
          (256, 4096, 4096, "bf16", None)]        # split K: partial sums in a workspace, then the sum
