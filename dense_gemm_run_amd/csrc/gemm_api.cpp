@@ -324,10 +324,12 @@ int split_count(int64_t tiles, int64_t steps, int64_t K, int bk, int min_steps =
 //    kernel for 1-8 rows: 7.0-7.3 against 8.9-11.0 us at 4096 x 4096, 20.2
 //    against 34.3 at 8 x 4096 x 14336.)
 //  * 8-bit inputs, up to 128 rows, K >= 2048: the 8-bit kernel at
-//    64 x 128 x 64 with A direct to LDS, split likewise, with at least 16
-//    K-steps of 64 per split up to 64 rows and 32 above (the fp32 partial
-//    sums, 4 bytes per output against 1-byte inputs, weigh more with more
-//    rows).  Beyond 128 rows they cost more than the split gains.  (E4M3,
+//    64 x 128 x 64 with A direct to LDS, split likewise, with at least 8
+//    K-steps of 64 per split up to 16 rows, 16 up to 64 rows and 32 above
+//    (the fp32 partial sums, 4 bytes per output against 1-byte inputs, weigh
+//    more with more rows; 1-16 rows x 4096 x 4096: 5.4-6.3 us with 8 splits
+//    against 6.1-6.6 with 4 and 6.4-7.7 on the strip kernel; 64 rows: 8.9
+//    with 4, 11.3 with 8).  Beyond 128 rows they cost more than the split gains.  (E4M3,
 //    against the 128 x 128 split: 16-128 rows x 4096 x 4096 6.6-9.7 us
 //    against 7.6-13.4, 1-5 % faster with N or K = 14336; 64 x 4096 x 14336:
 //    17.0 us with 8 splits on 128 x 128 tiles against 38.4 on the strip
@@ -350,7 +352,8 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
         const int64_t steps = (p.K + 63) / 64;
         if (steps < 32) return c;
         cfg = kSplitConfig8;
-        s = split_count(((p.M + 63) / 64) * ((p.N + 127) / 128), steps, p.K, 64, p.M > 64 ? 32 : 16);
+        s = split_count(((p.M + 63) / 64) * ((p.N + 127) / 128), steps, p.K, 64,
+                        p.M <= 16 ? 8 : p.M <= 64 ? 16 : 32);
     } else {
         return c;
     }

@@ -367,9 +367,11 @@ def test_workspace_sizes_follow_the_split_rule():
     assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
     assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(16, 14336, 4096, 3) == 2 * 16 * 14336 * 4
-    # 8-bit tiles are 64 x 128: 16 rows of 4096 columns are 32 tiles -> 4 splits (64 K-steps);
-    # beyond 64 rows each split keeps at least 32 K-steps: 128 x 4096 x 4096 -> 2
-    assert L.gemm_workspace_size(16, 4096, 4096, 3) == 4 * 16 * 4096 * 4
+    # 8-bit tiles are 64 x 128: 16 rows of 4096 columns are 32 tiles -> 8 splits of 8 K-steps;
+    # up to 64 rows each split keeps at least 16 K-steps (4 splits), beyond that 32:
+    # 128 x 4096 x 4096 -> 2
+    assert L.gemm_workspace_size(16, 4096, 4096, 3) == 8 * 16 * 4096 * 4
+    assert L.gemm_workspace_size(32, 4096, 4096, 3) == 4 * 32 * 4096 * 4
     assert L.gemm_workspace_size(128, 4096, 4096, 3) == 2 * 128 * 4096 * 4
     # 1 to 8 rows split too (8 splits of the 32 tiles of 64 x 128)
     assert L.gemm_workspace_size(8, 4096, 4096, 2) == 8 * 8 * 4096 * 4
