@@ -135,7 +135,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(32))
+@pytest.mark.parametrize("cid", range(40))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
