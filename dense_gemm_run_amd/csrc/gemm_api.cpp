@@ -86,6 +86,8 @@ const Entry kTable[] = {
     {{37, 64, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_64x128x32_adma", 1}, kMfma16x16},
     // the 8-bit kernel at 64 x 128 x 64, A direct to LDS: few rows with split K
     {{38, 64, 128, 64, 4, 256, 0x18, 1, 1, "fp8_64x128x64_adma", 1}, kFp8},
+    // the 8-bit kernel at 192 x 256 x 64, A direct to LDS: partial last waves
+    {{39, 192, 256, 64, 4, 256, 0x18, 1, 1, "fp8_192x256x64_adma", 1}, kFp8},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -229,6 +231,10 @@ int select(const Problem& p)
         // on 128 x 128 tiles, 256 x 4096 x 4096 28 %; 1536^3 slower).
         const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
         const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
+        // a partial last wave of 256 x 256 tiles: 192 x 256 where its waves
+        // cost less, by the 16-bit rule below
+        const int64_t t192 = ((p.M + 191) / 192) * ((p.N + 255) / 256) * p.batch;
+        if (t256 >= 128 && ((t192 + 255) / 256) * 80 < ((t256 + 255) / 256) * 95) return 39;
         return t256 >= 256 ? 32 : t256 >= 128 ? 13 : t64 <= 256 ? 38 : 33;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) {

@@ -98,7 +98,7 @@ template <int BN> __device__ __forceinline__ int swz_b(int k)
 }
 
 template <int FMT, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
-__global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_kernel(
+__global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_kernel(
     const unsigned char* A, const unsigned char* B, __bf16* C,
     int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
 {
@@ -121,7 +121,9 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     constexpr int NR = FM + FN;                  // operand fragments per K-slice
     constexpr int BAR = XS - NT / 2;             // MFMAs of a K-step before its barrier
     static_assert(BK == 64 || BK == 128, "K-step");
-    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 128 && ADMA), "tile");
+    static_assert((BM == 256 && BN == 256) || (BM == 128 && BN == 128) || (BM == 64 && BN == 128 && ADMA) ||
+                      (BM == 192 && BN == 256 && ADMA),
+                  "tile");
     static_assert(LEAD % 2 == 0 && LEAD % SB == 0, "slot and stage periods must divide the unroll");
     static_assert((SB - 1) * B_BYTES < 65536, "LDS immediate offsets");
     static_assert(!ADMA || (SB == 4 && LEAD == 4), "direct A loads: 64-deep K-steps");
@@ -421,8 +423,11 @@ __global__ __launch_bounds__(256, BM * BN == 256 * 256 ? 1 : 2) void gemm_fp8_ke
     const int row0 = m0 + wm * WM, col0 = n0 + wn * WN;
     constexpr int BLOCK = WM * WN * 2;
     if constexpr (SB == 4) {
-        store_c_block_32x32<__bf16, WM, WN, (B_BYTES < BLOCK ? B_BYTES : BLOCK)>(acc, b_stage(wave), lane,
-                                                                              row0, col0, M, N, C);
+        // passes of as many whole 32-row tile rows as a B stage holds and WM
+        // divides into (32 of 96)
+        constexpr int CWB = B_BYTES < BLOCK ? B_BYTES : BLOCK;
+        constexpr int CW = WM % (CWB / (WN * 2)) == 0 ? CWB : 32 * WN * 2;
+        store_c_block_32x32<__bf16, WM, WN, CW>(acc, b_stage(wave), lane, row0, col0, M, N, C);
     } else {
         static_assert(A_BYTES == B_BYTES, "one C region per wavefront");
         lds_byte* cw = wave < 2 ? a_stage(wave) : b_stage(wave - 2);
@@ -460,6 +465,9 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
                                a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
         else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
+                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+        else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 64)
+            hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 192, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
                                a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
         else
             return hipErrorInvalidValue;

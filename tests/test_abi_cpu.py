@@ -338,11 +338,13 @@ def test_8bit_tile_size_follows_the_tile_count():
         assert name(A, Bb, Cb, M, N, K, 3) == "fp8_64x128x64_adma", (M, N, K)
     for M, N, K in [(2048, 2048, 2048), (1536, 1536, 1536), (2816, 2816, 1024)]:
         assert name(A, Bb, Cb, M, N, K, 3).startswith("fp8_128x128"), (M, N, K)
-    for M, N, K in [(3072, 3072, 3072), (4096, 4096, 4096), (8192, 14336, 4096)]:
+    for M, N, K in [(4096, 4096, 4096), (8192, 14336, 4096), (8192, 8192, 8192)]:
         assert name(A, Bb, Cb, M, N, K, 4).startswith("fp8_256x256"), (M, N, K)
+    # a partial last wave of 256 x 256 tiles that 192 x 256 tiles fill: 3072^2, 6144^2
+    for n in (3072, 6144):
+        assert name(A, Bb, Cb, n, n, n, 3) == "fp8_192x256x64_adma", n
     # A direct to LDS except for a partial single wave of 256 x 256 tiles
     assert name(A, Bb, Cb, 4096, 4096, 4096, 3) == "fp8_256x256x64_adma"
-    assert name(A, Bb, Cb, 3072, 3072, 3072, 3) == "fp8_256x256x64"
     assert name(A, Bb, Cb, 2048, 2048, 2048, 3) == "fp8_128x128x64_adma"
     # the batch counts: 16 products of 1024^2 are 256 tiles of 256 x 256
     cid = dg.gemm_select_config_batched(A, Bb, Cb, 16, 1024, 1024, 1024, 1024 * 1024, 1024 * 1024,

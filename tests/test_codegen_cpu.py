@@ -32,9 +32,9 @@ FAMILIES = {
                   40, 2, "v_mfma_f32_16x16x32", 32, 16 * 16),
     "fp8": ("gemm_fp8.hip", r"gemm_fp8_kernelILi\d+ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)ELb(\d)E",
             # {e4m3, e5m2} x ({256x256, 128x128} x {64, 128} x {one pass, split K}
-            #                 + {256x256, 128x128, 64x128} x 64 with A direct to LDS
+            #                 + {256x256, 192x256, 128x128, 64x128} x 64 with A direct to LDS
             #                 + {128x128, 64x128} x 64 split with A direct to LDS)
-            26, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
+            28, 1, "v_mfma_f32_32x32x64_f8f6f4", 64, 32 * 32),
 }
 
 
