@@ -3,7 +3,9 @@
 ``gemm(a, b)`` takes two row-major CUDA/ROCm tensors of one dtype (fp32, fp16
 or bf16) and returns C = a @ b of that dtype, computed by the library's HIP
 kernels on the current stream (fp32 accumulation, round-to-nearest-even
-output).  8-bit inputs (``torch.float8_e4m3fn`` or ``torch.float8_e5m2``,
+output) through ``gemm_run``, which allocates nothing; ``split_k=True`` opts
+into the split-K schedule of ``gemm_run_ws`` with a workspace from torch's
+allocator.  8-bit inputs (``torch.float8_e4m3fn`` or ``torch.float8_e5m2``,
 the OCP formats) give a bf16 C.  The C-ABI functions are re-exported under their C names.
 PyTorch supplies device memory and the stream; nothing else.
 """
@@ -64,10 +66,13 @@ class Gemm:
         except Exception:
             pass
 
-    def __call__(self, a, b, out=None, config: int | None = None, splits: int | None = None):
-        """C = a @ b.  Products that gemm_run_ws would split over K get their
-        workspace from torch's allocator on the current stream (stream-ordered,
-        so concurrent streams never share one).  ``config`` forces a kernel
+    def __call__(self, a, b, out=None, config: int | None = None, splits: int | None = None,
+                 split_k: bool = False):
+        """C = a @ b through gemm_run, which allocates nothing.  With
+        ``split_k=True`` the product goes through gemm_run_ws instead: where
+        it splits K (few output tiles, long K) its workspace comes from
+        torch's allocator on the current stream (stream-ordered, so
+        concurrent streams never share one).  ``config`` forces a kernel
         configuration, and with it ``splits`` a split count."""
         import torch
         if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
@@ -90,7 +95,7 @@ class Gemm:
         stream = torch.cuda.current_stream(self.device).cuda_stream
         with torch.cuda.device(self.device):
             if config is None:
-                ws = gemm_workspace_size(M, N, K, code)
+                ws = gemm_workspace_size(M, N, K, code) if split_k else 0
                 if ws > 0:
                     work = torch.empty(ws, dtype=torch.uint8, device=self.device)
                     gemm_run_ws(self.handle, a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
@@ -157,13 +162,15 @@ class Gemm:
 _default: dict[int, Gemm] = {}
 
 
-def gemm(a, b, out=None, config: int | None = None, splits: int | None = None):
-    """C = a @ b on a's device and the current stream (see module docstring)."""
+def gemm(a, b, out=None, config: int | None = None, splits: int | None = None,
+         split_k: bool = False):
+    """C = a @ b on a's device and the current stream (see module docstring
+    and Gemm.__call__)."""
     idx = a.device.index if a.device.index is not None else 0
     g = _default.get(idx)
     if g is None:
         g = _default[idx] = Gemm(idx)
-    return g(a, b, out=out, config=config, splits=splits)
+    return g(a, b, out=out, config=config, splits=splits, split_k=split_k)
 
 
 def gemm_batched(a, b, out=None, config: int | None = None):

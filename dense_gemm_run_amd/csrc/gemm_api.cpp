@@ -380,9 +380,35 @@ gemm_status_t check_ws(const Problem& p, const void* ws, int64_t ws_bytes)
     return GEMM_OK;
 }
 
+// Whether configuration e's grid for these arguments fits the launch: its
+// kernels number their workgroups with 32-bit ints (at most 2^31-1 of them),
+// and HIP takes at most 2^32-1 lanes in one grid.  Every launcher makes
+// ceil(M/bm) * ceil(N/bn) workgroups per product (ceil(M/bm) for the
+// matrix-vector kernel, whose workgroups cover all N <= 4 columns), times the
+// batch, or times the split count for a split product.
+bool grid_fits(const Entry& e, const Problem& p, int splits)
+{
+    const int64_t tm = (p.M + e.cfg.bm - 1) / e.cfg.bm;
+    const int64_t tn = e.kind == kGemv ? 1 : (p.N + e.cfg.bn - 1) / e.cfg.bn;
+    const int64_t per = tm * tn;   // < 2^62: M, N < 2^31
+    if (per > INT32_MAX) return false;
+    const int64_t groups = per * (splits > 1 ? splits : p.batch);   // < 2^62
+    return groups <= INT32_MAX && groups * e.cfg.threads <= (int64_t)UINT32_MAX;
+}
+
+// The checks of gemm_run before anything is enqueued: the arguments, then
+// the grid of the configuration it selects.
+gemm_status_t check_run(const Problem& p)
+{
+    const gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    return grid_fits(kTable[select(p)], p, 1) ? GEMM_OK : GEMM_ERR_TOO_LARGE;
+}
+
 gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream, int splits = 1,
                      void* ws = nullptr)
 {
+    if (!grid_fits(e, p, splits)) return GEMM_ERR_TOO_LARGE;
     if (!h) return GEMM_ERR_INVALID_VALUE;
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return GEMM_ERR_HIP;
@@ -514,14 +540,14 @@ const char* gemm_status_string(int32_t s)
 gemm_status_t gemm_check_args(const void* A, const void* B, const void* C,
                               int64_t M, int64_t N, int64_t K, int32_t dtype)
 {
-    return check_args(single(A, B, const_cast<void*>(C), M, N, K, dtype));
+    return check_run(single(A, B, const_cast<void*>(C), M, N, K, dtype));
 }
 
 gemm_status_t gemm_check_args_batched(const void* A, const void* B, const void* C, int64_t batch,
                                       int64_t M, int64_t N, int64_t K, int64_t stride_a,
                                       int64_t stride_b, int64_t stride_c, int32_t dtype)
 {
-    return check_args(Problem{A, B, const_cast<void*>(C), M, N, K, dtype, batch, stride_a, stride_b, stride_c});
+    return check_run(Problem{A, B, const_cast<void*>(C), M, N, K, dtype, batch, stride_a, stride_b, stride_c});
 }
 
 int32_t gemm_config_count(void) { return kTableSize; }

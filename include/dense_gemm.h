@@ -66,7 +66,8 @@ typedef enum gemm_status {
     GEMM_ERR_INVALID_VALUE = 1,      /* negative size, null pointer with data, null handle, wrong device, bad config id */
     GEMM_ERR_UNSUPPORTED_DTYPE = 2,  /* dtype is not one of gemm_dtype_t */
     GEMM_ERR_UNSUPPORTED_DEVICE = 3, /* no GPU, or the current device is not gfx950 */
-    GEMM_ERR_TOO_LARGE = 4,          /* a dimension > 2^31-1 or a matrix of 2^31 bytes or more */
+    GEMM_ERR_TOO_LARGE = 4,          /* a dimension > 2^31-1, a matrix of 2^31 bytes or more, or a
+                                      * launch grid beyond 2^31-1 workgroups or 2^32-1 lanes */
     GEMM_ERR_ALIASING = 5,           /* C's bytes overlap A's or B's (or, batched, another C matrix) */
     GEMM_ERR_HIP = 6,                /* a HIP runtime call failed */
     GEMM_ERR_CONFIG_MISMATCH = 7     /* forced kernel configuration cannot run these arguments */

@@ -27,6 +27,14 @@ Functions and what pins them (tests/test_oracle_pins.py):
                     (numpy's binary16 decode), and by the ordering invariant
                     (codes 0 .. largest finite decode strictly increasing; the
                     sign bit mirrors them).
+``decoded_max_abs``  the largest finite magnitude among decoded codes (it
+                    sets the absolute floor of the 8-bit comparisons).
+                    Pinned by hand-checked sets of codes: every code gives the
+                    format's largest finite value (448 / 57344), a negative
+                    code of larger magnitude beats a positive one whose raw
+                    code is smaller, NaN and infinity codes are ignored, an
+                    empty set gives 0 (``test_fp8_decoded_max_abs``, with
+                    planted mistakes in ``test_oracle_mutants.py``).
 ``reference_fp8``   the product of decoded inputs in fp64 (``gemm64``) rounded
                     once to bf16, the output type of the 8-bit path.  Pinned
                     by exact integer products (small integers are exact in

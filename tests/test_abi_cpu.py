@@ -191,9 +191,31 @@ def test_xcd_remap_gives_each_xcd_a_compact_block():
     ((A, B, C, 2, 1 << 16, 1 << 14, 1, 0, 0, 1 << 30, 1), TOOBIG),   # one C matrix of 2^31 bytes
     ((A, B, C, 3, 4, 5, 6, 1 << 62, 30, 20, 1), TOOBIG),   # A's span overflows
     ((A, B, C, 1 << 20, 4096, 4096, 8, 0, 0, 1 << 24, 1), TOOBIG),   # grid of 2^32 workgroups
+    # batched matrix-vector products (4 rows of A per 256-lane workgroup):
+    # 1024 workgroups per product, so 16383 products are 2^32 - 2^18 lanes
+    # and 16384 are 2^32, one more than a grid holds
+    ((A, B, C, 16383, 4096, 1, 4096, 0, 0, 4096, 1), OK),
+    ((A, B, C, 16384, 4096, 1, 4096, 0, 0, 4096, 1), TOOBIG),
 ])
 def test_check_args_batched(args, want):
     assert dg.gemm_check_args_batched(*args) == want
+
+
+def test_grid_limit_is_checked_before_the_handle():
+    """A batched matrix-vector product whose grid would exceed 2^32-1 lanes
+    is refused as too large by gemm_run_batched itself, before anything
+    else (here: the missing handle) is looked at; one product fewer reaches
+    the handle check."""
+    assert dg.gemm_select_config_batched(A, B, C, 16384, 4096, 1, 4096, 0, 0, 4096, 1) == 34
+    info = dg.gemm_config_info(34)
+    assert (info["bm"], info["threads"]) == (4, 256)
+    L = _lib.lib()
+    assert L.gemm_run_batched(None, A, B, C, 16384, 4096, 1, 4096, 0, 0, 4096, 1, None) == TOOBIG
+    assert L.gemm_run_batched(None, A, B, C, 16383, 4096, 1, 4096, 0, 0, 4096, 1, None) == INVALID
+    # a batch of 2^21 products would wrap a 32-bit workgroup count
+    assert L.gemm_run_batched(None, A, B, C, 1 << 21, 4096, 1, 4096, 0, 0, 4096, 1, None) == TOOBIG
+    # forced configurations: the grid of the configuration that was asked for
+    assert L.gemm_run_batched_config(None, A, B, C, 16384, 4096, 1, 4096, 0, 0, 4096, 1, 34, None) == TOOBIG
 
 
 def test_single_calls_are_the_batch_of_one():

@@ -169,9 +169,9 @@ def test_fp8_workloads_sampled(name):
     rows = [0, w.M - 1, int(rng.integers(0, w.M))]
     cols = [0, w.N - 1, int(rng.integers(0, w.N))]
     pr = np.concatenate([np.full(w.N, r) for r in rows] + [np.arange(w.M) for _ in cols]
-                        + [rng.integers(0, w.M, 20000)])
+                        + [rng.integers(0, w.M, 100000)])
     pc = np.concatenate([np.arange(w.N) for _ in rows] + [np.full(w.M, c_) for c_ in cols]
-                        + [rng.integers(0, w.N, 20000)])
+                        + [rng.integers(0, w.N, 100000)])
     A64 = fp8.decode(fp8._bits(A), fmt)
     B64 = fp8.decode(fp8._bits(B), fmt)
     exact_vals = gemm64.gemm_points_f64(A64, B64, pr, pc)

@@ -2,9 +2,10 @@
 
 Every comparison is element by element on the same seeded inputs, with the
 acceptance rule of ``oracle.tolerance`` (rtol 2e-3 fp16 / 1e-2 bf16 / 1e-5
-fp32, floor 1e-3·sqrt(K)·max|A|·max|B|).  Small and mid shapes are compared
-whole; the full-size workloads are compared on sampled outputs (whole rows
-and columns plus random points), each computed by the oracle one by one.
+fp32, floor 1e-3·sqrt(K)·max|A|·max|B|).  Small and mid shapes and the
+4096^3 headline product are compared whole; the 8192-row workloads are
+compared on sampled outputs (whole rows and columns plus 100,000 random
+points), each computed by the oracle one by one.
 """
 import math
 import sys
@@ -66,7 +67,7 @@ def check_full(A, B, dtype, C_gpu, use_floor=True):
     return rep
 
 
-def sampled_check(A, B, dtype, C_gpu, n_points=20000, seed=0):
+def sampled_check(A, B, dtype, C_gpu, n_points=100000, seed=0):
     M, K = A.shape
     N = B.shape[1]
     rng = np.random.default_rng(seed)
@@ -255,14 +256,37 @@ def test_api_errors_on_gpu():
         dg.gemm_destroy(h)
 
 
-# ---------------------------------------------------------------- full-size workloads, sampled
-FULL = ["f16_4096x4096x4096", "bf16_8192x8192x8192", "bf16_prefill_qkv_8192x12288x4096",
+# ---------------------------------------------------------------- full-size workloads
+def test_headline_workload_whole():
+    """The square fp16 4096^3 product that bench.py times, in the
+    configuration gemm_run picks, compared with the oracle on every one of
+    its 16.8 M outputs (the correctness check of notebook "Triton tiled
+    matmul", section "Correctness check", compares the whole output too)."""
+    name = "f16_4096x4096x4096"
+    w = WORKLOADS[name]
+    note(f"[parity] full-size {name}, whole output")
+    A, B = workload_operands(name)
+    a, b = A.cuda(), B.cuda()
+    C = torch.empty((w.M, w.N), dtype=a.dtype, device="cuda")
+    cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), C.data_ptr(), w.M, w.N, w.K,
+                                DT_CODE[w.dtype])
+    note(f"  config {cid} {dg.gemm_config_info(cid)['name']}")
+    dg.gemm(a, b, out=C)
+    torch.cuda.synchronize()
+    rep = check_full(A, B, w.dtype, C)
+    note(f"  {rep}")
+
+
+FULL = ["bf16_8192x8192x8192", "bf16_prefill_qkv_8192x12288x4096",
         "bf16_prefill_out_8192x4096x4096", "bf16_prefill_up_8192x14336x4096",
         "bf16_prefill_down_8192x4096x14336"]
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_workloads_sampled(name):
+    """The 8192-row workloads: whole rows 0, M-1 and one random row, whole
+    columns 0, N-1 and one random column, and 100,000 random points, each an
+    fp64 dot product of the oracle."""
     w = WORKLOADS[name]
     note(f"[parity] full-size {name}")
     A, B = workload_operands(name)

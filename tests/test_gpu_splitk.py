@@ -73,7 +73,7 @@ def test_selected_split_shapes_sampled(shape):
     cid, s = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, 2, need)
     note(f"[splitk] selected {dg.gemm_config_info(cid)['name']} x {s} for {shape}")
     assert s > 1 and need == s * M * N * 4
-    dg.gemm(a, b, out=c)
+    dg.gemm(a, b, out=c, split_k=True)
     torch.cuda.synchronize()
     rep = sampled_check(A, B, "bf16", c, seed=M)
     note(f"  {rep}")
@@ -181,7 +181,7 @@ def test_selected_8bit_split_shapes_sampled(shape):
     cid, s = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, 3, need)
     note(f"[splitk] selected {dg.gemm_config_info(cid)['name']} x {s} for 8-bit {shape}")
     assert s > 1 and dg.gemm_config_info(cid)["name"].startswith("fp8_64x128")
-    dg.gemm(a, b, out=c)
+    dg.gemm(a, b, out=c, split_k=True)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M)
     pr = np.concatenate([np.full(N, 0), np.full(N, M - 1), np.arange(M), rng.integers(0, M, 20000)])

@@ -155,3 +155,43 @@ def test_unmutated_decode_passes():
                                     "sign_dropped"])
 def test_decode_mutant_is_caught(mutant):
     assert not decode_pins_pass(lambda b, f: decode_mutant(b, f, mutant))
+
+
+# ---------------------------------------------------------------- 8-bit input magnitude
+def max_abs_mutant(x, fmt, mutant):
+    """A copy of the oracle's decoded-max-abs with one planted mistake."""
+    from oracle import fp8
+    codes = fp8._bits(x)
+    v = fp8.decode(codes, fmt)
+    if mutant == "raw_codes":
+        v = codes.astype(np.float64)
+    elif mutant == "signed_max":
+        v = v[np.isfinite(v)]
+        return float(v.max()) if v.size else 0.0
+    elif mutant == "specials_kept":   # infinities count (NaN still dropped)
+        v = v[~np.isnan(v)]
+        return float(np.abs(v).max()) if v.size else 0.0
+    elif mutant == "first_only":
+        v = v.reshape(-1)[:1]
+    v = v[np.isfinite(v)]
+    return float(np.abs(v).max()) if v.size else 0.0
+
+
+@pytest.mark.parametrize("mutant", ["raw_codes", "signed_max", "specials_kept", "first_only"])
+def test_max_abs_mutant_is_caught(mutant):
+    import torch
+    from test_oracle_pins import fp8_max_abs_checks
+    caught = 0
+    for fmt, tdt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        try:
+            fp8_max_abs_checks(lambda x, f: max_abs_mutant(x, f, mutant), fmt, tdt)
+        except AssertionError:
+            caught += 1
+    assert caught >= 1, mutant
+
+
+def test_unmutated_max_abs_passes():
+    import torch
+    from test_oracle_pins import fp8_max_abs_checks
+    for fmt, tdt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        fp8_max_abs_checks(lambda x, f: max_abs_mutant(x, f, None), fmt, tdt)

@@ -519,3 +519,40 @@ def test_fp8_reference_rounds_once_to_bf16():
     ref, raw = fp8.reference_fp8(a5, b5, "e5m2")
     assert raw[0, 0] == 1 + 2.0 ** -8 + 2.0 ** -12
     assert ref[0, 0] == 1 + 2.0 ** -7
+
+
+def fp8_max_abs_checks(fn, fmt, tdt):
+    """Checks of a decoded-max-abs function ``fn(codes, fmt)`` (raises
+    AssertionError on the first failure).  Expected values come from the OCP
+    definitions (E4M3 largest 448, E5M2 largest 57344; NaN and infinity codes
+    are not values and are left out)."""
+    from oracle import fp8
+    # every code: the format's largest finite magnitude
+    assert fn(np.arange(256, dtype=np.uint8), fmt) == {"e4m3": 448.0, "e5m2": 57344.0}[fmt]
+    # the magnitude counts, not the signed value or the raw code: -4 (0xC8
+    # in E4M3, 0xC4 in E5M2) against +1 (0x38 / 0x3C) gives 4, where the
+    # largest raw code (0xC8 = 200) or the largest signed value (1) would not
+    minus4 = {"e4m3": 0xC8, "e5m2": 0xC4}[fmt]
+    one = {"e4m3": 0x38, "e5m2": 0x3C}[fmt]
+    assert list(fp8.decode(np.array([minus4, one]), fmt)) == [-4.0, 1.0]
+    assert fn(np.array([minus4, one], dtype=np.uint8), fmt) == 4.0
+    assert fn(np.array([one, minus4], dtype=np.uint8), fmt) == 4.0
+    # the smallest subnormal alone (2^-9 / 2^-16)
+    assert fn(np.array([0x81], dtype=np.uint8), fmt) == {"e4m3": 2.0 ** -9, "e5m2": 2.0 ** -16}[fmt]
+    # NaN (and, for E5M2, infinity) codes only, or nothing: 0
+    specials = np.array(FP8_NAN[fmt] + ([0x7C, 0xFC] if fmt == "e5m2" else []), dtype=np.uint8)
+    assert fn(specials, fmt) == 0.0
+    assert fn(np.array([], dtype=np.uint8), fmt) == 0.0
+    # a special next to a finite value is ignored
+    assert fn(np.concatenate([specials, np.array([one], dtype=np.uint8)]), fmt) == 1.0
+    # a CPU torch tensor of the format is read by its codes: -3.5 and 1.0 give 3.5
+    t = torch.tensor([[-3.5, 1.0], [0.0, 0.5]]).to(tdt)
+    assert fn(t, fmt) == 3.5
+
+
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)])
+def test_fp8_decoded_max_abs(fmt, tdt):
+    """The largest finite magnitude of a set of 8-bit codes, which sets the
+    absolute floor of the 8-bit comparisons."""
+    from oracle import fp8
+    fp8_max_abs_checks(fp8.decoded_max_abs, fmt, tdt)
