@@ -67,7 +67,11 @@ SIGNATURES = {
                                   _VP]),
     "gemm_select_config_ws": (_I32, [_VP, _VP, _VP, _I64, _I64, _I64, _I32, _I64,
                                      ctypes.POINTER(_I32)]),
+    "gemm_run_noalloc": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _VP]),
 }
+
+# Size of the library's own scratch used by gemm_run_noalloc (per device).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -213,3 +217,9 @@ def gemm_select_config_ws(A: int, B: int, C: int, M: int, N: int, K: int, dtype:
     s = _I32(1)
     cid = lib().gemm_select_config_ws(A, B, C, M, N, K, dtype, workspace_bytes, ctypes.byref(s))
     return cid, s.value
+
+
+def gemm_run_noalloc(h, A: int, B: int, C: int, M: int, N: int, K: int, dtype: int,
+                     stream=None) -> None:
+    """gemm_run_ws with the library's own scratch (allocates nothing)."""
+    _check(lib().gemm_run_noalloc(h, A, B, C, M, N, K, dtype, stream), "gemm_run_noalloc")

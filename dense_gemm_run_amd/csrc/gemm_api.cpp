@@ -5,6 +5,7 @@
 // section "The kernel", and chapter "Fast matrix multiplication", the
 // Triton wrapper): [M,K] @ [K,N] -> [M,N], the caller provides C of the input
 // type, one 1-D grid of ceil(M/BM)*ceil(N/BN) workgroups, asynchronous launch.
+#include <mutex>
 #include <string.h>
 
 #include <hip/hip_runtime.h>
@@ -12,10 +13,18 @@
 #include "../../include/dense_gemm.h"
 #include "gemm_internal.h"
 
+// Scratch of gemm_run_noalloc (for callers that cannot allocate): the fp32
+// partial sums of a split-K product.  Every device the library runs on holds
+// its own copy until the process ends.  In host code this name is only a
+// stand-in for the device array; its device address, looked up once per
+// device by gemm_create, is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
 struct gemm_ctx {
     int device;
     int cu_count;
     char arch[64];
+    void* scratch;   // device address of `scratch` on `device`
 };
 
 namespace dgr {
@@ -485,6 +494,41 @@ gemm_status_t run_config(gemm_handle_t h, const Problem& p, int32_t config_id, v
     return launch(e, h, p, stream);
 }
 
+// Device address of `scratch` per device, looked up once per device (with
+// that device current) and kept for the life of the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+gemm_status_t scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return GEMM_ERR_HIP;
+        }
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return GEMM_OK;
+}
+
+// gemm_run_ws's choice with the library's scratch as the workspace.
+gemm_status_t run_noalloc(gemm_handle_t h, const Problem& p, void* stream)
+{
+    const gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    if (!h || !h->scratch) return GEMM_ERR_INVALID_VALUE;
+    int splits = 1;
+    const int c = select_ws(p, INT64_MAX, splits);
+    if (splits > 1 && (int64_t)splits * p.M * p.N * 4 > (int64_t)GEMM_NOALLOC_SCRATCH_BYTES)
+        return GEMM_ERR_TOO_LARGE;
+    return launch(kTable[c], h, p, stream, splits, splits > 1 ? h->scratch : nullptr);
+}
+
 }  // namespace
 }  // namespace dgr
 
@@ -506,8 +550,12 @@ gemm_status_t gemm_create(gemm_handle_t* out)
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    void* sp = nullptr;
+    const gemm_status_t st = scratch_address(dev, &sp);
+    if (st != GEMM_OK) return st;
     gemm_ctx* h = new (std::nothrow) gemm_ctx;
     if (!h) return GEMM_ERR_HIP;
+    h->scratch = sp;
     h->device = dev;
     h->cu_count = prop.multiProcessorCount;
     strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
@@ -635,6 +683,12 @@ gemm_status_t gemm_run_ws(gemm_handle_t h, const void* A, const void* B, void* C
                           int64_t K, int32_t dtype, void* workspace, int64_t workspace_bytes, void* stream)
 {
     return run_ws(h, single(A, B, C, M, N, K, dtype), workspace, workspace_bytes, stream);
+}
+
+gemm_status_t gemm_run_noalloc(gemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                               int64_t K, int32_t dtype, void* stream)
+{
+    return run_noalloc(h, single(A, B, C, M, N, K, dtype), stream);
 }
 
 gemm_status_t gemm_run_ws_config(gemm_handle_t h, const void* A, const void* B, void* C, int64_t M,

@@ -157,6 +157,33 @@ gemm_status_t gemm_run_ws(gemm_handle_t h, const void* A, const void* B, void* C
                           int64_t M, int64_t N, int64_t K, int32_t dtype,
                           void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * gemm_run_noalloc is gemm_run_ws with the library's own scratch in place of
+ * the workspace argument: a file-scope device array of
+ * GEMM_NOALLOC_SCRATCH_BYTES (16 MiB) in the library, of which every device
+ * the library runs on holds one copy until the process ends (gemm_create
+ * looks up its address once per device).  The call allocates nothing (no
+ * hipMalloc, no allocating library routine) and never synchronises.
+ * Arguments, results and errors are gemm_run_ws's with a 16 MiB workspace:
+ * the same kernels, split count and bitwise result, except that a product
+ * whose split would need more than the array holds is refused with
+ * GEMM_ERR_TOO_LARGE before anything is enqueued (the split rule asks for at
+ * most 11 MiB: s * M * N * 4 bytes for about 256 workgroups of 64 x 128
+ * outputs).  Products that do not split run as gemm_run.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents; nothing in it has to start at zero (each split writes
+ * every element of its slice before the reduction reads it).  Calls that may
+ * overlap in time on one device (other streams, other host threads) race on
+ * the array and must be serialised by the caller.
+ * ------------------------------------------------------------------------- */
+#define GEMM_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+gemm_status_t gemm_run_noalloc(gemm_handle_t h, const void* A, const void* B, void* C,
+                               int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream);
+
 /* Release a handle.  NULL is accepted and ignored.  No work may still be
  * using the handle (enqueued work does not refer to it). */
 gemm_status_t gemm_destroy(gemm_handle_t h);

@@ -499,3 +499,24 @@ def test_few_tiles_select_64x128_tiles_while_they_fit_one_wave():
     # 288 and 512 tiles of 64 x 128: 128 x 128
     for n in (1536, 2048):
         assert name(A, Bb, Cb, n, n, n, 2) == "mfma16x16_128x128x32_adma", n
+
+
+def test_noalloc_entry_point_host_checks():
+    """gemm_run_noalloc's host side: the scratch size in the header and the
+    binding agree, every split the selection makes fits it (so its
+    too-large refusal is a guard, not a case the split rule reaches), and
+    argument errors come before any device work."""
+    text = open(HEADER).read()
+    m = re.search(r"#define GEMM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+    most = 0
+    for dtype in (1, 2, 3, 4):
+        for M in list(range(1, 130)) + [200, 256, 300, 512]:
+            for N in (8, 128, 1000, 4096, 10240, 14336, 20480, 28672):
+                for K in (2048, 4096, 14336, 65536):
+                    most = max(most, dg.gemm_workspace_size(M, N, K, dtype))
+    assert 0 < most <= _lib.NOALLOC_SCRATCH_BYTES, most
+    L = _lib.lib()
+    assert L.gemm_run_noalloc(None, A, B, C, 16, 4096, 4096, 2, None) == INVALID
+    assert L.gemm_run_noalloc(None, A, B, C, 16, 4096, 4096, 9, None) == BADTYPE
+    assert L.gemm_run_noalloc(None, A, B, A + 8, 16, 4096, 4096, 2, None) == ALIAS
