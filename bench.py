@@ -35,8 +35,6 @@ Prints one JSON line (stdout):
                       output (all rows at 4096^3), with the acceptance rule of
                       the tests
   repeats/median/min  five blocks of K steps: per-step times, median, minimum
-  roofline.clock_mhz  the graphics clock sampled while the timed block ran
-                      (amdsmi, where readable) and the fraction at that clock
 
 ``--sweep`` instead times every kernel configuration that accepts each shape
 of a size sweep (square 512^3 .. 8192^3, few-row products against the HBM
@@ -175,48 +173,6 @@ def parity_of(c_gpu, C64, amax: float, bmax: float, out_dtype: str, K: int) -> d
     return {"ok": bool(rep["ok"]), "rows": int(rows), "outputs": int(rep["n"]), "n_bad": rep["n_bad"],
             "max_rel_err": rep["max_rel_err"], "n_not_bitequal": rep["n_not_bitequal"],
             "rule": "|gpu - oracle| <= max(rtol*|oracle|, 1e-3*sqrt(K)*max|A|*max|B|), oracle rounded once"}
-
-
-class ClockSampler:
-    """The GPU's graphics clock (MHz) read through amdsmi's metrics table
-    while kernels run; every method returns None where that is not
-    available (no amdsmi, no permission, more than one device)."""
-
-    def __init__(self):
-        self.h = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            hs = amdsmi.amdsmi_get_processor_handles()
-            if len(hs) == 1:
-                self.amdsmi, self.h = amdsmi, hs[0]
-        except Exception:
-            self.h = None
-
-    def sample(self):
-        if self.h is None:
-            return None
-        try:
-            m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
-        except Exception:
-            return None
-        vals = []
-        for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
-            v = m.get(key)
-            if isinstance(v, (list, tuple)):
-                vals = [float(x) for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
-            elif isinstance(v, (int, float)) and 0 < v < 10000:
-                vals = [float(v)]
-            if vals:
-                return sum(vals) / len(vals)
-        return None
-
-    def close(self):
-        if self.h is not None:
-            try:
-                self.amdsmi.amdsmi_shut_down()
-            except Exception:
-                pass
 
 
 SWEEP_SQUARE = [512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192]
@@ -460,7 +416,6 @@ def main(argv=None) -> int:
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
 
-    clock = ClockSampler()
     if args.warmup is not None:
         for _ in range(args.warmup):
             step()
@@ -481,8 +436,7 @@ def main(argv=None) -> int:
 
     def timed_block():
         """K steps between two events on the kernels' stream, bracketed by
-        device synchronisations; returns (ms per step, wall seconds, clock
-        samples taken while the block ran)."""
+        device synchronisations; returns (ms per step, wall seconds)."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         ev0.record(stream)
@@ -493,17 +447,11 @@ def main(argv=None) -> int:
             for _ in range(args.steps):
                 step()
         ev1.record(stream)
-        mhz = []
-        while not ev1.query():
-            v = clock.sample()
-            if v is not None:
-                mhz.append(v)
-            time.sleep(2e-4)
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0, mhz
+        return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
 
     # the timed region: exactly K steps
-    ms, wall, mhz = timed_block()
+    ms, wall = timed_block()
     log(f"[bench] {args.steps} timed steps: {ms * 1e3:.1f} us/step (events), wall {wall:.3f} s")
     # the timing protocol of notebook "Triton tiled matmul", section
     # "Performance" (n_iter back-to-back calls, t = elapsed / n_iter), with
@@ -528,13 +476,6 @@ def main(argv=None) -> int:
         roofline = {"bound": "mfma" if w.dtype != "f32" else "alu",
                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}
-    if mhz:
-        # the fraction at the clock the GPU actually ran (the power limit
-        # lowers it below the 2.4 GHz the peak is quoted at)
-        clk = sum(mhz) / len(mhz)
-        roofline["clock_mhz"] = round(clk, 1)
-        roofline["frac_at_clock"] = round(roofline["frac"] * 2400.0 / clk, 4)
-    clock.close()
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),

@@ -97,6 +97,12 @@ const Entry kTable[] = {
     {{38, 64, 128, 64, 4, 256, 0x18, 1, 1, "fp8_64x128x64_adma", 1}, kFp8},
     // the 8-bit kernel at 192 x 256 x 64, A direct to LDS: partial last waves
     {{39, 192, 256, 64, 4, 256, 0x18, 1, 1, "fp8_192x256x64_adma", 1}, kFp8},
+    // the default 256 x 256 configuration (29) with other tile orders, for
+    // measuring the order's effect on cache reuse; never selected: the band
+    // height GROUP_M = 1 (row-major) and 8, and no XCD remap
+    {{40, 256, 256, 32, 1, 256, 0x6, 1, 1, "mfma16x16_256x256x32_g1_adma", 1}, kMfma16x16},
+    {{41, 256, 256, 32, 8, 256, 0x6, 1, 1, "mfma16x16_256x256x32_g8_adma", 1}, kMfma16x16},
+    {{42, 256, 256, 32, 4, 256, 0x6, 1, 0, "mfma16x16_256x256x32_noxcd_adma", 1}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -209,8 +215,7 @@ bool accepts(const Entry& e, const Problem& p)
 //  * otherwise the 16x16x32 kernel at 128 x 128, which gives 4x the tiles
 //    (2048^3: 842 TFLOP/s against 383 at 256 x 256);
 //  * each of these tiled choices in its variant with A loaded direct to
-//    LDS (configs 29-31) unless A and B together overflow the Infinity Cache
-//    (see the end of select).
+//    LDS (configs 29-31).
 // The 32x32x16 configurations and the 256 x 128 tiles were never the fastest
 // in the sweep and stay available through gemm_run_config.
 int select(const Problem& p)
@@ -290,13 +295,12 @@ int select(const Problem& p)
     const int64_t t192 = ((p.M + 191) / 192) * ((p.N + 255) / 256) * p.batch;
     const int64_t w256 = (t256 + 255) / 256, w192 = (t192 + 255) / 256;
     const bool rows192 = w192 * 80 < w256 * 95;
-    // A direct to LDS (one ring with B) unless the operands overflow the
-    // 256 MB Infinity Cache: then loads come from HBM and A's register path,
-    // which covers half a K-step more latency, was faster
-    // (8192 x 4096 x 14336: 1352 against 1310 TFLOP/s; 4096^3: 1245 against
-    // 1281-1284 the other way round)
-    const bool adma = (p.M * p.K + p.K * p.N) * in_bytes(p.dtype) * p.batch <= ((int64_t)256 << 20);
-    return rows192 ? (adma ? 31 : 28) : (adma ? 29 : 6);
+    // A direct to LDS (one ring with B), also where the operands overflow the
+    // 256 MB Infinity Cache: with its loads spread over the K-step it leads
+    // the A-through-registers configuration there too (bf16
+    // 8192 x 4096 x 14336: 676 against 709 us in the kernel trace; 4096^3:
+    // 105 against 110 us)
+    return rows192 ? 31 : 29;
 }
 
 // ---- split K (gemm_run_ws)

@@ -66,6 +66,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // c (+)= b-fragment x a-fragment over one 64-deep K-slice.  FMT 0: both
 // operands E4M3 (the instruction's default); FMT 1: both E5M2.
+// Inline-assembly MFMAs: the wait-state rules the schedule relies on are
+// those listed at the 16x16 kernel's MFMA definitions (gemm_mfma16x16.hip):
+// accumulator reads 19+ wait states after the last write (the epilogue's
+// s_nop waits), operands written only by LDS reads covered by the
+// compiler's s_waitcnt, source C either 0 or exactly the destination.
 template <int FMT> struct MfmaFp8;
 template <> struct MfmaFp8<0> {
     static __device__ __forceinline__ void acc(f32x16& c, const u32x8& b, const u32x8& a)
@@ -100,7 +105,7 @@ template <int BN> __device__ __forceinline__ int swz_b(int k)
 template <int FMT, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
 __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_kernel(
     const unsigned char* A, const unsigned char* B, __bf16* C,
-    int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
+    int M, int N, int K, int group_m, int xcd_remap, Batch bt, float* ws, int splits)
 {
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
     // with split K the batch axis of the tile order is the split (one product)
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, SPLIT ? splits : bt.count, group_m, true, b, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, SPLIT ? splits : bt.count, group_m, xcd_remap != 0, b, tm, tn);
     if constexpr (!SPLIT) {
         A += b * bt.sa;
         B += b * bt.sb;
@@ -449,26 +454,26 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
         if (a.splits > 1) {
             if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
                 hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, true, true>), dim3(tiles * a.splits), block,
-                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
             else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
                 hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, true, true>), dim3(tiles * a.splits), block,
-                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
             else
                 return hipErrorInvalidValue;
             return hipGetLastError();
         }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 256, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 192, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
@@ -477,10 +482,10 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     else if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                          \
         if (a.splits > 1)                                                                                \
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_, true>), dim3(tiles * a.splits), block, 0, \
-                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);  \
+                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);  \
         else                                                                                             \
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_, false>), grid, block, 0, a.stream, A, B, C, \
-                               a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);                            \
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);                            \
     }
     if (false) {}
     DGR_FP8(256, 256, 64)

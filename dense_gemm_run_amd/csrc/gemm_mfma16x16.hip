@@ -65,6 +65,19 @@
 namespace dgr {
 namespace {
 
+// The MFMAs below are inline assembly, so the compiler's hazard handling does
+// not see them.  The schedule relies on these wait-state rules of the CDNA
+// ISA for matrix (XDL) instructions, which the generated-code tests check:
+//  (1) a VALU or memory instruction may read an accumulator only P + 3 wait
+//      states after the last MFMA writing it (P passes, at most 16 here):
+//      the epilogue's s_nop waits and the order of the last K-step give 27
+//      or more;
+//  (2) sources A and B are written by LDS reads, whose data the compiler's
+//      own s_waitcnt before each MFMA covers (it sees the asm's register
+//      operands), into the register set the MFMAs in flight do not read; no
+//      VALU result reaches an MFMA operand within 5 wait states;
+//  (3) source C is either 0 (the first K-slice) or exactly the destination,
+//      of the same opcode, which the hardware orders by itself.
 template <typename T> struct Mfma16x16;
 template <> struct Mfma16x16<_Float16> {
     // c += b-fragment x a-fragment (16x16x32)
@@ -159,7 +172,7 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
 template <typename T, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
 __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const T* A, const T* B, T* C,
-    int M, int N, int K, int group_m, Batch bt, float* ws, int splits)
+    int M, int N, int K, int group_m, int xcd_remap, Batch bt, float* ws, int splits)
 {
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
     // with split K the batch axis of the tile order is the split (one product)
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, SPLIT ? splits : bt.count, group_m, true, b, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, SPLIT ? splits : bt.count, group_m, xcd_remap != 0, b, tm, tn);
     if constexpr (!SPLIT) {
         A += b * bt.sa;
         B += b * bt.sb;
@@ -501,7 +514,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     // ---- epilogue
     // The last row of tiles was written by the most recent MFMAs: give them
     // time to finish before any accumulator is read (the tiles of earlier
-    // rows are at least FN MFMAs old).
+    // rows are at least FN MFMAs old): 24 wait states, rule (1) at the MFMA
+    // definitions.
     static_assert(FN == 4 || FN == 8, "the wait below lists the last row's tiles");
     if constexpr (FN == 8)
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
@@ -556,26 +570,26 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
         if (a.splits > 1) {
             if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)
                 hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, true, true>), dim3(tiles * a.splits),
-                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
             else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 32)
                 hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 64, 128, 32, true, true>), dim3(tiles * a.splits),
-                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits);
+                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
             else
                 return hipErrorInvalidValue;
             return hipGetLastError();
         }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 256, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 192, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 64, 128, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
@@ -584,10 +598,10 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                                \
         if (a.splits > 1)                                                                                 \
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_, true>), dim3(tiles * a.splits), block, \
-                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, a.splits); \
+                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits); \
         else                                                                                              \
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_, false>), grid, block, 0, a.stream, A, B, \
-                               C, a.M, a.N, a.K, cfg.group_m, a.batch, a.ws, 1);                          \
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);                          \
         return hipGetLastError();                                                                         \
     }
     DGR_LAUNCH(256, 256, 32)

@@ -98,6 +98,10 @@ WORKLOADS: dict[str, Workload] = {w.name: w for w in [
              "16 tokens through a 4096 x 4096 projection (weights B [K, N])"),
     Workload("bf16_tokens128_128x4096x4096", 128, 4096, 4096, "bf16", "prefill", 17,
              "128 tokens through a 4096 x 4096 projection (weights B [K, N])"),
+    Workload("bf16_3072x3072x3072", 3072, 3072, 3072, "bf16", "normal_sqrtk", 18,
+             "square bf16 3072^3, N(0,1)/sqrt(K): 144 tiles of 256 x 256, a partial wave of the 256 CUs"),
+    Workload("f32_4096x4096x4096", 4096, 4096, 4096, "f32", "uniform", 19,
+             "square fp32 4096^3, U[-1,1): the fp32 path at a size where it is compute-bound"),
 ]}
 
 # Order in which the four prefill projections of one layer run.

@@ -135,7 +135,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(40))
+@pytest.mark.parametrize("cid", range(43))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -341,9 +341,10 @@ def test_192_row_tiles_where_256_leaves_a_partial_wave():
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 12288, 4096), (8192, 14336, 4096),
                     (5120, 5120, 5120)]:
         assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_256x256x32_adma", (M, N, K)
-    # operands beyond the 256 MB Infinity Cache: A through registers
-    assert name(A, Bb, Cb, 8192, 4096, 14336, 2) == "mfma16x16_256x256x32"
-    assert name(A, Bb, Cb, 6144, 6144, 16384, 2) == "mfma16x16_192x256x32"
+    # operands beyond the 256 MB Infinity Cache: A direct to LDS as well
+    assert name(A, Bb, Cb, 8192, 4096, 14336, 2) == "mfma16x16_256x256x32_adma"
+    assert name(A, Bb, Cb, 12288, 12288, 12288, 2) == "mfma16x16_256x256x32_adma"
+    assert name(A, Bb, Cb, 6144, 6144, 16384, 2) == "mfma16x16_192x256x32_adma"
     # fewer than 128 tiles: 128 x 128, A direct to LDS
     assert name(A, Bb, Cb, 2048, 2048, 2048, 1) == "mfma16x16_128x128x32_adma"
     info = dg.gemm_config_info(28)

@@ -247,3 +247,92 @@ def test_matrix_vector_kernel_structure(tmp_path):
     assert len(seen) == 2 * 4 * 4, seen
     sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", "\n".join(lines))]
     assert len(sizes) == 32 and all(x == 0 for x in sizes), sizes
+
+
+# ---------------------------------------------------------------- wait states around the MFMAs
+# The MFMAs are inline assembly, so the compiler's hazard recognizer does not
+# see them; the schedule relies on these rules of the CDNA3/CDNA4 ISA for
+# XDL (matrix) instructions, checked here on the generated code:
+#  * an MFMA with P passes needs P + 3 independent wait states between its
+#    last write of an accumulator and a VALU or memory instruction reading
+#    that accumulator; the MFMAs here have at most 16 passes, so 19;
+#  * a VALU write of a VGPR needs a few wait states before an MFMA reads it
+#    as source A or B (the fragments come from LDS reads, whose data the
+#    compiler's own s_waitcnt covers; VALU writes of an operand register
+#    must be further away than that small count);
+#  * an MFMA accumulating into the registers of an earlier MFMA of the same
+#    opcode (source C = destination, exactly overlapped) is ordered by the
+#    hardware; every other MFMA-to-MFMA register dependence is absent.
+ACC_READ_WAIT = 19
+VALU_TO_MFMA_WAIT = 5
+
+
+def _instructions(body):
+    return [l.strip() for l in body
+            if l.strip() and not l.strip().startswith((";", ".")) and not l.strip().split()[0].endswith(":")]
+
+
+def _regs(tok, kind):
+    m = re.match(kind + r"\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(kind + r"(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _operands(line):
+    parts = line.split(None, 1)
+    return [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
+
+
+def _wait_states(line):
+    ops = _operands(line)
+    return int(ops[0]) + 1 if line.split()[0] == "s_nop" else 1
+
+
+def test_accumulators_are_read_only_after_the_mfma_latency(kernels):
+    """Every non-MFMA read of an accumulator comes at least 19 wait states
+    after the last MFMA that wrote it (the epilogue's s_nop waits plus the
+    instructions before the read; the loop falls through into it)."""
+    for name, kn in kernels.items():
+        ins = _instructions(kn.body)
+        last_write, ws, worst = {}, 0, None
+        for l in ins:
+            op = l.split()[0]
+            ops = _operands(l)
+            if op.startswith("v_mfma"):
+                for r in _regs(ops[0], "a"):
+                    last_write[r] = ws
+            elif op != "s_nop":
+                for o in ops[1:]:
+                    for r in _regs(o, "a"):
+                        if r in last_write:
+                            d = ws - last_write.pop(r) - 1
+                            worst = d if worst is None else min(worst, d)
+            ws += _wait_states(l)
+        assert worst is not None and worst >= ACC_READ_WAIT, (name, worst)
+
+
+def test_mfma_operands_are_not_fresh_valu_results(kernels):
+    """Between the first and the last MFMA, no VALU instruction writes a
+    VGPR that an MFMA reads as source A or B within 5 wait states."""
+    for name, kn in kernels.items():
+        ins = _instructions(kn.body)
+        first = next(i for i, l in enumerate(ins) if l.startswith("v_mfma"))
+        last = max(i for i, l in enumerate(ins) if l.startswith("v_mfma"))
+        written, ws = {}, 0
+        for l in ins[first:last + 1]:
+            op = l.split()[0]
+            ops = _operands(l)
+            if op.startswith("v_mfma"):
+                for o in ops[1:3]:
+                    for r in _regs(o, "v"):
+                        if r in written:
+                            assert ws - written[r] - 1 >= VALU_TO_MFMA_WAIT, (name, l)
+            elif op.startswith("v_") and ops:
+                for r in _regs(ops[0], "v"):
+                    written[r] = ws
+            elif op.startswith(("ds_read", "buffer_load", "global_load")) and ops and " lds" not in l:
+                for r in _regs(ops[0], "v"):
+                    written.pop(r, None)
+            ws += _wait_states(l)
