@@ -68,7 +68,7 @@ def log(*a):
 # Kernel source of each configuration family (by configuration-name prefix).
 KERNEL_FILES = {"mfma16x16": "gemm_mfma16x16.hip", "mfma32x32": "gemm_mfma32x32.hip",
                 "fp8": "gemm_fp8.hip", "gemv": "gemm_gemv.hip", "generic": "gemm_generic.hip",
-                "skinny": "gemm_skinny.hip"}
+                "skinny": "gemm_skinny.hip", "fp32": "gemm_fp32.hip"}
 # What every kernel's code depends on besides its own file.
 SHARED_FILES = ["gemm_device.h", "gemm_internal.h"]
 
@@ -302,6 +302,8 @@ def main(argv=None) -> int:
     p.add_argument("--config", type=int, default=None, help="force a kernel configuration id")
     p.add_argument("--splits", type=int, default=1,
                    help="with --config: split K over this many workgroups per tile (gemm_run_ws_config)")
+    p.add_argument("--no-workspace", action="store_true",
+                   help="time gemm_run's own choice (no split K) also where gemm_run_ws would split")
     p.add_argument("--graph", type=int, default=0,
                    help="time K steps as K/G replays of a HIP graph of G captured steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -348,6 +350,8 @@ def main(argv=None) -> int:
     elif w.batch > 1:
         cid = dg.gemm_select_config_batched(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.batch,
                                             w.M, w.N, w.K, *strides, code)
+    elif args.no_workspace:
+        cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code)
     else:
         # what gemm_run_ws picks with an ample workspace (split K where it helps)
         cid, splits = dg.gemm_select_config_ws(a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N,
@@ -473,7 +477,8 @@ def main(argv=None) -> int:
         roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_GBPS, "unit": "GB/s",
                     "frac": round(gbps / HBM_GBPS, 4), "traffic": traffic}
     else:
-        roofline = {"bound": "mfma" if w.dtype != "f32" else "alu",
+        # (fp32 runs on the MFMA unit too: v_mfma_f32_16x16x4f32 / 32x32x2f32)
+        roofline = {"bound": "mfma",
                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(tflops / peak, 4), "traffic": traffic}
     out = {

@@ -30,7 +30,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5, kFp32 = 6 };
 
 struct Entry {
     Config cfg;
@@ -103,6 +103,12 @@ const Entry kTable[] = {
     {{40, 256, 256, 32, 1, 256, 0x6, 1, 1, "mfma16x16_256x256x32_g1_adma", 1}, kMfma16x16},
     {{41, 256, 256, 32, 8, 256, 0x6, 1, 1, "mfma16x16_256x256x32_g8_adma", 1}, kMfma16x16},
     {{42, 256, 256, 32, 4, 256, 0x6, 1, 0, "mfma16x16_256x256x32_noxcd_adma", 1}, kMfma16x16},
+    // few rows: strips with more K-steps of B in flight per CU (16 wavefronts
+    // on a 16-column strip; 32-column strips with 32-deep K-steps)
+    {{43, 16, 16, 32, 1, 1024, 0x6, 1, 1, "skinny_16x16x32_w16"}, kSkinny},
+    {{44, 16, 32, 32, 1, 512, 0x6, 1, 1, "skinny_16x32x32"}, kSkinny},
+    // fp32 on the MFMA unit (v_mfma_f32_16x16x4f32), 128 x 128 x 32 tiles
+    {{45, 128, 128, 32, 4, 256, 0x1, 1, 1, "fp32_128x128x32"}, kFp32},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -204,7 +210,8 @@ bool accepts(const Entry& e, const Problem& p)
 //    few dozen tiles (M = 16, N = K = 4096: 44 against 18 TFLOP/s) - up to
 //    32 rows with strips of 32 columns for N >= 8192, and from 33 rows only
 //    for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles were faster);
-//  * small (M*N*K*batch < 128^3), fp32 or unaligned: the generic kernel;
+//  * fp32 with 16-byte rows from 128^3 up: the fp32 MFMA kernel (config 45);
+//  * small (M*N*K*batch < 128^3), other fp32 or unaligned: the generic kernel;
 //  * at least 128 output tiles of 256 x 256 over the whole batch (half the
 //    256 CUs or more): the 16x16x32 kernel at 256 x 256.  At one wave of
 //    tiles it is 30-40 % faster than the 128 x 128 tile, and even at 144
@@ -221,7 +228,13 @@ bool accepts(const Entry& e, const Problem& p)
 int select(const Problem& p)
 {
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
-    if (p.dtype == kF32) return 0;
+    if (p.dtype == kF32) {
+        // fp32 on the MFMA unit for aligned rows from 128^3 up (1024^3: 28.6
+        // against 21.8 TFLOP/s on the generic kernel, 4096^3: 138 against 48;
+        // at 256^3 the two are even)
+        if (accepts(kTable[45], p) && p.M * p.N * p.K * p.batch >= (int64_t)128 * 128 * 128) return 45;
+        return 0;
+    }
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
         if (p.M <= 64 && p.N < 8192) {
@@ -445,6 +458,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
         if (err == hipSuccess && splits > 1) err = launch_reduce_splits(la);
         break;
     case kSkinny: err = launch_skinny(e.cfg, la); break;
+    case kFp32: err = launch_fp32(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

@@ -416,6 +416,8 @@ hipError_t launch_e(const Config& cfg, const LaunchArgs& a)
         DGR_LAUNCH(32, 32, 64, 4)
         DGR_LAUNCH(64, 32, 32, 4)
         DGR_LAUNCH(16, 16, 32, 8)
+        DGR_LAUNCH(16, 16, 32, 16)
+        DGR_LAUNCH(16, 32, 32, 8)
     } else {
         DGR_LAUNCH(16, 16, 128, 8)
         DGR_LAUNCH(32, 16, 128, 8)

@@ -336,3 +336,25 @@ def test_mfma_operands_are_not_fresh_valu_results(kernels):
                 for r in _regs(ops[0], "v"):
                     written.pop(r, None)
             ws += _wait_states(l)
+
+
+def test_fp32_kernel_structure(tmp_path):
+    """The fp32 MFMA kernel: no scratch, the 16x16x4 fp32 MFMA only, two
+    blocks of 4 x 4 tiles x 8 K-steps (256 MFMAs) per round of its loop, and
+    one barrier per block."""
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    out = tmp_path / "fp32.s"
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_fp32.hip"),
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
+    assert sizes == [0], sizes
+    ins = [l.strip() for l in text.split("\n") if l.strip() and not l.strip().startswith((";", "."))]
+    mfma = [l for l in ins if l.startswith("v_mfma")]
+    assert len(mfma) == 256 and all(l.startswith("v_mfma_f32_16x16x4_f32") for l in mfma)
+    # prologue barrier + one per block of the loop round
+    assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 3

@@ -22,18 +22,21 @@ def note(msg):
     sys.stdout.flush()
 
 
-# one shape per kernel family the selection reaches (with a workspace, as
-# gemm() runs them), and the strip kernels forced by name
-CASES = [(1000, 1000, 1000, "f16", None),        # 16x16x32 kernel at 64 x 128
-         (2048, 2048, 1024, "bf16", None),       # 16x16x32 kernel at 256 x 256
-         (16, 4096, 4096, "bf16", None),         # split K on 64 x 128 tiles
-         (16, 4096, 4096, "bf16", "skinny_16x16x32"),   # few-row strip kernel
-         (4096, 4, 4096, "bf16", None),          # matrix-vector kernel (K split over wavefronts)
-         (127, 255, 65, "f16", None),            # generic kernel
-         (1024, 1024, 2048, "fp8_e4m3", None),   # 8-bit kernel at 64 x 128
-         (32, 4096, 4096, "fp8_e5m2", None),     # 8-bit split K on 64 x 128 tiles
-         (32, 4096, 4096, "fp8_e5m2", "skinny8_32x32x128"),   # 8-bit strip kernel
-         (256, 4096, 4096, "bf16", None)]        # split K: partial sums in a workspace, then the sum
+# one shape per kernel family the selection reaches, through gemm_run, or
+# through gemm_run_ws where the last field asks for split K (the workspace
+# then comes from the graph's memory pool), and the strip kernels forced by
+# name
+CASES = [(1000, 1000, 1000, "f16", None, False),        # 16x16x32 kernel at 64 x 128
+         (2048, 2048, 1024, "bf16", None, False),       # 16x16x32 kernel at 256 x 256
+         (16, 4096, 4096, "bf16", None, True),          # split K on 64 x 128 tiles
+         (16, 4096, 4096, "bf16", None, False),         # few-row strip kernel (gemm_run's choice)
+         (4096, 4, 4096, "bf16", None, False),          # matrix-vector kernel (K split over wavefronts)
+         (127, 255, 65, "f16", None, False),            # generic kernel
+         (1024, 1024, 2048, "fp8_e4m3", None, False),   # 8-bit kernel at 64 x 128
+         (32, 4096, 4096, "fp8_e5m2", None, True),      # 8-bit split K on 64 x 128 tiles
+         (32, 4096, 4096, "fp8_e5m2", None, False),     # 8-bit strip kernel (gemm_run's choice)
+         (1024, 1024, 1024, "f32", None, False),        # fp32 MFMA kernel
+         (256, 4096, 4096, "bf16", None, True)]         # split K: partial sums in a workspace, then the sum
 
 
 def config_id(name):
@@ -43,18 +46,18 @@ def config_id(name):
 
 @pytest.mark.parametrize("case", CASES)
 def test_every_replay_matches_the_eager_call(case):
-    M, N, K, dtype, cname = case
+    M, N, K, dtype, cname, split_k = case
     cid = config_id(cname)
     note(f"[graph] {case}")
     A, B = make_operands(M, N, K, dtype, "normal", 800 + M)
     A2, _ = make_operands(M, N, K, dtype, "normal", 900 + M)
     a, b = A.cuda(), B.cuda()
     c = torch.empty((M, N), dtype=dg.out_dtype(a.dtype), device="cuda")
-    dg.gemm(a, b, out=c, config=cid)      # creates the handle outside the capture
+    dg.gemm(a, b, out=c, config=cid, split_k=split_k)      # creates the handle outside the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        dg.gemm(a, b, out=c, config=cid)
+        dg.gemm(a, b, out=c, config=cid, split_k=split_k)
     sources = [A, A2, A, A2]
     for r, src in enumerate(sources):
         a.copy_(src.cuda())               # eager work between replays
@@ -62,7 +65,7 @@ def test_every_replay_matches_the_eager_call(case):
         c.zero_()
         g.replay()
         torch.cuda.synchronize()
-        eager = dg.gemm(a, b, config=cid)
+        eager = dg.gemm(a, b, config=cid, split_k=split_k)
         torch.cuda.synchronize()
         same = torch.equal(c.view(torch.int16), eager.view(torch.int16))
         note(f"  replay {r}: identical to the eager call: {same}")

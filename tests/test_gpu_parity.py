@@ -147,7 +147,9 @@ def test_fp32_keeps_full_input_precision():
     # values with all 24 significand bits in use: a reduced-precision input
     # mode would be off by >1e-4 relative; the fp32 path must be within 1e-5
     # relative with no absolute floor
-    for shape in [(64, 64, 64), (130, 70, 257)]:
+    # (64^3 and the ragged shape run the generic kernel, 256 x 260 x 1024 the
+    # fp32 MFMA kernel)
+    for shape in [(64, 64, 64), (130, 70, 257), (256, 260, 1024)]:
         A, B = make_operands(shape[0], shape[1], shape[2], "f32", "fp32_fine", 21)
         C = run_gpu(A, B)
         check_full(A, B, "f32", C, use_floor=False)
@@ -274,6 +276,24 @@ def test_headline_workload_whole():
     dg.gemm(a, b, out=C)
     torch.cuda.synchronize()
     rep = check_full(A, B, w.dtype, C)
+    note(f"  {rep}")
+
+
+def test_fp32_workload_sampled():
+    """The square fp32 4096^3 product in the configuration gemm_run picks
+    (the fp32 MFMA kernel): whole rows and columns and 100,000 random points,
+    with fp32's 1e-5 relative tolerance."""
+    name = "f32_4096x4096x4096"
+    w = WORKLOADS[name]
+    A, B = workload_operands(name)
+    a, b = A.cuda(), B.cuda()
+    C = torch.empty((w.M, w.N), dtype=a.dtype, device="cuda")
+    cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), C.data_ptr(), w.M, w.N, w.K, DT_CODE["f32"])
+    note(f"[parity] full-size {name} config {cid} {dg.gemm_config_info(cid)['name']}")
+    assert dg.gemm_config_info(cid)["name"] == "fp32_128x128x32"
+    dg.gemm(a, b, out=C)
+    torch.cuda.synchronize()
+    rep = sampled_check(A, B, "f32", C, seed=w.seed)
     note(f"  {rep}")
 
 
