@@ -109,6 +109,9 @@ const Entry kTable[] = {
     {{44, 16, 32, 32, 1, 512, 0x6, 1, 1, "skinny_16x32x32"}, kSkinny},
     // fp32 on the MFMA unit (v_mfma_f32_16x16x4f32), 128 x 128 x 32 tiles
     {{45, 128, 128, 32, 4, 256, 0x1, 1, 1, "fp32_128x128x32"}, kFp32},
+    // the same at 64 x 128 and 64 x 64, for products with few 128 x 128 tiles
+    {{46, 64, 128, 32, 4, 256, 0x1, 1, 1, "fp32_64x128x32"}, kFp32},
+    {{47, 64, 64, 32, 4, 256, 0x1, 1, 1, "fp32_64x64x32"}, kFp32},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -210,7 +213,8 @@ bool accepts(const Entry& e, const Problem& p)
 //    few dozen tiles (M = 16, N = K = 4096: 44 against 18 TFLOP/s) - up to
 //    32 rows with strips of 32 columns for N >= 8192, and from 33 rows only
 //    for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles were faster);
-//  * fp32 with 16-byte rows from 128^3 up: the fp32 MFMA kernel (config 45);
+//  * fp32 with 16-byte rows from 128^3 up: the fp32 MFMA kernel (128 x 128
+//    tiles from 1024 of them, else 64 x 64);
 //  * small (M*N*K*batch < 128^3), other fp32 or unaligned: the generic kernel;
 //  * at least 128 output tiles of 256 x 256 over the whole batch (half the
 //    256 CUs or more): the 16x16x32 kernel at 256 x 256.  At one wave of
@@ -229,10 +233,13 @@ int select(const Problem& p)
 {
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
     if (p.dtype == kF32) {
-        // fp32 on the MFMA unit for aligned rows from 128^3 up (1024^3: 28.6
-        // against 21.8 TFLOP/s on the generic kernel, 4096^3: 138 against 48;
-        // at 256^3 the two are even)
-        if (accepts(kTable[45], p) && p.M * p.N * p.K * p.batch >= (int64_t)128 * 128 * 128) return 45;
+        // fp32 on the MFMA unit for aligned rows from 128^3 up: 128 x 128
+        // tiles from 1024 of them (4 per CU) over the batch, else 64 x 64
+        // (4096^3 sustained: 147.1 against 144.6 TFLOP/s on 64 x 64; 3072^3,
+        // 576 tiles: 141.8 against 104.6; 1024^3: 96.6 on 64 x 64 against
+        // 32.7 on 128 x 128 and 21.8 on the generic kernel)
+        if (accepts(kTable[45], p) && p.M * p.N * p.K * p.batch >= (int64_t)128 * 128 * 128)
+            return ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch >= 1024 ? 45 : 47;
         return 0;
     }
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {

@@ -12,7 +12,9 @@
 //
 //  * 128 x 128 tile, 4 wavefronts in 2 x 2, each owning 64 x 64 outputs as
 //    4 x 4 MFMA tiles of 16 x 16 (64 accumulator registers); two workgroups
-//    fit a CU, which hides one's barrier behind the other's MFMAs.
+//    fit a CU, which hides one's barrier behind the other's MFMAs.  Products
+//    with too few such tiles for the chip take 64 x 128 or 64 x 64 tiles
+//    (the latter four workgroups per CU).
 //  * K is walked in blocks of 32.  Within a block the 8 MFMAs of a tile take
 //    K in an order chosen for the operand reads: MFMA j gives lane group g
 //    (= lane/16) the K index 8g + j, so a lane's A values of a block are 8
@@ -25,9 +27,15 @@
 //  * Staging: global -> registers (16-byte buffer loads, one block ahead) ->
 //    LDS (two stages, one barrier per block).  A rows are padded to 36 floats
 //    (the two 16-byte reads of a fragment then hit 64 distinct banks across
-//    16 lanes); B stays [K][N], its 16-column groups XOR-ed by 16*((k/8)%4)
-//    so that the four K rows one 4-byte read gathers (k = 8g + j) land on
-//    distinct banks.
+//    16 lanes); B stays [K][N], its 16-column groups XOR-ed by 16*x(k) with
+//    x(k) = ((k/8) % 4) ^ (2*(k % 2)), so that the four K rows one 4-byte
+//    read gathers (k = 8g + j) land on distinct banks, and so do the four
+//    rows of the 32 lanes that a paired read (rows j and j+1 at once, which
+//    the compiler forms from two such reads) serves in one pass.
+//  * Each block's LDS writes and global loads (for the next block and the
+//    one after) are spread over its first 64 MFMAs and its fragment reads
+//    over the last 64, so that a wavefront issues MFMAs throughout the block
+//    and the other wavefront on its SIMD has little to cover.
 //  * Out-of-range 16-byte pieces read zeros through the buffer range check
 //    (the zero padding of chapter "Matrix Multiplication", section "The real
 //    tiled loop"); only rows < M and columns < N of C are written.
@@ -37,22 +45,32 @@
 namespace dgr {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int NW = 4;                       // wavefronts, 2 x 2
-constexpr int WM = BM / 2, WN = BN / 2;     // per-wavefront block
-constexpr int FM = WM / 16, FN = WN / 16;   // 16 x 16 tiles per wavefront
-constexpr int A_PITCH = BK + 4;             // floats per A row in LDS
-constexpr int A_FLOATS = BM * A_PITCH;
-constexpr int B_FLOATS = BK * BN;
-constexpr int LOADS = 4;                    // 16-byte loads per lane per block, of A and of B
+constexpr int BK = 32;
+constexpr int A_PITCH = BK + 4;   // floats per A row in LDS
 
-__device__ __forceinline__ int b_col(int k, int n) { return n ^ (16 * ((k >> 3) & 3)); }
+__device__ __forceinline__ int b_col(int k, int n) { return n ^ (16 * (((k >> 3) & 3) ^ ((k & 1) << 1))); }
 
-__global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const float* B, float* C, int M, int N,
-                                                           int K, int group_m, int xcd_remap, Batch bt)
+// BM x BN tiles (128 x 128, 64 x 128 or 64 x 64), 4 wavefronts in 2 x 2.
+template <int BM, int BN> struct Tile {
+    static constexpr int WM = BM / 2, WN = BN / 2;     // per-wavefront block
+    static constexpr int FM = WM / 16, FN = WN / 16;   // 16 x 16 tiles per wavefront
+    static constexpr int A_FLOATS = BM * A_PITCH, B_FLOATS = BK * BN;
+    static constexpr int AL = BM / 32, BL = BN / 32;   // 16-byte loads per lane per block
+    static constexpr int PB = BN / 4;                  // 16-byte pieces per B row
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256, (BM * BN <= 64 * 64 ? 4 : 2)) void gemm_fp32_kernel(const float* A, const float* B,
+                                                                                    float* C, int M, int N, int K,
+                                                                                    int group_m, int xcd_remap,
+                                                                                    Batch bt)
 {
-    __shared__ __attribute__((aligned(16))) float sa[2][A_FLOATS];
-    __shared__ __attribute__((aligned(16))) float sb[2][B_FLOATS];
+    using T = Tile<BM, BN>;
+    // (the launch bound: 4 workgroups per CU at 64 x 64, whose registers allow it, else 2)
+    constexpr int WM = T::WM, WN = T::WN, FM = T::FM, FN = T::FN, AL = T::AL, BL = T::BL, PB = T::PB;
+    static_assert(BN >= 64 && BN % 64 == 0, "the B swizzle permutes 64-column groups");
+    __shared__ __attribute__((aligned(16))) float sa[2][T::A_FLOATS];
+    __shared__ __attribute__((aligned(16))) float sb[2][T::B_FLOATS];
 
     typedef __attribute__((address_space(3))) float lds_float;
     auto lds_a = [&](int st) __attribute__((always_inline)) { return (lds_float*)sa[st]; };
@@ -71,19 +89,22 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * 4u);
     // A load i of a block: row t/8 + 32i, piece t%8 (4 floats at K 4*(t%8));
-    // B load i: K row t/32 + 8i, piece t%32 (columns 4*(t%32) .. +3).
-    unsigned a_off[LOADS];
-    int a_k[LOADS];
-    unsigned b_off[LOADS];
+    // B load i: K row t/PB + (256/PB)*i, piece t%PB (columns 4*(t%PB) .. +3).
+    unsigned a_off[AL];
+    int a_k[AL];
+    unsigned b_off[BL];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
+    for (int i = 0; i < AL; ++i) {
         const int row = t / 8 + 32 * i;
         a_k[i] = 4 * (t % 8);
         a_off[i] = (m0 + row) < M ? ((unsigned)(m0 + row) * (unsigned)K + (unsigned)a_k[i]) * 4u : kOOB;
-        const int k = t / 32 + 8 * i, col = n0 + 4 * (t % 32);
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+        const int k = t / PB + (256 / PB) * i, col = n0 + 4 * (t % PB);
         b_off[i] = col < N ? ((unsigned)k * (unsigned)N + (unsigned)col) * 4u : kOOB;
     }
-    u32x4 stage_a[LOADS], stage_b[LOADS];
+    u32x4 stage_a[AL], stage_b[BL];
     auto load_block = [&](int k0) __attribute__((always_inline)) {
         k0 = __builtin_amdgcn_readfirstlane(k0);
         const int krem = K - k0;
@@ -91,20 +112,24 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
         const __amdgpu_buffer_rsrc_t rb =
             make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 4u);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        for (int i = 0; i < AL; ++i) {
             const unsigned ao = a_k[i] < krem ? a_off[i] : kOOB;
             stage_a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, ao, k0 * 4, 0));
-            const unsigned bo = b_off[i];
-            stage_b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, bo, 0, 0));
         }
+#pragma unroll
+        for (int i = 0; i < BL; ++i)
+            stage_b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[i], 0, 0));
     };
     auto store_block = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
+        for (int i = 0; i < AL; ++i) {
             const int row = t / 8 + 32 * i;
             *(u32x4 __attribute__((address_space(3)))*)(lds_a(st) + row * A_PITCH + a_k[i]) = stage_a[i];
-            const int k = t / 32 + 8 * i;
-            *(u32x4 __attribute__((address_space(3)))*)(lds_b(st) + k * BN + b_col(k, 4 * (t % 32))) = stage_b[i];
+        }
+#pragma unroll
+        for (int i = 0; i < BL; ++i) {
+            const int k = t / PB + (256 / PB) * i;
+            *(u32x4 __attribute__((address_space(3)))*)(lds_b(st) + k * BN + b_col(k, 4 * (t % PB))) = stage_b[i];
         }
     };
 
@@ -155,7 +180,15 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
     // reading (block it-1's fragments) before block it-1's barrier; the loads
     // of block it+2; the barrier; block it+1's fragments -> the other set,
     // between the second half of the MFMAs.
+    // Scheduling groups (instruction classes of the compiler's interleave
+    // directive): MFMA, LDS read, LDS write, global read.
+    constexpr int kMfma = 0x008, kLdsRead = 0x100, kLdsWrite = 0x200, kVmemRead = 0x020;
+    constexpr int HALF = 4 * FM * FN;                          // MFMAs per half block
+    constexpr int PER_LOAD = (HALF + AL + BL - 1) / (AL + BL);  // MFMAs per LDS write + global load
+    constexpr int RGROUPS = HALF / 4, READS = 2 * FM + 8 * FN;  // reads: at most, before pairing
+    constexpr int PER_GROUP = (READS + RGROUPS - 1) / RGROUPS;  // LDS reads per 4 MFMAs
     auto block = [&](const int par, int it) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -164,6 +197,14 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
                 for (int bj = 0; bj < FN; ++bj) mfma(par, j, bi, bj);
         store_block(par ^ 1);
         load_block((it + 2) * BK);
+        // the LDS writes and global loads spread over the MFMAs
+#pragma unroll
+        for (int i = 0; i < AL + BL; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kLdsWrite, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kMfma, PER_LOAD, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // this wavefront's LDS writes done, then the barrier (no fence: the
         // loads of block it+2 stay in flight across it); the empty asm
         // statements keep LDS accesses on their side of it
@@ -171,6 +212,7 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         read_frags(par ^ 1, par ^ 1);
 #pragma unroll
         for (int j = 4; j < 8; ++j)
@@ -178,6 +220,13 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
             for (int bi = 0; bi < FM; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < FN; ++bj) mfma(par, j, bi, bj);
+        // the fragment reads of the next block spread over the MFMAs
+#pragma unroll
+        for (int i = 0; i < RGROUPS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kLdsRead, PER_GROUP, 0);
+            __builtin_amdgcn_sched_group_barrier(kMfma, 4, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
     // blocks rounded up to pairs: an extra block multiplies the zeros its
     // loads brought in
@@ -198,17 +247,24 @@ __global__ __launch_bounds__(256, 2) void gemm_fp32_kernel(const float* A, const
         }
 }
 
+template <int BM, int BN> hipError_t launch_tile(const LaunchArgs& a, const Config& cfg)
+{
+    const int tiles = cdiv_i(a.M, BM) * cdiv_i(a.N, BN);
+    hipLaunchKernelGGL((gemm_fp32_kernel<BM, BN>), dim3(tiles * a.batch.count), dim3(256), 0, a.stream,
+                       static_cast<const float*>(a.A), static_cast<const float*>(a.B), static_cast<float*>(a.C), a.M,
+                       a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fp32(const Config& cfg, const LaunchArgs& a)
 {
-    if (a.dtype != kF32 || cfg.bm != BM || cfg.bn != BN || cfg.bk != BK || cfg.threads != 256)
-        return hipErrorInvalidValue;
-    const int tiles = cdiv_i(a.M, BM) * cdiv_i(a.N, BN);
-    hipLaunchKernelGGL(gemm_fp32_kernel, dim3(tiles * a.batch.count), dim3(256), 0, a.stream,
-                       static_cast<const float*>(a.A), static_cast<const float*>(a.B), static_cast<float*>(a.C), a.M,
-                       a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch);
-    return hipGetLastError();
+    if (a.dtype != kF32 || cfg.bk != BK || cfg.threads != 256) return hipErrorInvalidValue;
+    if (cfg.bm == 128 && cfg.bn == 128) return launch_tile<128, 128>(a, cfg);
+    if (cfg.bm == 64 && cfg.bn == 128) return launch_tile<64, 128>(a, cfg);
+    if (cfg.bm == 64 && cfg.bn == 64) return launch_tile<64, 64>(a, cfg);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace dgr

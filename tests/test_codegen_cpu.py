@@ -339,9 +339,10 @@ def test_mfma_operands_are_not_fresh_valu_results(kernels):
 
 
 def test_fp32_kernel_structure(tmp_path):
-    """The fp32 MFMA kernel: no scratch, the 16x16x4 fp32 MFMA only, two
-    blocks of 4 x 4 tiles x 8 K-steps (256 MFMAs) per round of its loop, and
-    one barrier per block."""
+    """The fp32 MFMA kernels (128 x 128, 64 x 128 and 64 x 64 tiles): no
+    scratch, the 16x16x4 fp32 MFMA only, two blocks of FM x FN tiles x 8
+    K-steps per round of the loop (256, 128 and 64 MFMAs), and one barrier
+    per block besides the prologue's."""
     if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
     from dense_gemm_run_amd import build as lib_build
@@ -352,9 +353,15 @@ def test_fp32_kernel_structure(tmp_path):
     assert r.returncode == 0, r.stderr
     text = out.read_text()
     sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
-    assert sizes == [0], sizes
-    ins = [l.strip() for l in text.split("\n") if l.strip() and not l.strip().startswith((";", "."))]
-    mfma = [l for l in ins if l.startswith("v_mfma")]
-    assert len(mfma) == 256 and all(l.startswith("v_mfma_f32_16x16x4_f32") for l in mfma)
-    # prologue barrier + one per block of the loop round
-    assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 3
+    assert sizes == [0, 0, 0], sizes
+    bodies = {}
+    for m in re.finditer(r"^(_Z\S*gemm_fp32_kernelILi(\d+)ELi(\d+)E\S*):[^\n]*$(.*?)^\.Lfunc_end", text, re.M | re.S):
+        bodies[(int(m.group(2)), int(m.group(3)))] = m.group(4)
+    assert sorted(bodies) == [(64, 64), (64, 128), (128, 128)], sorted(bodies)
+    for (bm, bn), body in bodies.items():
+        ins = [l.strip() for l in body.split("\n") if l.strip() and not l.strip().startswith((";", "."))]
+        mfma = [l for l in ins if l.startswith("v_mfma")]
+        assert len(mfma) == 2 * 8 * (bm // 32) * (bn // 32), (bm, bn, len(mfma))
+        assert all(l.startswith("v_mfma_f32_16x16x4_f32") for l in mfma), (bm, bn)
+        # prologue barrier + one per block of the loop round
+        assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 3, (bm, bn)
