@@ -63,18 +63,18 @@ const Entry kTable[] = {
     // few rows: bm = rows of A per workgroup (all of M, normally), bn =
     // columns of the strip, bk = K per step; the wavefronts (threads / 64)
     // of a workgroup split K
-    {{15, 16, 16, 64, 1, 512, 0x6, 1, 1, "skinny_16x16x64"}, kSkinny},
-    {{16, 32, 16, 64, 1, 512, 0x6, 1, 1, "skinny_32x16x64"}, kSkinny},
-    {{17, 64, 16, 32, 1, 256, 0x6, 1, 1, "skinny_64x16x32"}, kSkinny},
-    {{18, 16, 32, 64, 1, 256, 0x6, 1, 1, "skinny_16x32x64"}, kSkinny},
-    {{19, 32, 32, 64, 1, 256, 0x6, 1, 1, "skinny_32x32x64"}, kSkinny},
-    {{20, 64, 32, 32, 1, 256, 0x6, 1, 1, "skinny_64x32x32"}, kSkinny},
-    {{21, 16, 16, 32, 1, 512, 0x6, 1, 1, "skinny_16x16x32"}, kSkinny},
+    {{15, 16, 16, 64, 2, 512, 0x6, 1, 1, "skinny_16x16x64"}, kSkinny},
+    {{16, 32, 16, 64, 2, 512, 0x6, 1, 1, "skinny_32x16x64"}, kSkinny},
+    {{17, 64, 16, 32, 2, 256, 0x6, 1, 1, "skinny_64x16x32"}, kSkinny},
+    {{18, 16, 32, 64, 2, 256, 0x6, 1, 1, "skinny_16x32x64"}, kSkinny},
+    {{19, 32, 32, 64, 2, 256, 0x6, 1, 1, "skinny_32x32x64"}, kSkinny},
+    {{20, 64, 32, 32, 2, 256, 0x6, 1, 1, "skinny_64x32x32"}, kSkinny},
+    {{21, 16, 16, 32, 2, 512, 0x6, 1, 1, "skinny_16x16x32"}, kSkinny},
     // the same for 8-bit inputs (bk in elements = bytes)
-    {{22, 16, 16, 128, 1, 512, 0x18, 1, 1, "skinny8_16x16x128"}, kSkinny},
-    {{23, 32, 16, 128, 1, 512, 0x18, 1, 1, "skinny8_32x16x128"}, kSkinny},
-    {{24, 16, 32, 128, 1, 256, 0x18, 1, 1, "skinny8_16x32x128"}, kSkinny},
-    {{25, 32, 32, 128, 1, 256, 0x18, 1, 1, "skinny8_32x32x128"}, kSkinny},
+    {{22, 16, 16, 128, 2, 512, 0x18, 1, 1, "skinny8_16x16x128"}, kSkinny},
+    {{23, 32, 16, 128, 2, 512, 0x18, 1, 1, "skinny8_32x16x128"}, kSkinny},
+    {{24, 16, 32, 128, 2, 256, 0x18, 1, 1, "skinny8_16x32x128"}, kSkinny},
+    {{25, 32, 32, 128, 2, 256, 0x18, 1, 1, "skinny8_32x32x128"}, kSkinny},
     // 8-bit tiles of 128 x 128 (two workgroups per CU)
     {{26, 128, 128, 64, 4, 256, 0x18, 1, 1, "fp8_128x128x64"}, kFp8},
     {{27, 128, 128, 128, 4, 256, 0x18, 1, 1, "fp8_128x128x128"}, kFp8},
@@ -105,8 +105,8 @@ const Entry kTable[] = {
     {{42, 256, 256, 32, 4, 256, 0x6, 1, 0, "mfma16x16_256x256x32_noxcd_adma", 1}, kMfma16x16},
     // few rows: strips with more K-steps of B in flight per CU (16 wavefronts
     // on a 16-column strip; 32-column strips with 32-deep K-steps)
-    {{43, 16, 16, 32, 1, 1024, 0x6, 1, 1, "skinny_16x16x32_w16"}, kSkinny},
-    {{44, 16, 32, 32, 1, 512, 0x6, 1, 1, "skinny_16x32x32"}, kSkinny},
+    {{43, 16, 16, 32, 2, 1024, 0x6, 1, 1, "skinny_16x16x32_w16"}, kSkinny},
+    {{44, 16, 32, 32, 2, 512, 0x6, 1, 1, "skinny_16x32x32"}, kSkinny},
     // fp32 on the MFMA unit (v_mfma_f32_16x16x4f32), 128 x 128 x 32 tiles
     {{45, 128, 128, 32, 4, 256, 0x1, 1, 1, "fp32_128x128x32"}, kFp32},
     // the same at 64 x 128 and 64 x 64, for products with few 128 x 128 tiles

@@ -33,7 +33,9 @@
 //    rounded (nearest even) and stored, skipping rows >= M.
 // Out-of-range pieces read zeros through the buffer range check, as in the
 // tiled kernels; workgroups are ordered so that the strips one XCD runs are
-// adjacent (they share the cache lines of B rows).
+// adjacent (they share the cache lines of B rows), and, where M takes two
+// row blocks, so that both row blocks of a strip run on one XCD (band height
+// 2: they read the same B strip through one L2).
 #include "gemm_internal.h"
 #include "gemm_device.h"
 
@@ -118,7 +120,7 @@ template <> struct Elem<E5M2> : Elem8<1> {};
 template <typename E, int BMS, int BN, int BK, int W>
 __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const unsigned char* A, const unsigned char* B,
                                                               typename Elem<E>::Out* C, int M, int N, int K,
-                                                              Batch bt)
+                                                              int group_m, Batch bt)
 {
     using Frag = typename Elem<E>::Frag;
     using Out = typename Elem<E>::Out;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_skinny_kernel(const unsigned c
 
     const int tiles_m = cdiv_i(M, BMS), tiles_n = cdiv_i(N, BN);
     int b, tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, 1, true, b, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
     A += b * bt.sa * ES;
     B += b * bt.sb * ES;
     C += b * bt.sc;
@@ -405,7 +407,7 @@ hipError_t launch_e(const Config& cfg, const LaunchArgs& a)
 #define DGR_LAUNCH(BMS_, BN_, BK_, W_)                                                                  \
     if (cfg.bm == BMS_ && cfg.bn == BN_ && cfg.bk == BK_ && cfg.threads == 64 * W_) {                  \
         hipLaunchKernelGGL((gemm_skinny_kernel<E, BMS_, BN_, BK_, W_>), dim3(tiles * a.batch.count),   \
-                           dim3(64 * W_), 0, a.stream, A, B, C, a.M, a.N, a.K, a.batch);               \
+                           dim3(64 * W_), 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, a.batch);  \
         return hipGetLastError();                                                                      \
     }
     if constexpr (Elem<E>::BYTES == 2) {
