@@ -50,7 +50,8 @@
 //  * A direct to LDS (ADMA, K-step 64): as in the 16x16x32 kernel, A's
 //    16-byte pieces go global -> LDS at the places the register path writes
 //    them, into the stage of B's ring for the same K-step (one LDS object per
-//    stage), issued after the barrier with B's.
+//    stage); a K-step's group of A and B loads is spread over the whole
+//    K-step, half after its barrier and half before the next one.
 //  * Split K (SPLIT): as in the 16x16x32 kernel, `splits` workgroups per
 //    tile walk disjoint ranges of K-steps and write their fp32 sums,
 //    unrounded, to their own M x N slice of a workspace; a second kernel adds
@@ -319,11 +320,28 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
     // ones issued after MFMA number pos are op_lo(pos) .. op_lo(pos+1)-1.
     auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
 
+    // ADMA: group it (A and B of K-step it+SB, into stage it % SB, which
+    // every wavefront finished reading before K-step it's barrier) is issued
+    // in two parts, as in the 16x16x32 kernel: loads 0 .. P-1 after K-step
+    // it's barrier, between the operand reads, and loads P .. LOADS-1 before
+    // K-step it+1's barrier, spread over its first MFMAs, so that the
+    // wavefronts do not queue a whole group each on the CU's load path at
+    // once.  The counted wait is unchanged: at barrier it, groups it-2 and
+    // it-1 are whole and group it has not started.
+    constexpr int P_ADMA = LOADS / 2;
+    auto load_group = [&](int st, int k0_in, int idx) __attribute__((always_inline)) {
+        if (idx < A_LOADS)
+            load_a_lds(st, k0_in, idx);
+        else
+            load_b(st, k0_in, idx - A_LOADS);
+    };
     auto kslice = [&](const int q, int it, const int sl, const bool first) __attribute__((always_inline)) {
         const int sta = ADMA ? q % SB : q & 1, stb = q % SB, set = (q * NS + sl) & 1;
         const int sta_next = ADMA ? (q + 1) % SB : sta ^ 1;
-        constexpr int NOPS1 = ADMA ? 0 : 2 * A_LOADS;
-        constexpr int LD2 = ADMA ? A_LOADS + B_LOADS : B_LOADS;   // loads after the barrier
+        // ops before the barrier: A writes and A loads (A through
+        // registers), or the second part of group it-1 (ADMA)
+        constexpr int NOPS1 = ADMA ? LOADS - P_ADMA : 2 * A_LOADS;
+        constexpr int LD2 = ADMA ? P_ADMA : B_LOADS;   // loads after the barrier
         constexpr int NOPS2 = LD2 + NR;
         auto mfma = [&](int xx) __attribute__((always_inline)) {
             if (first && sl == 0)
@@ -341,7 +359,15 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
                 for (int o = op_lo(xx, NR, NT); o < op_lo(xx + 1, NR, NT); ++o)
                     read_frag(set ^ 1, sta, stb, sl + 1, o);
             }
-            if constexpr (NOPS1 > 0) {
+            if constexpr (ADMA) {
+                // the second part of group it-1 (none in the first K-step: the
+                // prologue issued group -1 whole)
+                if (!first) {
+#pragma unroll
+                    for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o)
+                        load_group((q + SB - 1) % SB, (it - 1 + SB) * BK, P_ADMA + o);
+                }
+            } else {
 #pragma unroll
                 for (int o = op_lo(x, NOPS1, BAR); o < op_lo(x + 1, NOPS1, BAR); ++o) {
                     if (o < A_LOADS)
@@ -363,10 +389,16 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
             mfma(x - lo);
 #pragma unroll
             for (int o = op_lo(x - BAR, NOPS2, XS - BAR); o < op_lo(x + 1 - BAR, NOPS2, XS - BAR); ++o) {
-                if (ADMA && o < A_LOADS)
-                    load_a_lds(stb, (it + SB) * BK, o);
-                else if (o < LD2)
-                    load_b(stb, (it + SB) * BK, o - (ADMA ? A_LOADS : 0));
+                if constexpr (ADMA) {
+                    // loads 0 .. P-1 of group it at evenly spaced ops
+                    // (o = 0, NOPS2/P, ...), the operand reads in between
+                    const int nld = (o * P_ADMA) / NOPS2 + 1;   // loads at ops 0 .. o
+                    if (o == 0 || (o * P_ADMA) / NOPS2 != ((o - 1) * P_ADMA) / NOPS2)
+                        load_group(stb, (it + SB) * BK, nld - 1);
+                    else
+                        read_frag(((q + 1) * NS) & 1, sta_next, (q + 1) % SB, 0, o - nld);
+                } else if (o < LD2)
+                    load_b(stb, (it + SB) * BK, o);
                 else
                     read_frag(((q + 1) * NS) & 1, sta_next, (q + 1) % SB, 0, o - LD2);
             }
