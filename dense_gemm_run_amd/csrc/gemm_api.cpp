@@ -30,7 +30,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5, kFp32 = 6 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5, kFp32 = 6, kShortK = 7 };
 
 struct Entry {
     Config cfg;
@@ -112,6 +112,9 @@ const Entry kTable[] = {
     // the same at 64 x 128 and 64 x 64, for products with few 128 x 128 tiles
     {{46, 64, 128, 32, 4, 256, 0x1, 1, 1, "fp32_64x128x32"}, kFp32},
     {{47, 64, 64, 32, 4, 256, 0x1, 1, 1, "fp32_64x64x32"}, kFp32},
+    // short K (at most 128, bk = the K extent staged): persistent 128 x 128
+    // tiles, the next tile's loads in flight during the current one's stores
+    {{48, 128, 128, 128, 4, 256, 0x6, 1, 1, "shortk_128x128x128"}, kShortK},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -195,6 +198,7 @@ bool accepts(const Entry& e, const Problem& p)
         if (p.batch > 1 && (p.sa % per16 || p.sb % per16)) return false;
         return true;
     }
+    if (e.kind == kShortK && p.K > e.cfg.bk) return false;   // the whole K range is staged at once
     if (e.cfg.needs_vec_align) {
         // elements per 16 bytes of A and B rows, and of C rows
         const int64_t pi = 16 / in_bytes(p.dtype), po = 16 / out_bytes(p.dtype);
@@ -215,6 +219,8 @@ bool accepts(const Entry& e, const Problem& p)
 //    for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles were faster);
 //  * fp32 with 16-byte rows from 128^3 up: the fp32 MFMA kernel (128 x 128
 //    tiles from 1024 of them, else 64 x 64);
+//  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
+//    kernel (config 48);
 //  * small (M*N*K*batch < 128^3), other fp32 or unaligned: the generic kernel;
 //  * at least 128 output tiles of 256 x 256 over the whole batch (half the
 //    256 CUs or more): the 16x16x32 kernel at 256 x 256.  At one wave of
@@ -293,6 +299,14 @@ int select(const Problem& p)
         if (p.M <= 32) return wide ? 19 : 16;
         if (!wide) return p.M <= 64 ? 19 : 20;
     }
+    // At most 128 K and at least 1024 tiles of 128 x 128: the persistent
+    // short-K kernel, whose workgroups load their next tile while they store
+    // the current one (bf16, graph-timed: 64 x 2048^2 x 128 122.6 against
+    // 133.6 us on config 12; short bursts: 8192^2 x 128 32.2 against 35.8,
+    // 8192^2 x 32 29.8 against 34.1, 16 x 2048^2 x 64 30.8 against 32.9;
+    // 4096^2 x 128, 1024 tiles, even)
+    if (p.K <= 128 && accepts(kTable[48], p) && ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch >= 1024)
+        return 48;
     // At most 8 K-steps of 32: a workgroup is mostly its prologue and its C
     // stores, and the 128 x 128 tile with A through registers (several
     // workgroups per CU) overlaps one's stores with another's loads (bf16,
@@ -451,6 +465,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
                   Batch{(int)p.batch, p.sa, p.sb, p.sc}};
     la.splits = splits;
     la.ws = static_cast<float*>(ws);
+    la.cus = h->cu_count;
     hipError_t err = hipSuccess;
     switch (e.kind) {
     case kGeneric: err = launch_generic(e.cfg, la); break;
@@ -466,6 +481,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
         break;
     case kSkinny: err = launch_skinny(e.cfg, la); break;
     case kFp32: err = launch_fp32(e.cfg, la); break;
+    case kShortK: err = launch_shortk(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

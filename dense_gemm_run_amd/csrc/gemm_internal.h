@@ -88,6 +88,8 @@ struct LaunchArgs {
     // fp32 sums to its M x N slice of `ws`; 1 = the single-pass kernels
     int splits = 1;
     float* ws = nullptr;
+    // compute units of the device (persistent grids)
+    int cus = 0;
 };
 
 // Kernel launchers; each returns the hipError_t of the launch.
@@ -98,6 +100,7 @@ hipError_t launch_gemv(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_fp8(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_skinny(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_fp32(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_shortk(const Config& cfg, const LaunchArgs& a);
 // Second pass of split K: C = the rounded sum of the `splits` slices of ws.
 hipError_t launch_reduce_splits(const LaunchArgs& a);
 

@@ -135,7 +135,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(48))
+@pytest.mark.parametrize("cid", range(49))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -248,7 +248,7 @@ def test_batched_selection_counts_the_whole_batch():
     assert dg.gemm_config_info(odd)["needs_vec_align"] == 0
 
 
-@pytest.mark.parametrize("cid", [0, 2, 6, 9])
+@pytest.mark.parametrize("cid", [0, 2, 6, 9, 48])
 def test_batched_tile_order_is_a_bijection(cid):
     info = dg.gemm_config_info(cid)
     for M, N, batch in [(300, 700, 3), (1024, 1024, 8), (100, 100, 17)]:
@@ -460,15 +460,27 @@ def test_short_k_selects_128x128_tiles_with_a_through_registers():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
-    # at most 8 K-steps of 32 (16-bit) or 4 of 64 (8-bit)
-    for M, N, K in [(8192, 8192, 64), (8192, 8192, 256), (4096, 4096, 128), (2048, 2048, 208)]:
+    # at most 8 K-steps of 32 (16-bit) or 4 of 64 (8-bit); 16-bit products
+    # with K <= 128 over at least 1024 tiles of 128 x 128 take the persistent
+    # short-K kernel
+    for M, N, K in [(8192, 8192, 64), (4096, 4096, 128), (8192, 8192, 8)]:
+        for dt in (1, 2):
+            assert name(A, Bb, Cb, M, N, K, dt) == "shortk_128x128x128", (M, N, K, dt)
+    for M, N, K in [(8192, 8192, 136), (8192, 8192, 256), (2048, 2048, 208), (2048, 2048, 128),
+                    (4096, 3968, 128)]:
         for dt in (1, 2):
             assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_128x128x32", (M, N, K, dt)
+    for M, N, K in [(8192, 8192, 64), (8192, 8192, 256), (4096, 4096, 128), (2048, 2048, 208)]:
         for dt in (3, 4):
             assert name(A, Bb, Cb, M, N, K, dt) == "fp8_128x128x64", (M, N, K, dt)
     cid = dg.gemm_select_config_batched(A, Bb, Cb, 64, 2048, 2048, 128, 2048 * 128, 128 * 2048,
                                         2048 * 2048, 2)
-    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32"
+    assert dg.gemm_config_info(cid)["name"] == "shortk_128x128x128"
+    cid = dg.gemm_select_config_batched(A, Bb, Cb, 3, 2048, 2048, 128, 2048 * 128, 128 * 2048,
+                                        2048 * 2048, 2)
+    assert dg.gemm_config_info(cid)["name"] == "mfma16x16_128x128x32"   # 768 tiles
+    info = dg.gemm_config_info(48)
+    assert (info["bm"], info["bn"], info["bk"], info["dtype_mask"], info["threads"]) == (128, 128, 128, 6, 256)
     # from K = 264 on, the tile-count rules again
     assert name(A, Bb, Cb, 8192, 8192, 264, 2) == "mfma16x16_256x256x32_adma"
     assert name(A, Bb, Cb, 8192, 8192, 512, 3) == "fp8_256x256x64_adma"

@@ -365,3 +365,30 @@ def test_fp32_kernel_structure(tmp_path):
         assert all(l.startswith("v_mfma_f32_16x16x4_f32") for l in mfma), (bm, bn)
         # prologue barrier + one per block of the loop round
         assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 3, (bm, bn)
+
+
+def test_short_k_kernel_structure(tmp_path):
+    """The persistent short-K kernel (fp16 and bf16): no scratch, 64 MFMAs of
+    16x16x32 per tile (4 K-steps x 4 x 4 tiles), two barriers per tile (data
+    landed; operands read out of LDS), and only loads with the LDS destination
+    for A and B (their registers are never staged)."""
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    out = tmp_path / "shortk.s"
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_shortk.hip"),
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
+    assert sizes == [0, 0], sizes
+    bodies = re.findall(r"^_Z\S*gemm_shortk_kernel\S*:[^\n]*$(.*?)^\.Lfunc_end", text, re.M | re.S)
+    assert len(bodies) == 2
+    for body in bodies:
+        ins = [l.strip() for l in body.split("\n") if l.strip() and not l.strip().startswith((";", "."))]
+        mfma = [l for l in ins if l.startswith("v_mfma")]
+        assert len(mfma) == 64 and all(l.startswith("v_mfma_f32_16x16x32_") for l in mfma), len(mfma)
+        assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 2
+        loads = [l for l in ins if l.split()[0].startswith("buffer_load")]
+        assert loads and all(l.rstrip().endswith("lds") for l in loads), loads[:3]

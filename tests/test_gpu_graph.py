@@ -36,6 +36,7 @@ CASES = [(1000, 1000, 1000, "f16", None, False),        # 16x16x32 kernel at 64 
          (32, 4096, 4096, "fp8_e5m2", None, True),      # 8-bit split K on 64 x 128 tiles
          (32, 4096, 4096, "fp8_e5m2", None, False),     # 8-bit strip kernel (gemm_run's choice)
          (1024, 1024, 1024, "f32", None, False),        # fp32 MFMA kernel
+         (4096, 4096, 128, "bf16", None, False),        # persistent short-K kernel
          (256, 4096, 4096, "bf16", None, True)]         # split K: partial sums in a workspace, then the sum
 
 
