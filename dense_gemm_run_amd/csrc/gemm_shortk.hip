@@ -29,8 +29,9 @@
 //      B rows (one K each) are 256 bytes; 32-byte group c of row k sits at
 //      c ^ x(k), x(k) = (k % 4) | 4 * ((k / 8) % 2), so the 8 rows a half
 //      wavefront's transpose read touches land on 8 distinct groups.
-//  * All fragments of the tile are read (64 + 64 registers per lane), then a
-//    barrier frees LDS for the next tile's loads, then the 64 MFMAs.
+//  * Each K-step's MFMAs run while the next K-step's fragments are read;
+//    after the second-last K-step's MFMAs a barrier frees LDS for the next
+//    tile's loads.
 //  * Epilogue: each wavefront rounds (nearest even) and stages 16 rows of its
 //    block at a time in an LDS area of its own (not the operand buffers,
 //    which the next tile's loads are filling), reads them back as whole
@@ -146,32 +147,37 @@ __global__ __launch_bounds__(256, 2) void gemm_shortk_kernel(const T* A, const T
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         u32x4 fa[KS][4], fb[KS][4];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        auto read_step = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) fa[s][i] = read_a(s, i);
 #pragma unroll
             for (int j = 0; j < 4; ++j) fb[s][j] = read_b(s, j);
-        }
-        // every wavefront has read the tile out of LDS: the next tile's loads
-        // may overwrite it
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (t + (int)gridDim.x < total) issue(t + gridDim.x);
-
+        };
         f32x4 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // K-step s's MFMAs run while K-step s+1's operands are read; after
+        // the MFMAs of the second-last K-step (the last reads long issued)
+        // every wavefront has read the tile out of LDS, and the next tile's
+        // loads may overwrite it
+        read_step(0);
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) {
+            if (s + 1 < KS) read_step(s + 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::run(fb[s][j], fa[s][i], acc[i][j]);
+            if (s == KS - 2) {
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                if (t + (int)gridDim.x < total) issue(t + gridDim.x);
+            }
+        }
 
         // epilogue: 16 rows (tile row bi) at a time through the staging area;
         // logical 16-byte piece p of staging row r sits at p ^ (r % 8)
