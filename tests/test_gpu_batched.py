@@ -60,6 +60,25 @@ def test_batched_every_configuration(dtype, shape):
         assert np.array_equal(ci.to("cpu", torch.float64).numpy(), ref_i)
 
 
+def test_batched_short_k_walks_several_tiles_per_workgroup():
+    """The persistent short-K kernel (config 48) on a batch of 60 ragged
+    matrices, 540 tiles of 128 x 128, more than its resident workgroups (two
+    per CU), so workgroups walk tiles of different matrices: whole output
+    against the oracle, and bit-exact on integer inputs."""
+    batch, M, N, K = 60, 300, 264, 72
+    cid = next(i for i in range(dg.gemm_config_count()) if dg.gemm_config_info(i)["name"] == "shortk_128x128x128")
+    A, B = make_batched_operands(batch, M, N, K, "bf16", "normal", 60)
+    Ai, Bi = make_batched_operands(batch, M, N, K, "bf16", "integers", 61)
+    note(f"[batched] short-K persistent {(batch, M, N, K)}")
+    c = dg.gemm_batched(A.cuda(), B.cuda(), config=cid)
+    torch.cuda.synchronize()
+    check_batch(A, B, "bf16", c)
+    ci = dg.gemm_batched(Ai.cuda(), Bi.cuda(), config=cid)
+    torch.cuda.synchronize()
+    ref_i, _ = gemm64.reference_batched(Ai, Bi, "bf16")
+    assert np.array_equal(ci.to("cpu", torch.float64).numpy(), ref_i)
+
+
 @pytest.mark.parametrize("shared", ["a", "b"])
 def test_batched_shared_operand(shared):
     batch, M, N, K = 6, 384, 512, 96

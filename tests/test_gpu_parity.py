@@ -338,3 +338,24 @@ def test_partial_wave_shapes_in_the_192_row_tiles(shape):
     torch.cuda.synchronize()
     rep = sampled_check(A, B, "bf16", C, seed=M)
     note(f"  {rep}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_short_k_kernel_walks_several_tiles_per_workgroup(dtype):
+    """The persistent short-K kernel (config 48) on a ragged product with more
+    128 x 128 tiles (24 x 23 = 552) than its resident workgroups (two per CU):
+    workgroups walk several tiles, loading the next one during the current
+    one's stores; K = 104 is zero-padded to the staged 128.  Whole output
+    against the oracle, and bit-exact on integer inputs."""
+    M, N, K = 3000, 2904, 104
+    cid = next(i for i in range(dg.gemm_config_count()) if dg.gemm_config_info(i)["name"] == "shortk_128x128x128")
+    A, B = make_operands(M, N, K, dtype, "normal", 48)
+    note(f"[parity] short-K persistent {dtype} {(M, N, K)}")
+    c = dg.gemm(A.cuda(), B.cuda(), config=cid)
+    torch.cuda.synchronize()
+    check_full(A, B, dtype, c)
+    Ai, Bi = make_operands(M, N, K, dtype, "integers", 49)
+    ci = dg.gemm(Ai.cuda(), Bi.cuda(), config=cid)
+    torch.cuda.synchronize()
+    ref, _ = gemm64.reference(Ai, Bi, dtype)
+    assert np.array_equal(ci.to("cpu", torch.float64).numpy(), ref)
