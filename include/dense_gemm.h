@@ -211,7 +211,8 @@ gemm_status_t gemm_check_args_batched(const void* A, const void* B, const void* 
  * and which element types and alignments it accepts. */
 typedef struct gemm_config_info {
     int32_t id;
-    int32_t bm, bn, bk;        /* output tile and K-step */
+    int32_t bm, bn, bk;        /* output tile and K-step (the persistent short-K configuration: the largest
+                                * K it accepts, staged whole) */
     int32_t group_m;           /* tile-rows walked before moving right */
     int32_t threads;           /* workgroup size */
     int32_t dtype_mask;        /* bit d set: accepts gemm_dtype_t d */
@@ -240,7 +241,9 @@ int32_t gemm_select_config_batched(const void* A, const void* B, const void* C, 
 
 /* Output tile (tile_m, tile_n) computed by workgroup `block` of
  * configuration `id` for an M x N output, evaluated on the host with the
- * same function the kernels use.  Used to test the tile order. */
+ * same function the kernels use.  Used to test the tile order.  (For the
+ * persistent short-K configuration `block` indexes the walk of tiles: its
+ * workgroup g of G takes indices g, g + G, g + 2G, ...) */
 gemm_status_t gemm_tile_of_block(int32_t id, int64_t M, int64_t N, int64_t block,
                                  int64_t* tile_m, int64_t* tile_n);
 
