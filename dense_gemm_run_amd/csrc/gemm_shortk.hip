@@ -33,7 +33,8 @@
 //    after the second-last K-step's MFMAs a barrier frees LDS for the next
 //    tile's loads.
 //  * Epilogue: each wavefront rounds (nearest even) and stages 16 rows of its
-//    block at a time in an LDS area of its own (not the operand buffers,
+//    block at a time in an LDS area of its own (16-byte pieces XOR-ed by
+//    (row / 2) % 8) (not the operand buffers,
 //    which the next tile's loads are filling), reads them back as whole
 //    128-byte row segments and stores them, skipping rows >= M and columns
 //    >= N.
@@ -180,7 +181,10 @@ __global__ __launch_bounds__(256, 2) void gemm_shortk_kernel(const T* A, const T
         }
 
         // epilogue: 16 rows (tile row bi) at a time through the staging area;
-        // logical 16-byte piece p of staging row r sits at p ^ (r % 8)
+        // logical 16-byte piece p of staging row r sits at p ^ ((r / 2) % 8):
+        // rows of 128 bytes put even and odd rows on the two bank halves, and
+        // the 8 rows of each parity that one pass of 8-byte writes touches
+        // (same logical piece) land on 8 distinct pieces
         int b, tm, tn;
         tile_of_block(t, tiles_m, tiles_n, bt.count, group_m, true, b, tm, tn);
         T* Cb = C + b * bt.sc;
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void gemm_shortk_kernel(const T* A, const T
                 u32x2 v;
                 v[0] = pack2<T>(acc[bi][bj][0], acc[bi][bj][1]);
                 v[1] = pack2<T>(acc[bi][bj][2], acc[bi][bj][3]);
-                const int p = (2 * bj + (g >> 1)) ^ (r16 & 7);
+                const int p = (2 * bj + (g >> 1)) ^ ((r16 >> 1) & 7);
                 *(lds_u32x2*)(stg + r16 * 128 + p * 16 + (g & 1) * 8) = v;
             }
             asm volatile("" ::: "memory");
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void gemm_shortk_kernel(const T* A, const T
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int r = 8 * h + (lane >> 3), pl = lane & 7;
-                const u32x4 v = *(const lds_u32x4*)(stg + r * 128 + (pl ^ (r & 7)) * 16);
+                const u32x4 v = *(const lds_u32x4*)(stg + r * 128 + (pl ^ ((r >> 1) & 7)) * 16);
                 const int row = row0 + 16 * bi + r, col = col0 + 8 * pl;
                 if (row < M && col < N) __builtin_nontemporal_store(v, (u32x4*)(Cb + (size_t)row * N + col));
             }
