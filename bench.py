@@ -35,6 +35,10 @@ Prints one JSON line (stdout):
                       output (all rows at 4096^3), with the acceptance rule of
                       the tests
   repeats/median/min  five blocks of K steps: per-step times, median, minimum
+  clock               the shader clock sampled inside one more product
+                      (gemm_run_clocked) right after each block, and the
+                      median block's fraction of the peak scaled to the
+                      median clock (single products through gemm_run only)
 
 ``--sweep`` instead times every kernel configuration that accepts each shape
 of a size sweep (square 512^3 .. 8192^3, few-row products against the HBM
@@ -437,6 +441,12 @@ def main(argv=None) -> int:
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    # clock samples: one more product after each block (outside the timed
+    # interval), through gemm_run_clocked, whose MFMA tile kernels sample the
+    # shader clock from inside; only where a step is a plain gemm_run
+    clocked = args.config is None and w.batch == 1 and splits == 1
+    clk = torch.zeros(4, dtype=torch.int64, device=dev)
+    clocks = []
 
     def timed_block():
         """K steps between two events on the kernels' stream, bracketed by
@@ -451,7 +461,15 @@ def main(argv=None) -> int:
             for _ in range(args.steps):
                 step()
         ev1.record(stream)
+        if clocked:
+            clk.zero_()
+            dg.gemm_run_clocked(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), w.M, w.N, w.K, code,
+                                clk.data_ptr(), stream.cuda_stream)
         torch.cuda.synchronize()
+        if clocked:
+            c0, c1, r0, r1 = clk.tolist()
+            if c1 > c0 and r1 > r0:
+                clocks.append(100.0 * (c1 - c0) / (r1 - r0))
         return ev0.elapsed_time(ev1) / args.steps, time.perf_counter() - t0
 
     # the timed region: exactly K steps
@@ -505,6 +523,17 @@ def main(argv=None) -> int:
         "wall_s_timed_region": round(wall, 4),
         "launch": launch,
     }
+    if clocks:
+        # the shader clock inside one product launched right after each
+        # block; the median block's rate against the peak scaled to the
+        # median clock separates the kernel's efficiency from the clock the
+        # board's power limit allows
+        clk_med = sorted(clocks)[len(clocks) // 2]
+        out["clock"] = {"mhz_in_product_after_each_block": [round(x, 1) for x in clocks],
+                        "median_mhz": round(clk_med, 1), "nominal_mhz": 2400.0}
+        if roofline["bound"] == "mfma":
+            out["clock"]["frac_at_median_clock"] = round(
+                w.flops / (med * 1e-3) / 1e12 / (peak * clk_med / 2400.0), 4)
     if args.cold:
         # the same product on copies of A and B that together exceed twice the
         # Infinity Cache, one copy per step in turn, so every step starts with

@@ -16,7 +16,8 @@ from ._lib import (GEMM_BF16, GEMM_F16, GEMM_F32, GEMM_FP8_E4M3, GEMM_FP8_E5M2, 
                    gemm_destroy, gemm_run, gemm_run_batched, gemm_run_batched_config,
                    gemm_run_config, gemm_run_ws, gemm_run_ws_config, gemm_select_config,
                    gemm_select_config_batched, gemm_select_config_ws, gemm_tile_of_block,
-                   gemm_tile_of_block_batched, gemm_workspace_size, gemm_run_noalloc, status_string)
+                   gemm_tile_of_block_batched, gemm_workspace_size, gemm_run_noalloc, gemm_run_clocked,
+                   status_string)
 
 __all__ = ["gemm", "gemm_batched", "Gemm", "gemm_create", "gemm_run", "gemm_run_config",
            "gemm_run_batched", "gemm_run_batched_config", "gemm_destroy",
@@ -24,7 +25,7 @@ __all__ = ["gemm", "gemm_batched", "Gemm", "gemm_create", "gemm_run", "gemm_run_
            "gemm_config_info", "gemm_select_config", "gemm_select_config_batched",
            "gemm_tile_of_block", "gemm_tile_of_block_batched", "status_string", "GemmError",
            "gemm_workspace_size", "gemm_run_ws", "gemm_run_ws_config", "gemm_select_config_ws",
-           "gemm_run_noalloc",
+           "gemm_run_noalloc", "gemm_run_clocked",
            "GEMM_F32", "GEMM_F16", "GEMM_BF16", "GEMM_FP8_E4M3", "GEMM_FP8_E5M2",
            "dtype_code", "out_dtype"]
 

@@ -68,6 +68,7 @@ SIGNATURES = {
     "gemm_select_config_ws": (_I32, [_VP, _VP, _VP, _I64, _I64, _I64, _I32, _I64,
                                      ctypes.POINTER(_I32)]),
     "gemm_run_noalloc": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _VP]),
+    "gemm_run_clocked": (_I32, [_VP, _VP, _VP, _VP, _I64, _I64, _I64, _I32, _VP, _VP]),
 }
 
 # Size of the library's own scratch used by gemm_run_noalloc (per device).
@@ -223,3 +224,10 @@ def gemm_run_noalloc(h, A: int, B: int, C: int, M: int, N: int, K: int, dtype: i
                      stream=None) -> None:
     """gemm_run_ws with the library's own scratch (allocates nothing)."""
     _check(lib().gemm_run_noalloc(h, A, B, C, M, N, K, dtype, stream), "gemm_run_noalloc")
+
+
+def gemm_run_clocked(h, A: int, B: int, C: int, M: int, N: int, K: int, dtype: int, clk: int,
+                     stream=None) -> None:
+    """gemm_run, with the MFMA tile kernels' clock samples written to clk
+    (device, 4 x uint64: clock0, clock1, real0, real1)."""
+    _check(lib().gemm_run_clocked(h, A, B, C, M, N, K, dtype, clk, stream), "gemm_run_clocked")

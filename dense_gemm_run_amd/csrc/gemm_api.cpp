@@ -453,7 +453,7 @@ gemm_status_t check_run(const Problem& p)
 }
 
 gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* stream, int splits = 1,
-                     void* ws = nullptr)
+                     void* ws = nullptr, unsigned long long* clk = nullptr)
 {
     if (!grid_fits(e, p, splits)) return GEMM_ERR_TOO_LARGE;
     if (!h) return GEMM_ERR_INVALID_VALUE;
@@ -466,6 +466,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
     la.splits = splits;
     la.ws = static_cast<float*>(ws);
     la.cus = h->cu_count;
+    la.clk = clk;
     hipError_t err = hipSuccess;
     switch (e.kind) {
     case kGeneric: err = launch_generic(e.cfg, la); break;
@@ -491,6 +492,14 @@ gemm_status_t run(gemm_handle_t h, const Problem& p, void* stream)
     const gemm_status_t st = check_args(p);
     if (st != GEMM_OK) return st;
     return launch(kTable[select(p)], h, p, stream);
+}
+
+gemm_status_t run_clocked(gemm_handle_t h, const Problem& p, void* clk, void* stream)
+{
+    const gemm_status_t st = check_args(p);
+    if (st != GEMM_OK) return st;
+    if (!clk || (reinterpret_cast<uintptr_t>(clk) & 7u)) return GEMM_ERR_INVALID_VALUE;
+    return launch(kTable[select(p)], h, p, stream, 1, nullptr, static_cast<unsigned long long*>(clk));
 }
 
 gemm_status_t run_ws(gemm_handle_t h, const Problem& p, void* ws, int64_t ws_bytes, void* stream)
@@ -730,6 +739,12 @@ gemm_status_t gemm_run_noalloc(gemm_handle_t h, const void* A, const void* B, vo
                                int64_t K, int32_t dtype, void* stream)
 {
     return run_noalloc(h, single(A, B, C, M, N, K, dtype), stream);
+}
+
+gemm_status_t gemm_run_clocked(gemm_handle_t h, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                               int64_t K, int32_t dtype, void* clk, void* stream)
+{
+    return run_clocked(h, single(A, B, C, M, N, K, dtype), clk, stream);
 }
 
 gemm_status_t gemm_run_ws_config(gemm_handle_t h, const void* A, const void* B, void* C, int64_t M,

@@ -36,6 +36,20 @@ constexpr unsigned waitcnt_vm(unsigned n)
 // ... and the one that waits for all of this wavefront's LDS operations.
 constexpr unsigned kWaitLgkm0 = 15u | (7u << 4) | (0u << 8) | (3u << 14);
 
+// Measurement aid: when `clk` is set, thread 0 of workgroup 0 records the
+// counter that ticks with the shader clock and the constant 100 MHz counter,
+// at entry (at = 0) and after its last store (at = 1), as clk = {clock0,
+// clock1, real0, real1}: the clock the kernel ran at, from inside it.
+__device__ __forceinline__ void clock_sample(unsigned long long* clk, int at)
+{
+    if (clk != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+        const unsigned long long c = __builtin_readcyclecounter();
+        const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+        clk[at] = c;
+        clk[2 + at] = r;
+    }
+}
+
 // Two fp32 values -> two 16-bit floats (round to nearest even), packed low
 // half first.
 template <typename T> __device__ __forceinline__ unsigned pack2(float a, float b);

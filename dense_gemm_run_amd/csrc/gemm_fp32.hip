@@ -63,8 +63,9 @@ template <int BM, int BN>
 __global__ __launch_bounds__(256, (BM * BN <= 64 * 64 ? 4 : 2)) void gemm_fp32_kernel(const float* A, const float* B,
                                                                                     float* C, int M, int N, int K,
                                                                                     int group_m, int xcd_remap,
-                                                                                    Batch bt)
+                                                                                    Batch bt, unsigned long long* clk)
 {
+    clock_sample(clk, 0);
     using T = Tile<BM, BN>;
     // (the launch bound: 4 workgroups per CU at 64 x 64, whose registers allow it, else 2)
     constexpr int WM = T::WM, WN = T::WN, FM = T::FM, FN = T::FN, AL = T::AL, BL = T::BL, PB = T::PB;
@@ -245,6 +246,7 @@ __global__ __launch_bounds__(256, (BM * BN <= 64 * 64 ? 4 : 2)) void gemm_fp32_k
             const int row = row0 + 16 * bi, col = col0 + 16 * bj;
             if (row < M && col < N) __builtin_nontemporal_store(acc[bi][bj], (f32x4*)(C + (size_t)row * N + col));
         }
+    clock_sample(clk, 1);
 }
 
 template <int BM, int BN> hipError_t launch_tile(const LaunchArgs& a, const Config& cfg)
@@ -252,7 +254,7 @@ template <int BM, int BN> hipError_t launch_tile(const LaunchArgs& a, const Conf
     const int tiles = cdiv_i(a.M, BM) * cdiv_i(a.N, BN);
     hipLaunchKernelGGL((gemm_fp32_kernel<BM, BN>), dim3(tiles * a.batch.count), dim3(256), 0, a.stream,
                        static_cast<const float*>(a.A), static_cast<const float*>(a.B), static_cast<float*>(a.C), a.M,
-                       a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch);
+                       a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
     return hipGetLastError();
 }
 

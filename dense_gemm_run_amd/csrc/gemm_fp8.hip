@@ -106,8 +106,9 @@ template <int BN> __device__ __forceinline__ int swz_b(int k)
 template <int FMT, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
 __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_kernel(
     const unsigned char* A, const unsigned char* B, __bf16* C,
-    int M, int N, int K, int group_m, int xcd_remap, Batch bt, float* ws, int splits)
+    int M, int N, int K, int group_m, int xcd_remap, Batch bt, float* ws, int splits, unsigned long long* clk)
 {
+    clock_sample(clk, 0);
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
     constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 tiles per wavefront
@@ -452,6 +453,7 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
                         v[3] = acc[bi][bj][4 * g + 3];
                         *(f32x4*)(P + (size_t)(r + 32 * bi) * N + c + 32 * bj + 8 * g) = v;
                     }
+        clock_sample(clk, 1);
         return;
     }
     __syncthreads();
@@ -471,6 +473,7 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
         store_c_block_32x32<__bf16, WM, WN, (A_BYTES < BLOCK ? A_BYTES : BLOCK)>(acc, cw, lane, row0, col0,
                                                                               M, N, C);
     }
+    clock_sample(clk, 1);
 }
 
 template <int FMT>
@@ -486,26 +489,26 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
         if (a.splits > 1) {
             if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
                 hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, true, true>), dim3(tiles * a.splits), block,
-                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
+                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits, a.clk);
             else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
                 hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, true, true>), dim3(tiles * a.splits), block,
-                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
+                                   0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits, a.clk);
             else
                 return hipErrorInvalidValue;
             return hipGetLastError();
         }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 256, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 128, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 64, 128, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 64)
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, 192, 256, 64, false, true>), grid, block, 0, a.stream, A, B, C,
-                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
@@ -514,10 +517,10 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     else if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                          \
         if (a.splits > 1)                                                                                \
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_, true>), dim3(tiles * a.splits), block, 0, \
-                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);  \
+                               a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits, a.clk);  \
         else                                                                                             \
             hipLaunchKernelGGL((gemm_fp8_kernel<FMT, BM_, BN_, BK_, false>), grid, block, 0, a.stream, A, B, C, \
-                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);                            \
+                               a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);                            \
     }
     if (false) {}
     DGR_FP8(256, 256, 64)

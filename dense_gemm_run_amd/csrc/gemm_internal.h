@@ -90,6 +90,8 @@ struct LaunchArgs {
     float* ws = nullptr;
     // compute units of the device (persistent grids)
     int cus = 0;
+    // measurement aid: clock samples of workgroup 0 (the MFMA tile kernels)
+    unsigned long long* clk = nullptr;
 };
 
 // Kernel launchers; each returns the hipError_t of the launch.

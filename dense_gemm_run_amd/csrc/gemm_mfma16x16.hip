@@ -172,8 +172,9 @@ __device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 1
 template <typename T, int BM, int BN, int BK, bool SPLIT, bool ADMA = false>
 __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     const T* A, const T* B, T* C,
-    int M, int N, int K, int group_m, int xcd_remap, Batch bt, float* ws, int splits)
+    int M, int N, int K, int group_m, int xcd_remap, Batch bt, float* ws, int splits, unsigned long long* clk)
 {
+    clock_sample(clk, 0);
     constexpr int NW = 4;                        // wavefronts, 2 x 2
     constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block
     constexpr int FM = WM / 16, FN = WN / 16;    // 16x16 tiles per wavefront
@@ -541,6 +542,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
             for (int bj = 0; bj < FN; ++bj)
                 if (r + 16 * bi < M && c + 16 * bj < N)
                     *(f32x4*)(P + (size_t)(r + 16 * bi) * N + c + 16 * bj) = acc[bi][bj];
+        clock_sample(clk, 1);
         return;
     }
     __syncthreads();
@@ -555,6 +557,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
         lds_byte* cw = wave < 2 ? a_stage(wave) : b_stage(wave - 2);
         store_c_block<T, WM, WN, CW>(acc, cw, lane, row0, col0, M, N, C);
     }
+    clock_sample(clk, 1);
 }
 
 template <typename T>
@@ -570,26 +573,26 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
         if (a.splits > 1) {
             if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)
                 hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, true, true>), dim3(tiles * a.splits),
-                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
+                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits, a.clk);
             else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 32)
                 hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 64, 128, 32, true, true>), dim3(tiles * a.splits),
-                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits);
+                                   block, 0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits, a.clk);
             else
                 return hipErrorInvalidValue;
             return hipGetLastError();
         }
         if (cfg.bm == 256 && cfg.bn == 256 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 256, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 128, 128, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else if (cfg.bm == 192 && cfg.bn == 256 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 192, 256, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else if (cfg.bm == 64 && cfg.bn == 128 && cfg.bk == 32)
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, 64, 128, 32, false, true>), grid, block, 0, a.stream, A, B,
-                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
@@ -598,10 +601,10 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     if (cfg.bm == BM_ && cfg.bn == BN_ && cfg.bk == BK_) {                                                \
         if (a.splits > 1)                                                                                 \
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_, true>), dim3(tiles * a.splits), block, \
-                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits); \
+                               0, a.stream, A, B, C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, a.splits, a.clk); \
         else                                                                                              \
             hipLaunchKernelGGL((gemm_mfma16x16_kernel<T, BM_, BN_, BK_, false>), grid, block, 0, a.stream, A, B, \
-                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1);                          \
+                               C, a.M, a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.ws, 1, a.clk);                          \
         return hipGetLastError();                                                                         \
     }
     DGR_LAUNCH(256, 256, 32)

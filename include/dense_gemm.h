@@ -184,6 +184,28 @@ gemm_status_t gemm_run_ws(gemm_handle_t h, const void* A, const void* B, void* C
 gemm_status_t gemm_run_noalloc(gemm_handle_t h, const void* A, const void* B, void* C,
                                int64_t M, int64_t N, int64_t K, int32_t dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid: the clock a product ran at, which the fraction of the
+ * nominal peak needs beside it (notebook "Triton tiled matmul", section
+ * "Performance"; under the board's power limit the shader clock of a long
+ * MFMA-bound product sits well below the nominal 2.4 GHz, and it moves within
+ * microseconds of the load changing, so it has to be read from inside the
+ * kernel).
+ *
+ * gemm_run_clocked is gemm_run (same selection, kernels and result), except
+ * that in the MFMA tile kernels (16-bit, 8-bit and fp32 inputs) thread 0 of
+ * workgroup 0 samples the counter that ticks with the shader clock and the
+ * constant 100 MHz counter at entry and after its last store, and writes
+ * clk = {clock0, clock1, real0, real1}: the shader clock in MHz is
+ * 100 * (clock1 - clock0) / (real1 - real0).  The other kernels (generic,
+ * strip, matrix-vector, short-K) leave clk untouched, so a caller clears it
+ * first.  clk: device memory on the handle's device, 8-byte aligned,
+ * 4 x uint64.  Errors as gemm_run, and GEMM_ERR_INVALID_VALUE for a NULL or
+ * misaligned clk.
+ * ------------------------------------------------------------------------- */
+gemm_status_t gemm_run_clocked(gemm_handle_t h, const void* A, const void* B, void* C,
+                               int64_t M, int64_t N, int64_t K, int32_t dtype, void* clk, void* stream);
+
 /* Release a handle.  NULL is accepted and ignored.  No work may still be
  * using the handle (enqueued work does not refer to it). */
 gemm_status_t gemm_destroy(gemm_handle_t h);

@@ -553,3 +553,13 @@ def test_fp32_selects_the_mfma_kernel_for_aligned_rows():
     assert name(A + 4, Bb, Cb, 1024, 1024, 1024, 0) == "generic_64x64"   # A not 16-byte aligned
     info = dg.gemm_config_info(45)
     assert (info["bm"], info["bn"], info["bk"], info["dtype_mask"], info["threads"]) == (128, 128, 32, 1, 256)
+
+
+def test_clocked_run_checks_its_arguments_on_the_host():
+    L = _lib.lib()
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    assert L.gemm_run_clocked(None, A, Bb, Cb, 64, 64, 64, 1, None, None) == INVALID          # no clk
+    assert L.gemm_run_clocked(None, A, Bb, Cb, 64, 64, 64, 1, A + (1 << 35) + 4, None) == INVALID   # misaligned
+    assert L.gemm_run_clocked(None, A, Bb, Cb, 64, 64, 64, 1, A + (1 << 35), None) == INVALID       # no handle
+    assert L.gemm_run_clocked(None, A, Bb, Cb, 64, 64, 64, 9, A + (1 << 35), None) == BADTYPE

@@ -359,3 +359,40 @@ def test_short_k_kernel_walks_several_tiles_per_workgroup(dtype):
     torch.cuda.synchronize()
     ref, _ = gemm64.reference(Ai, Bi, dtype)
     assert np.array_equal(ci.to("cpu", torch.float64).numpy(), ref)
+
+
+def test_clocked_run_matches_gemm_run_and_reads_a_plausible_clock():
+    """gemm_run_clocked computes gemm_run's product bit for bit, and in the
+    MFMA tile kernels its clock samples give a shader clock between 0.5 and
+    2.5 GHz; a kernel without samples (the generic one) leaves clk as it
+    was."""
+    h = dg.gemm_create()
+    try:
+        stream = torch.cuda.current_stream().cuda_stream
+        for dtype, (M, N, K) in [("f16", (4096, 4096, 4096)), ("bf16", (1000, 1000, 1000)),
+                                 ("fp8_e4m3", (2048, 2048, 2048)), ("f32", (1024, 1024, 1024))]:
+            A, B = make_operands(M, N, K, dtype, "normal", 77)
+            a, b = A.cuda(), B.cuda()
+            c1 = dg.gemm(a, b)
+            c2 = torch.empty_like(c1)
+            clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+            dg.gemm_run_clocked(h, a.data_ptr(), b.data_ptr(), c2.data_ptr(), M, N, K, dg.dtype_code(a.dtype),
+                                clk.data_ptr(), stream)
+            torch.cuda.synchronize()
+            assert torch.equal(c1.view(torch.int8), c2.view(torch.int8)), dtype
+            c0, cc1, r0, r1 = clk.tolist()
+            assert cc1 > c0 > 0 and r1 > r0 > 0, (dtype, clk.tolist())
+            mhz = 100.0 * (cc1 - c0) / (r1 - r0)
+            note(f"[clock] {dtype} {(M, N, K)}: {mhz:.0f} MHz over {(r1 - r0) / 100:.1f} us")
+            assert 500 < mhz < 2500, (dtype, mhz)
+        # the generic kernel takes no samples
+        A, B = make_operands(127, 255, 65, "f16", "normal", 78)
+        a, b = A.cuda(), B.cuda()
+        c = torch.empty((127, 255), dtype=torch.float16, device="cuda")
+        clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+        dg.gemm_run_clocked(h, a.data_ptr(), b.data_ptr(), c.data_ptr(), 127, 255, 65, 1, clk.data_ptr(), stream)
+        torch.cuda.synchronize()
+        assert clk.tolist() == [0, 0, 0, 0]
+        check_full(A, B, "f16", c)
+    finally:
+        dg.gemm_destroy(h)
