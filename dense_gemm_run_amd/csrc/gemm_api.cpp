@@ -217,8 +217,8 @@ bool accepts(const Entry& e, const Problem& p)
 //    few dozen tiles (M = 16, N = K = 4096: 44 against 18 TFLOP/s) - up to
 //    32 rows with strips of 32 columns for N >= 8192, and from 33 rows only
 //    for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles were faster);
-//  * fp32 with 16-byte rows from 128^3 up: the fp32 MFMA kernel (128 x 128
-//    tiles from 1024 of them, else 64 x 64);
+//  * fp32 with 16-byte rows: the fp32 MFMA kernel (128 x 128 tiles from 1024
+//    of them, else 64 x 64);
 //  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
 //    kernel (config 48);
 //  * small (M*N*K*batch < 128^3), other fp32 or unaligned: the generic kernel;
@@ -239,12 +239,13 @@ int select(const Problem& p)
 {
     if (p.M == 0 || p.N == 0 || p.K == 0 || p.batch == 0) return 0;
     if (p.dtype == kF32) {
-        // fp32 on the MFMA unit for aligned rows from 128^3 up: 128 x 128
-        // tiles from 1024 of them (4 per CU) over the batch, else 64 x 64
-        // (4096^3 sustained: 147.1 against 144.6 TFLOP/s on 64 x 64; 3072^3,
-        // 576 tiles: 141.8 against 104.6; 1024^3: 96.6 on 64 x 64 against
-        // 32.7 on 128 x 128 and 21.8 on the generic kernel)
-        if (accepts(kTable[45], p) && p.M * p.N * p.K * p.batch >= (int64_t)128 * 128 * 128)
+        // fp32 on the MFMA unit for aligned rows: 128 x 128 tiles from 1024
+        // of them (4 per CU) over the batch, else 64 x 64 (4096^3 sustained:
+        // 147.1 against 144.6 TFLOP/s on 64 x 64; 3072^3, 576 tiles: 141.8
+        // against 104.6; 1024^3: 96.6 on 64 x 64 against 32.7 on 128 x 128
+        // and 21.8 on the generic kernel; 64^3, graph-timed: 3.5 against
+        // 6.7 us on the generic kernel)
+        if (accepts(kTable[45], p))
             return ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch >= 1024 ? 45 : 47;
         return 0;
     }

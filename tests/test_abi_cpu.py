@@ -120,8 +120,10 @@ def test_config_table():
 
 
 def test_selection_rules():
-    # the generic configuration takes anything small, ragged or unaligned
-    assert dg.gemm_select_config(A, B, C, 64, 64, 64, 0) == 0
+    # the generic configuration takes anything small (16-bit), ragged or
+    # unaligned; aligned fp32 rows run the fp32 MFMA kernel at any size
+    assert dg.gemm_select_config(A, B, C, 64, 64, 64, 1) == 0
+    assert dg.gemm_config_info(dg.gemm_select_config(A, B, C, 64, 64, 64, 0))["name"] == "fp32_64x64x32"
     assert dg.gemm_select_config(A, B, C, 127, 255, 65, 1) == 0
     assert dg.gemm_select_config(A + 2, B, C, 4096, 4096, 4096, 1) == 0   # misaligned A
     assert dg.gemm_select_config(A, B, C, 4096, 4096, 4094, 1) in (0,)   # K not a multiple of 8
@@ -536,19 +538,18 @@ def test_noalloc_entry_point_host_checks():
 
 
 def test_fp32_selects_the_mfma_kernel_for_aligned_rows():
-    """fp32 products with 16-byte rows (K and N multiples of 4) from 128^3 up
-    run the fp32 MFMA kernel, on 128 x 128 tiles from 1024 of them and on
-    64 x 64 tiles below; smaller, ragged or misaligned ones the generic
-    kernel."""
+    """fp32 products with 16-byte rows (K and N multiples of 4) run the fp32
+    MFMA kernel, on 128 x 128 tiles from 1024 of them and on 64 x 64 tiles
+    below; ragged or misaligned ones the generic kernel."""
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 128), (4096, 4096 - 124, 64)]:
         assert name(A, Bb, Cb, M, N, K, 0) == "fp32_128x128x32", (M, N, K)
     for M, N, K in [(3072, 3072, 3072), (4096, 4096 - 128, 64), (1024, 1024, 1024), (128, 128, 128),
-                    (8192, 4, 4096), (300, 1000, 8)]:
+                    (8192, 4, 4096), (300, 1000, 8), (64, 64, 64), (127, 128, 128), (1, 4, 4)]:
         assert name(A, Bb, Cb, M, N, K, 0) == "fp32_64x64x32", (M, N, K)
-    for M, N, K in [(64, 64, 64), (4096, 4096, 4094), (4096, 4094, 4096), (127, 128, 128)]:
+    for M, N, K in [(4096, 4096, 4094), (4096, 4094, 4096), (64, 62, 64), (3, 5, 7)]:
         assert name(A, Bb, Cb, M, N, K, 0) == "generic_64x64", (M, N, K)
     assert name(A + 4, Bb, Cb, 1024, 1024, 1024, 0) == "generic_64x64"   # A not 16-byte aligned
     info = dg.gemm_config_info(45)

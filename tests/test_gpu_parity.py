@@ -147,7 +147,7 @@ def test_fp32_keeps_full_input_precision():
     # values with all 24 significand bits in use: a reduced-precision input
     # mode would be off by >1e-4 relative; the fp32 path must be within 1e-5
     # relative with no absolute floor
-    # (64^3 and the ragged shape run the generic kernel, 256 x 260 x 1024 the
+    # (the ragged shape runs the generic kernel, 64^3 and 256 x 260 x 1024 the
     # fp32 MFMA kernel)
     for shape in [(64, 64, 64), (130, 70, 257), (256, 260, 1024)]:
         A, B = make_operands(shape[0], shape[1], shape[2], "f32", "fp32_fine", 21)
