@@ -105,14 +105,17 @@ __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
     f32x16 acc;
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-    for (int k0 = 0; k0 < K; k0 += BK) {
-        V8 av, bv;
+    // this lane's share of the A and B tiles of the K-step at k0
+    auto fetch = [&](int k0, V8& av, V8& bv) __attribute__((always_inline)) {
         for (int e = 0; e < 8; ++e) {
             const int ka = k0 + a_k + e;
             av[e] = (gm < M && ka < K) ? widen(A[(size_t)gm * K + ka]) : T(0.0f);
             const int kb = k0 + b_k + e;
             bv[e] = (kb < K && gn < N) ? widen(B[(size_t)kb * N + gn]) : T(0.0f);
         }
+    };
+    // fill the LDS tiles, multiply them, and free them for the next fill
+    auto step = [&](const V8& av, const V8& bv) __attribute__((always_inline)) {
         *reinterpret_cast<V8*>(&As[a_row * LDK + a_k]) = av;
         *reinterpret_cast<V8*>(&Bs[b_col * LDK + b_k]) = bv;
         __syncthreads();   // tile complete before anyone reads it
@@ -123,6 +126,26 @@ __global__ __launch_bounds__(kThreads) void gemm_generic16_kernel(
             acc = mfma16(a, b, acc);
         }
         __syncthreads();   // all reads done before the next fill overwrites the tile
+    };
+
+    constexpr int PRE = 4;
+    if (K <= PRE * BK) {
+        // short K: every K-step's share is fetched at once, so the product
+        // waits for memory once rather than once per K-step (K is the same
+        // for all lanes: every lane takes the same steps and barriers)
+        V8 av[PRE], bv[PRE];
+#pragma unroll
+        for (int s = 0; s < PRE; ++s)
+            if (s * BK < K) fetch(s * BK, av[s], bv[s]);
+#pragma unroll
+        for (int s = 0; s < PRE; ++s)
+            if (s * BK < K) step(av[s], bv[s]);
+    } else {
+        for (int k0 = 0; k0 < K; k0 += BK) {
+            V8 av, bv;
+            fetch(k0, av, bv);
+            step(av, bv);
+        }
     }
 
     const int col = n0 + wn * 32 + (lane & 31);
