@@ -174,7 +174,10 @@ def parity_of(c_gpu, C64, amax: float, bmax: float, out_dtype: str, K: int) -> d
     got = first[:rows].to("cpu", torch.float64).numpy()
     ref = gemm64.bits_to_f64(gemm64.round_to_bits(C64, out_dtype), out_dtype)
     rep = tolerance.compare(got, ref, out_dtype, K, amax, bmax)
+    # (max_rel_err is set by outputs near zero, which the absolute floor
+    # covers; max_abs_err against the floor is the telling figure)
     return {"ok": bool(rep["ok"]), "rows": int(rows), "outputs": int(rep["n"]), "n_bad": rep["n_bad"],
+            "max_abs_err": rep["max_abs_err"], "abs_floor": rep["floor"],
             "max_rel_err": rep["max_rel_err"], "n_not_bitequal": rep["n_not_bitequal"],
             "rule": "|gpu - oracle| <= max(rtol*|oracle|, 1e-3*sqrt(K)*max|A|*max|B|), oracle rounded once"}
 
