@@ -72,7 +72,8 @@ def log(*a):
 # Kernel source of each configuration family (by configuration-name prefix).
 KERNEL_FILES = {"mfma16x16": "gemm_mfma16x16.hip", "mfma32x32": "gemm_mfma32x32.hip",
                 "fp8": "gemm_fp8.hip", "gemv": "gemm_gemv.hip", "generic": "gemm_generic.hip",
-                "skinny": "gemm_skinny.hip", "fp32": "gemm_fp32.hip", "shortk": "gemm_shortk.hip"}
+                "skinny": "gemm_skinny.hip", "fp32": "gemm_fp32.hip", "shortk": "gemm_shortk.hip",
+                "fewrow": "gemm_fewrow.hip"}
 # What every kernel's code depends on besides its own file.
 SHARED_FILES = ["gemm_device.h", "gemm_internal.h"]
 

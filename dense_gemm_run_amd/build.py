@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libdense_gemm_run_amd.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["gemm_api.cpp", "gemm_generic.hip", "gemm_mfma32x32.hip", "gemm_mfma16x16.hip", "gemm_gemv.hip",
            "gemm_fp8.hip", "gemm_skinny.hip", "gemm_splitk.hip", "gemm_fp32.hip",
-           "gemm_shortk.hip"]
+           "gemm_shortk.hip", "gemm_fewrow.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -30,7 +30,7 @@ struct gemm_ctx {
 namespace dgr {
 namespace {
 
-enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5, kFp32 = 6, kShortK = 7 };
+enum Kind { kGeneric = 0, kMfma32x32 = 1, kMfma16x16 = 2, kGemv = 3, kFp8 = 4, kSkinny = 5, kFp32 = 6, kShortK = 7, kFewRow = 8 };
 
 struct Entry {
     Config cfg;
@@ -115,6 +115,14 @@ const Entry kTable[] = {
     // short K (at most 128, bk = the K extent staged): persistent 128 x 128
     // tiles, the next tile's loads in flight during the current one's stores
     {{48, 128, 128, 128, 4, 256, 0x6, 1, 1, "shortk_128x128x128"}, kShortK},
+    // few rows in one launch with A streamed beside B (bm = rows per
+    // workgroup, bn = strip columns, bk = K per step; each of the threads/64
+    // wavefronts owns a contiguous K range)
+    {{49, 16, 16, 32, 2, 512, 0x6, 1, 1, "fewrow_16x16x32"}, kFewRow},
+    {{50, 16, 16, 64, 2, 512, 0x6, 1, 1, "fewrow_16x16x64"}, kFewRow},
+    {{51, 16, 32, 32, 2, 512, 0x6, 1, 1, "fewrow_16x32x32"}, kFewRow},
+    {{52, 16, 16, 128, 2, 512, 0x18, 1, 1, "fewrow8_16x16x128"}, kFewRow},
+    {{53, 16, 32, 128, 2, 256, 0x18, 1, 1, "fewrow8_16x32x128"}, kFewRow},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -212,11 +220,13 @@ bool accepts(const Entry& e, const Problem& p)
 // Shape classes (measured with bench.py --sweep over square 512^3 .. 8192^3,
 // few-row products and the prefill projections):
 //  * N <= 4: the matrix-vector kernel (it streams A at HBM bandwidth);
-//  * M <= 128 (few rows, B streamed once): the split-K strip kernel, whose
-//    N/16 or N/32 workgroups fill the chip where the tiled kernels have a
-//    few dozen tiles (M = 16, N = K = 4096: 44 against 18 TFLOP/s) - up to
-//    32 rows with strips of 32 columns for N >= 8192, and from 33 rows only
-//    for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles were faster);
+//  * M <= 128 (few rows, B streamed once): kernels of N/16 or N/32
+//    workgroups, one per strip of B's columns, which fill the chip where the
+//    tiled kernels have a few dozen tiles (M = 16, N = K = 4096: 44 against
+//    18 TFLOP/s) - up to 32 rows the one-launch few-row kernel (A streamed
+//    beside B) below N = 12288, the 64 x 128 tiles above; from 33 rows the
+//    strip kernel for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles
+//    were faster);
 //  * fp32 with 16-byte rows: the fp32 MFMA kernel (128 x 128 tiles from 1024
 //    of them, else 64 x 64);
 //  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
@@ -251,11 +261,17 @@ int select(const Problem& p)
     }
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
-        if (p.M <= 64 && p.N < 8192) {
-            // few rows: the strip kernel (16-column strips up to 16 rows,
-            // 32 x 32 above; K >= 8192 keeps 16 columns for more strips)
-            if (p.M <= 16) return p.K >= 8192 ? 22 : 24;
-            return 25;
+        if (p.M <= 32 && p.N < 12288) {
+            // few rows: the one-launch few-row kernel, 32-column strips
+            // (16 columns for K >= 8192 up to 16 rows, for more strips).
+            // (E4M3, graph-timed: 1-16 x 4096 x 4096 5.9-6.0 us against
+            // 6.5-7.7 on the strip kernel; 24-32 rows 7.5-7.6 against 9.0-9.6;
+            // 16 x 4096 x 14336 24.9 against 27.1; 16 x 8192 x 4096 10.9
+            // against 12.2 on the 64 x 128 tiles.)  From 33 rows and from N =
+            // 12288 the tiled rules below pick the 64 x 128 tiles (48-64 x
+            // 4096 x 4096: 10.3-10.4 us against 11.1-11.2 on the strip
+            // kernel; 16 x 14336 x 4096: 14.2 against 17.9).
+            return p.M <= 16 && p.K >= 8192 ? 52 : 53;
         }
         // at most 4 K-steps of 64: 128 x 128 tiles with A through registers,
         // for the same reason as the 16-bit short-K rule below (E4M3,
@@ -292,12 +308,27 @@ int select(const Problem& p)
     if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
     if (p.M <= 128) {
-        // few rows: the split-K strip kernel, except for wide B (N >= 8192)
-        // from 33 rows up, where the 128 x 128 tiles already give enough
-        // workgroups
+        // Few rows.  Up to 32 rows: the one-launch few-row kernel (A streamed
+        // beside B), 16-column strips with 64-deep K-steps up to 16 rows
+        // below N = 8192 (32-column strips where K <= 2048 leaves each
+        // wavefront few steps), else 32-column strips; from N = 12288 (and
+        // K >= 1024) the 64 x 128 tiles instead, whose one pass already has
+        // enough workgroups.  (bf16, graph-timed: 1-16 x 4096 x 4096 7.7-8.8
+        // us against 8.9-12.0 on the strip kernel; 16 x 4096 x 14336 32.6
+        // against 37.2; 24 and 32 x 4096 x 4096 11.1 and 11.6 against 12.4
+        // and 13.1; 16 x 8192 x 4096 14.3 against 15.3; 16 x 14336 x 4096
+        // 23.2 on the tiles against 24.7 and 26.6.)  From 33 rows: the strip
+        // kernel, except for wide B (N >= 8192), where the 128 x 128 tiles
+        // already give enough workgroups.
         const bool wide = p.N >= 8192;
-        if (p.M <= 16) return wide ? 18 : (p.K >= 8192 ? 15 : 21);
-        if (p.M <= 32) return wide ? 19 : 16;
+        if (p.M <= 32) {
+            if (p.N >= 12288) {
+                if (p.K >= 1024) return 37;
+                return p.M <= 16 ? 18 : 19;
+            }
+            if (p.M <= 16 && !wide) return p.K <= 2048 && p.N >= 4096 ? 51 : 50;
+            return 51;
+        }
         if (!wide) return p.M <= 64 ? 19 : 20;
     }
     // At most 128 K and at least 1024 tiles of 128 x 128: the persistent
@@ -396,6 +427,12 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
     int cfg = -1, s = 1;
     if (p.dtype == kF16 || p.dtype == kBF16) {
         if (!accepts(kTable[kSplitConfigFew], p) || kTable[c].kind == kGemv) return c;
+        // the one-launch few-row kernel beats a split where K or B is small
+        // (bf16: 16 x 2048 x 2048 4.5 against 6.6 us with 4 splits, 16 x 4096
+        // x 2048 5.0 against 7.1, 16 x 2048 x 4096 6.3 against 7.0; 16 x 3072
+        // x 3072 7.9 against 7.1 and 16 x 4096 x 4096 8.8 against 8.2 the
+        // other way round)
+        if (kTable[c].kind == kFewRow && (p.K <= 2048 || (p.K <= 4096 && p.N <= 2048))) return c;
         const int64_t steps = (p.K + 31) / 32;
         const int64_t t = ((p.M + 63) / 64) * ((p.N + 127) / 128);
         if (steps < 64 || t > 160) return c;
@@ -403,6 +440,11 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
         s = split_count(t, steps, p.K, 32);
     } else if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[kSplitConfig8], p) || p.M > 128) return c;
+        // up to 16 rows with K and N at most 4096: the one-launch few-row
+        // kernel (E4M3: 16 x 4096 x 4096 6.0 against 6.5 us with 8 splits,
+        // 16 x 2048-3072 x 2048-4096 3.9-5.0 against 5.6-6.1; 1-8 rows x 4096
+        // x 4096 5.9-6.0 against 5.6-5.9, the one loss)
+        if (kTable[c].kind == kFewRow && p.M <= 16 && p.K <= 4096 && p.N <= 4096) return c;
         const int64_t steps = (p.K + 63) / 64;
         if (steps < 32) return c;
         cfg = kSplitConfig8;
@@ -484,6 +526,7 @@ gemm_status_t launch(const Entry& e, gemm_handle_t h, const Problem& p, void* st
     case kSkinny: err = launch_skinny(e.cfg, la); break;
     case kFp32: err = launch_fp32(e.cfg, la); break;
     case kShortK: err = launch_shortk(e.cfg, la); break;
+    case kFewRow: err = launch_fewrow(e.cfg, la); break;
     }
     return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

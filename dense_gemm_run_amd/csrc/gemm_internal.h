@@ -103,6 +103,7 @@ hipError_t launch_fp8(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_skinny(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_fp32(const Config& cfg, const LaunchArgs& a);
 hipError_t launch_shortk(const Config& cfg, const LaunchArgs& a);
+hipError_t launch_fewrow(const Config& cfg, const LaunchArgs& a);
 // Second pass of split K: C = the rounded sum of the `splits` slices of ws.
 hipError_t launch_reduce_splits(const LaunchArgs& a);
 

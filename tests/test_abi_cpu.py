@@ -137,7 +137,7 @@ def test_selection_rules():
         assert (info["dtype_mask"] >> dt) & 1
 
 
-@pytest.mark.parametrize("cid", range(49))
+@pytest.mark.parametrize("cid", range(64))
 def test_tile_order_is_a_bijection(cid):
     if cid >= dg.gemm_config_count():
         pytest.skip("no such configuration")
@@ -307,28 +307,38 @@ def test_8bit_inputs_select_their_kernels():
                                          1024 * 1024, 1024 * 1024 + 8, 3) in fp8_cfgs
 
 
-def test_few_rows_select_the_strip_kernel():
+def test_few_rows_select_the_few_row_kernels():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
-    for M, N, K in [(16, 4096, 4096), (1, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096),
-                    (128, 4096, 4096), (16, 14336, 4096), (16, 4096, 14336), (32, 14336, 4096)]:
+    # 16-bit: the one-launch few-row kernel up to 32 rows below N = 12288, the
+    # strip kernel for 33-128 rows of a narrow B, the 64 x 128 tiles for wide B
+    expect16 = {(16, 4096, 4096): "fewrow_16x16x64", (1, 4096, 4096): "fewrow_16x16x64",
+                (16, 4096, 14336): "fewrow_16x16x64", (16, 4096, 2048): "fewrow_16x32x32",
+                (16, 2048, 2048): "fewrow_16x16x64", (32, 4096, 4096): "fewrow_16x32x32",
+                (24, 4096, 4096): "fewrow_16x32x32", (16, 8192, 4096): "fewrow_16x32x32",
+                (16, 14336, 4096): "mfma16x16_64x128x32_adma", (32, 14336, 4096): "mfma16x16_64x128x32_adma",
+                (16, 14336, 512): "skinny_16x32x64", (64, 4096, 4096): "skinny_32x32x64",
+                (128, 4096, 4096): "skinny_64x32x32"}
+    for (M, N, K), want in expect16.items():
         for dt in (1, 2):
-            n = name(A, Bb, Cb, M, N, K, dt)
-            assert n.startswith("skinny"), (M, N, K, n)
-            info = dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb, M, N, K, dt))
-            assert info["bm"] >= min(M, 32) or M > 64
-    # wide B from 33 rows up, many rows, fp32, unaligned rows: not
+            assert name(A, Bb, Cb, M, N, K, dt) == want, (M, N, K, dt)
+    # wide B from 33 rows up, many rows, fp32, unaligned rows: none of them
     for args in [(A, Bb, Cb, 64, 14336, 4096, 2), (A, Bb, Cb, 256, 4096, 4096, 2),
                  (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4092, 2)]:
-        assert not name(*args).startswith("skinny"), args
-    # 8-bit inputs take the 8-bit strip configurations, up to 64 rows for N < 8192
-    for M, N, K in [(1, 4096, 4096), (16, 4096, 14336), (32, 4096, 4096), (64, 4096, 4096)]:
+        n = name(*args)
+        assert not n.startswith("skinny") and not n.startswith("fewrow"), args
+    # 8-bit: the 8-bit few-row configurations up to 32 rows below N = 12288
+    expect8 = {(1, 4096, 4096): "fewrow8_16x32x128", (16, 4096, 4096): "fewrow8_16x32x128",
+               (32, 4096, 4096): "fewrow8_16x32x128", (16, 8192, 4096): "fewrow8_16x32x128",
+               (16, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 8192): "fewrow8_16x16x128",
+               (64, 4096, 4096): "fp8_64x128x64_adma", (16, 14336, 4096): "fp8_64x128x64_adma"}
+    for (M, N, K), want in expect8.items():
         for dt in (3, 4):
-            info = dg.gemm_config_info(dg.gemm_select_config(A, Bb, Cb, M, N, K, dt))
-            assert info["name"].startswith("skinny8") and info["dtype_mask"] == 0x18, (M, N, K, info)
-    for M, N, K in [(16, 14336, 4096), (64, 14336, 4096), (128, 4096, 4096), (16, 4096, 4088)]:
-        assert not name(A, Bb, Cb, M, N, K, 3).startswith("skinny"), (M, N, K)
+            assert name(A, Bb, Cb, M, N, K, dt) == want, (M, N, K, dt)
+    for M, N, K in [(128, 4096, 4096), (16, 4096, 4088)]:
+        n = name(A, Bb, Cb, M, N, K, 3)
+        assert not n.startswith("skinny") and not n.startswith("fewrow"), (M, N, K)
 
 
 def test_192_row_tiles_where_256_leaves_a_partial_wave():
@@ -394,15 +404,20 @@ def test_workspace_sizes_follow_the_split_rule():
     assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
     assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(16, 14336, 4096, 3) == 2 * 16 * 14336 * 4
-    # 8-bit tiles are 64 x 128: 16 rows of 4096 columns are 32 tiles -> 8 splits of 8 K-steps;
-    # up to 64 rows each split keeps at least 16 K-steps (4 splits), beyond that 32:
-    # 128 x 4096 x 4096 -> 2
-    assert L.gemm_workspace_size(16, 4096, 4096, 3) == 8 * 16 * 4096 * 4
+    # 8-bit tiles are 64 x 128: up to 64 rows each split keeps at least 16 K-steps
+    # (32 x 4096 x 4096: 4 splits), beyond that 32: 128 x 4096 x 4096 -> 2
     assert L.gemm_workspace_size(32, 4096, 4096, 3) == 4 * 32 * 4096 * 4
     assert L.gemm_workspace_size(128, 4096, 4096, 3) == 2 * 128 * 4096 * 4
     # 1 to 8 rows split too (8 splits of the 32 tiles of 64 x 128)
     assert L.gemm_workspace_size(8, 4096, 4096, 2) == 8 * 8 * 4096 * 4
     assert L.gemm_workspace_size(1, 4096, 4096, 1) == 8 * 1 * 4096 * 4
+    # where the one-launch few-row kernel is faster: no split (16-bit K <= 2048, or
+    # K <= 4096 with N <= 2048; 8-bit up to 16 rows with K and N <= 4096)
+    for args in [(16, 2048, 2048, 2), (16, 4096, 2048, 1), (16, 2048, 4096, 2), (8, 2048, 2048, 2),
+                 (16, 4096, 4096, 3), (1, 2048, 4096, 4), (16, 3072, 3072, 3)]:
+        assert L.gemm_workspace_size(*args) == 0, args
+    assert L.gemm_workspace_size(16, 3072, 3072, 2) > 0
+    assert L.gemm_workspace_size(24, 4096, 4096, 3) > 0
     # enough tiles, GEMV, fp32, K < 2048, K = 0, and 8-bit inputs beyond 128 rows: no split
     for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2),
                  (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
@@ -486,9 +501,9 @@ def test_short_k_selects_128x128_tiles_with_a_through_registers():
     # from K = 264 on, the tile-count rules again
     assert name(A, Bb, Cb, 8192, 8192, 264, 2) == "mfma16x16_256x256x32_adma"
     assert name(A, Bb, Cb, 8192, 8192, 512, 3) == "fp8_256x256x64_adma"
-    # few rows keep the strip kernels, few columns the vector kernel
-    assert name(A, Bb, Cb, 16, 4096, 128, 2).startswith("skinny")
-    assert name(A, Bb, Cb, 16, 4096, 128, 3).startswith("skinny8")
+    # few rows keep the few-row kernels, few columns the vector kernel
+    assert name(A, Bb, Cb, 16, 4096, 128, 2).startswith("fewrow")
+    assert name(A, Bb, Cb, 16, 4096, 128, 3).startswith("fewrow8")
     assert name(A, Bb, Cb, 4096, 1, 128, 2).startswith("gemv")
 
 
@@ -499,9 +514,11 @@ def test_wide_few_rows_select_64x128_tiles_while_they_fit_one_wave():
     for M, N, K in [(40, 14336, 4096), (128, 14336, 4096), (64, 8192, 4096), (128, 8192, 8192)]:
         for dt in (1, 2):
             assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_64x128x32_adma", (M, N, K, dt)
-    # 448 tiles of 64 x 128: back to 128 x 128; up to 32 rows the strip kernels keep wide B
+    # 448 tiles of 64 x 128: back to 128 x 128; up to 32 rows of a wide B the
+    # 64 x 128 tiles from K = 1024, the strip kernel below
     assert name(A, Bb, Cb, 128, 28672, 4096, 2) == "mfma16x16_128x128x32_adma"
-    assert name(A, Bb, Cb, 32, 14336, 4096, 2).startswith("skinny")
+    assert name(A, Bb, Cb, 32, 14336, 4096, 2) == "mfma16x16_64x128x32_adma"
+    assert name(A, Bb, Cb, 32, 14336, 512, 2).startswith("skinny")
 
 
 def test_few_tiles_select_64x128_tiles_while_they_fit_one_wave():

@@ -392,3 +392,41 @@ def test_short_k_kernel_structure(tmp_path):
         assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 2
         loads = [l for l in ins if l.split()[0].startswith("buffer_load")]
         assert loads and all(l.rstrip().endswith("lds") for l in loads), loads[:3]
+
+
+def test_few_row_kernel_structure(tmp_path):
+    """The one-launch few-row kernel (every instance): no scratch, only loads
+    with the LDS destination (A and B of a K-step go straight to its ring
+    stage), two barriers (both in the final sum of the wavefronts' partial
+    sums: no wavefront waits for another during the K walk), the unscaled
+    8-bit MFMA, and vector-memory waits only at the counts its ring assumes:
+    (stages - 1 - t) K-steps of loads, t = 0 .. 3."""
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    out = tmp_path / "fewrow.s"
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_fewrow.hip"),
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    sizes = [int(x) for x in re.findall(r"\.amdhsa_private_segment_fixed_size (\d+)", text)]
+    assert len(sizes) == 10 and all(x == 0 for x in sizes), sizes
+    assert "v_mfma_scale" not in text
+    pat = r"^(_Z\S*gemm_fewrow_kernel\S*?(DF16_|DF16b|E4M3|E5M2)\S*?Li16ELi(\d+)ELi(\d+)ELi(\d+)ELi4E\S*):[^\n]*$(.*?)^\.Lfunc_end"
+    bodies = re.findall(pat, text, re.M | re.S)
+    assert len(bodies) == 10
+    for name, ty, bn, bk, w, body in bodies:
+        es = 1 if ty in ("E4M3", "E5M2") else 2
+        bn, bk = int(bn), int(bk)
+        per_step = (bk * bn * es) // 1024 + (16 * bk * es) // 1024      # B then A loads of a K-step
+        ins = [l.strip() for l in body.split("\n") if l.strip() and not l.strip().startswith((";", "."))]
+        loads = [l for l in ins if l.split()[0].startswith("buffer_load")]
+        assert loads and all(l.rstrip().endswith("lds") for l in loads), (name, loads[:3])
+        assert sum(1 for l in ins if l.split()[0] == "s_barrier") == 2, name
+        mfma = [l.split()[0] for l in ins if l.startswith("v_mfma")]
+        want = "v_mfma_f32_16x16x128_f8f6f4" if es == 1 else "v_mfma_f32_16x16x32_" + ("f16" if ty == "DF16_" else "bf16")
+        assert mfma and all(m == want for m in mfma), (name, set(mfma))
+        waits = {int(x) for x in re.findall(r"s_waitcnt[^\n]*vmcnt\((\d+)\)", body)}
+        assert waits <= {t * per_step for t in range(4)}, (name, sorted(waits), per_step)
+        assert 3 * per_step in waits, (name, sorted(waits))
