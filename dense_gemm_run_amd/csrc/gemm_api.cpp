@@ -123,6 +123,9 @@ const Entry kTable[] = {
     {{51, 16, 32, 32, 2, 512, 0x6, 1, 1, "fewrow_16x32x32"}, kFewRow},
     {{52, 16, 16, 128, 2, 512, 0x18, 1, 1, "fewrow8_16x16x128"}, kFewRow},
     {{53, 16, 32, 128, 2, 256, 0x18, 1, 1, "fewrow8_16x32x128"}, kFewRow},
+    // the same with 8 rows per workgroup (half the A loads) for up to 8 rows
+    {{54, 8, 16, 64, 2, 512, 0x6, 1, 1, "fewrow_8x16x64"}, kFewRow},
+    {{55, 8, 32, 128, 2, 256, 0x18, 1, 1, "fewrow8_8x32x128"}, kFewRow},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -224,9 +227,9 @@ bool accepts(const Entry& e, const Problem& p)
 //    workgroups, one per strip of B's columns, which fill the chip where the
 //    tiled kernels have a few dozen tiles (M = 16, N = K = 4096: 44 against
 //    18 TFLOP/s) - up to 32 rows the one-launch few-row kernel (A streamed
-//    beside B) below N = 12288, the 64 x 128 tiles above; from 33 rows the
-//    strip kernel for N < 8192 (at N = 14336 and 64 rows the 128 x 128 tiles
-//    were faster);
+//    beside B) below N = 12288 (10240 for 8-bit inputs), the 64 x 128 tiles
+//    above; from 33 rows the strip kernel for N < 8192 (at N = 14336 and 64
+//    rows the 128 x 128 tiles were faster);
 //  * fp32 with 16-byte rows: the fp32 MFMA kernel (128 x 128 tiles from 1024
 //    of them, else 64 x 64);
 //  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
@@ -261,16 +264,20 @@ int select(const Problem& p)
     }
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
-        if (p.M <= 32 && p.N < 12288) {
+        if (p.M <= 32 && p.N < 10240) {
             // few rows: the one-launch few-row kernel, 32-column strips
-            // (16 columns for K >= 8192 up to 16 rows, for more strips).
-            // (E4M3, graph-timed: 1-16 x 4096 x 4096 5.9-6.0 us against
-            // 6.5-7.7 on the strip kernel; 24-32 rows 7.5-7.6 against 9.0-9.6;
+            // (8-row workgroups up to 8 rows; 16 columns for K >= 8192 up to
+            // 16 rows, for more strips, and from K = 12288 up to 8 rows too).
+            // (E4M3, graph-timed: 1-16 x 4096 x 4096 5.6-6.0 us against
+            // 6.4-7.7 on the strip kernel; 24-32 rows 7.5-7.6 against 9.0-9.6;
             // 16 x 4096 x 14336 24.9 against 27.1; 16 x 8192 x 4096 10.9
             // against 12.2 on the 64 x 128 tiles.)  From 33 rows and from N =
-            // 12288 the tiled rules below pick the 64 x 128 tiles (48-64 x
+            // 10240 the tiled rules below pick the 64 x 128 tiles (48-64 x
             // 4096 x 4096: 10.3-10.4 us against 11.1-11.2 on the strip
-            // kernel; 16 x 14336 x 4096: 14.2 against 17.9).
+            // kernel; 4 x 11008 x 4096: 12.5 against 14.8; 16 x 14336 x
+            // 4096: 14.2 against 17.9).
+            if (p.M <= 16 && p.K >= 12288) return 52;
+            if (p.M <= 8) return 55;
             return p.M <= 16 && p.K >= 8192 ? 52 : 53;
         }
         // at most 4 K-steps of 64: 128 x 128 tiles with A through registers,
@@ -326,7 +333,12 @@ int select(const Problem& p)
                 if (p.K >= 1024) return 37;
                 return p.M <= 16 ? 18 : 19;
             }
-            if (p.M <= 16 && !wide) return p.K <= 2048 && p.N >= 4096 ? 51 : 50;
+            if (p.M <= 16 && !wide) {
+                if (p.K <= 2048 && p.N >= 4096) return 51;
+                // up to 8 rows, workgroups of 8 rows load half the A bytes
+                // (1-8 x 4096 x 4096: 7.4-8.2 against 7.9-8.5 us)
+                return p.M <= 8 ? 54 : 50;
+            }
             return 51;
         }
         if (!wide) return p.M <= 64 ? 19 : 20;

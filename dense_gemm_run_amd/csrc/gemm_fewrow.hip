@@ -16,8 +16,9 @@
 // owning a contiguous K range and the workgroups of an XCD starting their
 // walks at different K-steps, 7.5-8.1 us.  This kernel is the latter:
 //
-//  * one workgroup of W wavefronts owns all BMS rows (16) and a strip of BN
-//    columns of C;
+//  * one workgroup of W wavefronts owns BMS rows (16, or 8 for products of
+//    at most 8 rows, which then load half the A bytes per K-step) and a
+//    strip of BN columns of C;
 //  * wavefront w owns the contiguous K-steps [w*S, (w+1)*S) and walks them
 //    starting at a step that depends on the strip (so neighbouring
 //    workgroups read different columns of A and rows of B at any moment);
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
     constexpr int ES = Mma<E>::BYTES;                // bytes per element of A and B
     constexpr int KI = Mma<E>::KI;                   // K per MFMA
     constexpr int FB = (int)sizeof(Frag);            // fragment bytes per lane (KI/4 * ES)
-    constexpr int FM = BMS / 16, FN = BN / 16;       // 16x16 tiles
+    constexpr int FN = BN / 16;                      // 16x16 tiles (one tile-row: 16 rows)
     constexpr int NS = BK / KI;                      // K-slices per K-step
     constexpr int ROW_B = BN * ES;                   // bytes of one B row of the strip
     constexpr int ROW_A = BK * ES;                   // bytes of one A row of a K-step
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
     constexpr int LB = STEP_B / 1024, LA = STEP_A / 1024;
     constexpr int L = LB + LA;                       // direct-to-LDS loads per K-step
     constexpr int PA = ROW_A / 16;                   // 16-byte pieces per A row of a step
-    static_assert(BMS == 16, "rows");
+    static_assert(BMS == 16 || BMS == 8, "rows");
     static_assert(BN == 16 || BN == 32, "strip width");
     static_assert(BK % KI == 0, "K-step");
     static_assert(STEP_B % 1024 == 0 && STEP_A % 1024 == 0, "whole 1 KB loads");
@@ -244,16 +245,17 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
             const int lg = k * ROW_B + byte;
             b_rd[ni][h] = lg ^ ((k & SWZ_BIT) ? SWZ : 0);
         }
-    // A fragment of K-slice s: lane -> row lane%16, logical pieces
-    // (FB/16)*(KI/(4*(16/ES)) ... ): the lane's KI/4 K start at K-slice
-    // offset (KI/4)*(lane/16), i.e. logical piece (KI*s + (KI/4)*(lane/16))/(16/ES) + h.
+    // A fragment of K-slice s: lane -> row lane%16 (lane%8 with 8 rows: the
+    // MFMA's rows 8-15 repeat rows 0-7 and are never stored), K from
+    // KI*s + (KI/4)*(lane/16): logical pieces (KI*s + (KI/4)*(lane/16))/(16/ES)
+    // + h, h < AH.
     constexpr int AH = FB / 16;   // 16-byte reads per A fragment
     int a_rd[NS][AH];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int h = 0; h < AH; ++h) {
-            const int r = lane & 15;
+            const int r = lane & (BMS - 1);
             const int lq = (KI * s + (KI / 4) * (lane >> 4)) / (16 / ES) + h;
             a_rd[s][h] = STEP_B + r * ROW_A + 16 * (lq ^ swz_a(r));
         }
@@ -335,11 +337,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
         const int g = w * BMS * BN * 4 + o;
         return (float __attribute__((address_space(3)))*)(stage(g / (W * STEP)) + g % (W * STEP));
     };
-    // tile ni: lane l holds row l%16, columns 16*ni + 4*(l/16) .. +3
+    // tile ni: lane l holds row l%16, columns 16*ni + 4*(l/16) .. +3 (rows
+    // below BMS only)
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
         const int m = lane & 15, n = 16 * ni + 4 * (lane >> 4);
-        *(f32x4 __attribute__((address_space(3)))*)part(wave, (m * BN + n) * 4) = acc[ni];
+        if (m < BMS) *(f32x4 __attribute__((address_space(3)))*)part(wave, (m * BN + n) * 4) = acc[ni];
     }
     __syncthreads();
     // thread t sums 4 consecutive columns of one row over the wavefronts, in order
@@ -376,9 +379,11 @@ hipError_t launch_e(const Config& cfg, const LaunchArgs& a)
         DGR_LAUNCH(16, 16, 32, 8)
         DGR_LAUNCH(16, 16, 64, 8)
         DGR_LAUNCH(16, 32, 32, 8)
+        DGR_LAUNCH(8, 16, 64, 8)
     } else {
         DGR_LAUNCH(16, 16, 128, 8)
         DGR_LAUNCH(16, 32, 128, 4)
+        DGR_LAUNCH(8, 32, 128, 4)
     }
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;

@@ -313,7 +313,8 @@ def test_few_rows_select_the_few_row_kernels():
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
     # 16-bit: the one-launch few-row kernel up to 32 rows below N = 12288, the
     # strip kernel for 33-128 rows of a narrow B, the 64 x 128 tiles for wide B
-    expect16 = {(16, 4096, 4096): "fewrow_16x16x64", (1, 4096, 4096): "fewrow_16x16x64",
+    expect16 = {(16, 4096, 4096): "fewrow_16x16x64", (1, 4096, 4096): "fewrow_8x16x64",
+                (8, 4096, 14336): "fewrow_8x16x64", (9, 4096, 4096): "fewrow_16x16x64",
                 (16, 4096, 14336): "fewrow_16x16x64", (16, 4096, 2048): "fewrow_16x32x32",
                 (16, 2048, 2048): "fewrow_16x16x64", (32, 4096, 4096): "fewrow_16x32x32",
                 (24, 4096, 4096): "fewrow_16x32x32", (16, 8192, 4096): "fewrow_16x32x32",
@@ -329,10 +330,12 @@ def test_few_rows_select_the_few_row_kernels():
         n = name(*args)
         assert not n.startswith("skinny") and not n.startswith("fewrow"), args
     # 8-bit: the 8-bit few-row configurations up to 32 rows below N = 12288
-    expect8 = {(1, 4096, 4096): "fewrow8_16x32x128", (16, 4096, 4096): "fewrow8_16x32x128",
+    expect8 = {(1, 4096, 4096): "fewrow8_8x32x128", (8, 1024, 8192): "fewrow8_8x32x128",
+               (8, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 4096): "fewrow8_16x32x128",
                (32, 4096, 4096): "fewrow8_16x32x128", (16, 8192, 4096): "fewrow8_16x32x128",
                (16, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 8192): "fewrow8_16x16x128",
-               (64, 4096, 4096): "fp8_64x128x64_adma", (16, 14336, 4096): "fp8_64x128x64_adma"}
+               (64, 4096, 4096): "fp8_64x128x64_adma", (16, 14336, 4096): "fp8_64x128x64_adma",
+               (4, 11008, 4096): "fp8_64x128x64_adma"}
     for (M, N, K), want in expect8.items():
         for dt in (3, 4):
             assert name(A, Bb, Cb, M, N, K, dt) == want, (M, N, K, dt)
