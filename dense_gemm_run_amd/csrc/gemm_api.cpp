@@ -324,12 +324,13 @@ int select(const Problem& p)
         // us against 8.9-12.0 on the strip kernel; 16 x 4096 x 14336 32.6
         // against 37.2; 24 and 32 x 4096 x 4096 11.1 and 11.6 against 12.4
         // and 13.1; 16 x 8192 x 4096 14.3 against 15.3; 16 x 14336 x 4096
-        // 23.2 on the tiles against 24.7 and 26.6.)  From 33 rows: the strip
+        // 23.2 on the tiles against 24.7 and 26.6; the tiles only while they
+        // fit one wave of workgroups.)  From 33 rows: the strip
         // kernel, except for wide B (N >= 8192), where the 128 x 128 tiles
         // already give enough workgroups.
         const bool wide = p.N >= 8192;
         if (p.M <= 32) {
-            if (p.N >= 12288) {
+            if (p.N >= 12288 && (p.N + 127) / 128 * p.batch <= 256) {
                 if (p.K >= 1024) return 37;
                 return p.M <= 16 ? 18 : 19;
             }

@@ -319,7 +319,8 @@ def test_few_rows_select_the_few_row_kernels():
                 (16, 2048, 2048): "fewrow_16x16x64", (32, 4096, 4096): "fewrow_16x32x32",
                 (24, 4096, 4096): "fewrow_16x32x32", (16, 8192, 4096): "fewrow_16x32x32",
                 (16, 14336, 4096): "mfma16x16_64x128x32_adma", (32, 14336, 4096): "mfma16x16_64x128x32_adma",
-                (16, 14336, 512): "skinny_16x32x64", (64, 4096, 4096): "skinny_32x32x64",
+                (16, 14336, 512): "skinny_16x32x64", (16, 65536, 4096): "fewrow_16x32x32",
+                (16, 32768, 4096): "mfma16x16_64x128x32_adma", (64, 4096, 4096): "skinny_32x32x64",
                 (128, 4096, 4096): "skinny_64x32x32"}
     for (M, N, K), want in expect16.items():
         for dt in (1, 2):
