@@ -126,6 +126,11 @@ const Entry kTable[] = {
     // the same with 8 rows per workgroup (half the A loads) for up to 8 rows
     {{54, 8, 16, 64, 2, 512, 0x6, 1, 1, "fewrow_8x16x64"}, kFewRow},
     {{55, 8, 32, 128, 2, 256, 0x18, 1, 1, "fewrow8_8x32x128"}, kFewRow},
+    // the same with 32 or 64 rows per workgroup
+    {{56, 32, 16, 32, 2, 512, 0x6, 1, 1, "fewrow_32x16x32"}, kFewRow},
+    {{57, 32, 32, 32, 2, 512, 0x6, 1, 1, "fewrow_32x32x32"}, kFewRow},
+    {{58, 64, 16, 32, 2, 512, 0x6, 1, 1, "fewrow_64x16x32"}, kFewRow},
+    {{59, 64, 32, 32, 2, 256, 0x6, 1, 1, "fewrow_64x32x32"}, kFewRow},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -228,8 +233,8 @@ bool accepts(const Entry& e, const Problem& p)
 //    tiled kernels have a few dozen tiles (M = 16, N = K = 4096: 44 against
 //    18 TFLOP/s) - up to 32 rows the one-launch few-row kernel (A streamed
 //    beside B) below N = 12288 (10240 for 8-bit inputs), the 64 x 128 tiles
-//    above; from 33 rows the strip kernel for N < 8192 (at N = 14336 and 64
-//    rows the 128 x 128 tiles were faster);
+//    above; from 33 rows the same kernel with 32- and 64-row workgroups for
+//    N < 8192 (33-64 rows up to N = 12288), the tiles for wider B;
 //  * fp32 with 16-byte rows: the fp32 MFMA kernel (128 x 128 tiles from 1024
 //    of them, else 64 x 64);
 //  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
@@ -315,19 +320,26 @@ int select(const Problem& p)
     if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
     if (p.M <= 128) {
-        // Few rows.  Up to 32 rows: the one-launch few-row kernel (A streamed
-        // beside B), 16-column strips with 64-deep K-steps up to 16 rows
-        // below N = 8192 (32-column strips where K <= 2048 leaves each
-        // wavefront few steps), else 32-column strips; from N = 12288 (and
-        // K >= 1024) the 64 x 128 tiles instead, whose one pass already has
-        // enough workgroups.  (bf16, graph-timed: 1-16 x 4096 x 4096 7.7-8.8
-        // us against 8.9-12.0 on the strip kernel; 16 x 4096 x 14336 32.6
-        // against 37.2; 24 and 32 x 4096 x 4096 11.1 and 11.6 against 12.4
-        // and 13.1; 16 x 8192 x 4096 14.3 against 15.3; 16 x 14336 x 4096
-        // 23.2 on the tiles against 24.7 and 26.6; the tiles only while they
-        // fit one wave of workgroups.)  From 33 rows: the strip
-        // kernel, except for wide B (N >= 8192), where the 128 x 128 tiles
-        // already give enough workgroups.
+        // Few rows: the one-launch few-row kernel (A streamed beside B), with
+        // workgroups of as many rows as keep about one workgroup per CU:
+        //  * up to 16 rows below N = 8192: 16-column strips with 64-deep
+        //    K-steps, 8-row workgroups up to 8 rows (32-column strips where
+        //    K <= 2048 leaves each wavefront few steps);
+        //  * up to 32 rows otherwise: 32-column strips of 16 rows, or of 32
+        //    rows from N = 8192 (17-32 rows);
+        //  * 33-64 rows: 32 x 32 below N = 8192, 64 x 32 up to N = 12288;
+        //  * 65-128 rows below N = 8192: 64 x 32;
+        //  * up to 32 rows from N = 12288 (K >= 1024) the 64 x 128 tiles while
+        //    they fit one wave, whose one pass already has enough workgroups;
+        //    the wider rows of 33-128 rows go to the tile rules below.
+        // (bf16, graph-timed: 1-16 x 4096 x 4096 7.4-8.8 us against 8.9-12.0
+        // on the strip kernel; 16 x 4096 x 14336 32.6 against 37.2; 24 and 32
+        // x 4096 x 4096 11.0 and 11.6 against 12.4 and 13.1; 32 x 8192 x 4096
+        // 15.1 on 32-row workgroups against 20.2 on 16-row ones; 48 and 64 x
+        // 4096 x 4096 13.1 and 13.9 against 15.7 and 17.0; 96 and 128 x 4096
+        // x 4096 16.5 and 18.1 against 20.6 and 22.5; 64 x 8192 x 4096 18.2
+        // against 22.7 on the tiles; 128 x 4096 x 14336 54.3 against 68.7;
+        // 16 x 14336 x 4096 23.2 on the tiles against 24.7 and 26.6.)
         const bool wide = p.N >= 8192;
         if (p.M <= 32) {
             if (p.N >= 12288 && (p.N + 127) / 128 * p.batch <= 256) {
@@ -340,9 +352,10 @@ int select(const Problem& p)
                 // (1-8 x 4096 x 4096: 7.4-8.2 against 7.9-8.5 us)
                 return p.M <= 8 ? 54 : 50;
             }
-            return 51;
+            return p.M > 16 && wide ? 57 : 51;
         }
-        if (!wide) return p.M <= 64 ? 19 : 20;
+        if (!wide) return p.M <= 64 ? 57 : 59;
+        if (p.M <= 64 && p.N < 12288) return 59;
     }
     // At most 128 K and at least 1024 tiles of 128 x 128: the persistent
     // short-K kernel, whose workgroups load their next tile while they store

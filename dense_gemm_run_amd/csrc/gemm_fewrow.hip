@@ -107,7 +107,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
     constexpr int ES = Mma<E>::BYTES;                // bytes per element of A and B
     constexpr int KI = Mma<E>::KI;                   // K per MFMA
     constexpr int FB = (int)sizeof(Frag);            // fragment bytes per lane (KI/4 * ES)
-    constexpr int FN = BN / 16;                      // 16x16 tiles (one tile-row: 16 rows)
+    constexpr int FN = BN / 16;                      // 16x16 tiles per row of them
+    constexpr int FM = BMS < 16 ? 1 : BMS / 16;      // rows of 16x16 tiles
     constexpr int NS = BK / KI;                      // K-slices per K-step
     constexpr int ROW_B = BN * ES;                   // bytes of one B row of the strip
     constexpr int ROW_A = BK * ES;                   // bytes of one A row of a K-step
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
     constexpr int LB = STEP_B / 1024, LA = STEP_A / 1024;
     constexpr int L = LB + LA;                       // direct-to-LDS loads per K-step
     constexpr int PA = ROW_A / 16;                   // 16-byte pieces per A row of a step
-    static_assert(BMS == 16 || BMS == 8, "rows");
+    static_assert(BMS == 8 || BMS == 16 || BMS == 32 || BMS == 64, "rows");
     static_assert(BN == 16 || BN == 32, "strip width");
     static_assert(BK % KI == 0, "K-step");
     static_assert(STEP_B % 1024 == 0 && STEP_A % 1024 == 0, "whole 1 KB loads");
@@ -245,17 +246,18 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
             const int lg = k * ROW_B + byte;
             b_rd[ni][h] = lg ^ ((k & SWZ_BIT) ? SWZ : 0);
         }
-    // A fragment of K-slice s: lane -> row lane%16 (lane%8 with 8 rows: the
-    // MFMA's rows 8-15 repeat rows 0-7 and are never stored), K from
-    // KI*s + (KI/4)*(lane/16): logical pieces (KI*s + (KI/4)*(lane/16))/(16/ES)
-    // + h, h < AH.
+    // A fragment of K-slice s, tile row mi: lane -> row 16*mi + lane%16
+    // (lane%8 with 8 rows: the MFMA's rows 8-15 repeat rows 0-7 and are
+    // never stored), K from KI*s + (KI/4)*(lane/16): logical pieces
+    // (KI*s + (KI/4)*(lane/16))/(16/ES) + h, h < AH.  The swizzle of row r
+    // and of row r + 16 is the same, so tile row mi is 16*mi rows further.
     constexpr int AH = FB / 16;   // 16-byte reads per A fragment
     int a_rd[NS][AH];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
         for (int h = 0; h < AH; ++h) {
-            const int r = lane & (BMS - 1);
+            const int r = lane & (BMS < 16 ? BMS - 1 : 15);
             const int lq = (KI * s + (KI / 4) * (lane >> 4)) / (16 / ES) + h;
             a_rd[s][h] = STEP_B + r * ROW_A + 16 * (lq ^ swz_a(r));
         }
@@ -278,19 +280,22 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
             return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
-    auto read_a = [&](const lds_byte* base, int s) __attribute__((always_inline)) -> Frag {
+    auto read_a = [&](const lds_byte* base, int s, int mi) __attribute__((always_inline)) -> Frag {
+        const lds_byte* p = base + mi * 16 * ROW_A;
         if constexpr (AH == 1) {
-            return __builtin_bit_cast(Frag, *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[s][0]));
+            return __builtin_bit_cast(Frag, *(const u32x4 __attribute__((address_space(3)))*)(p + a_rd[s][0]));
         } else {
-            const u32x4 lo = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[s][0]);
-            const u32x4 hi = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[s][1]);
+            const u32x4 lo = *(const u32x4 __attribute__((address_space(3)))*)(p + a_rd[s][0]);
+            const u32x4 hi = *(const u32x4 __attribute__((address_space(3)))*)(p + a_rd[s][1]);
             return __builtin_bit_cast(Frag, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
 
-    f32x4 acc[FN];
+    f32x4 acc[FN][FM];
 #pragma unroll
-    for (int ni = 0; ni < FN; ++ni) acc[ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Step j of the wavefront (stage j % NSTG, a literal below): wait until
     // its loads have landed (`after` = this wavefront's loads issued after
@@ -300,19 +305,22 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(decltype(after_c)::value));
         asm volatile("" ::: "memory");
         const lds_byte* base = stage(st) + wave * STEP;
-        Frag bf[NS][FN], af[NS];
+        Frag bf[NS][FN], af[NS][FM];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
 #pragma unroll
             for (int ni = 0; ni < FN; ++ni) bf[s][ni] = read_b(base, s, ni);
-            af[s] = read_a(base, s);
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi) af[s][mi] = read_a(base, s, mi);
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the stage is read: it may be refilled
         if (refill) issue(st, j + NSTG);
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int ni = 0; ni < FN; ++ni) Mma<E>::run(acc[ni], bf[s][ni], af[s]);
+            for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < FM; ++mi) Mma<E>::run(acc[ni][mi], bf[s][ni], af[s][mi]);
     };
     // prologue: steps 0 .. NSTG-1 (S is a multiple of NSTG)
     each<0, NSTG>([&](auto t) __attribute__((always_inline)) { issue(decltype(t)::value, decltype(t)::value); });
@@ -337,13 +345,15 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_fewrow_kernel(const unsigned c
         const int g = w * BMS * BN * 4 + o;
         return (float __attribute__((address_space(3)))*)(stage(g / (W * STEP)) + g % (W * STEP));
     };
-    // tile ni: lane l holds row l%16, columns 16*ni + 4*(l/16) .. +3 (rows
-    // below BMS only)
+    // tile (ni, mi): lane l holds row 16*mi + l%16, columns 16*ni + 4*(l/16)
+    // .. +3 (rows below BMS only)
 #pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
-        const int m = lane & 15, n = 16 * ni + 4 * (lane >> 4);
-        if (m < BMS) *(f32x4 __attribute__((address_space(3)))*)part(wave, (m * BN + n) * 4) = acc[ni];
-    }
+    for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi) {
+            const int m = 16 * mi + (lane & 15), n = 16 * ni + 4 * (lane >> 4);
+            if (m < BMS) *(f32x4 __attribute__((address_space(3)))*)part(wave, (m * BN + n) * 4) = acc[ni][mi];
+        }
     __syncthreads();
     // thread t sums 4 consecutive columns of one row over the wavefronts, in order
     for (int e = threadIdx.x; e < BMS * BN / 4; e += 64 * W) {
@@ -380,6 +390,10 @@ hipError_t launch_e(const Config& cfg, const LaunchArgs& a)
         DGR_LAUNCH(16, 16, 64, 8)
         DGR_LAUNCH(16, 32, 32, 8)
         DGR_LAUNCH(8, 16, 64, 8)
+        DGR_LAUNCH(32, 16, 32, 8)
+        DGR_LAUNCH(32, 32, 32, 8)
+        DGR_LAUNCH(64, 16, 32, 8)
+        DGR_LAUNCH(64, 32, 32, 4)
     } else {
         DGR_LAUNCH(16, 16, 128, 8)
         DGR_LAUNCH(16, 32, 128, 4)

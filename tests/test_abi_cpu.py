@@ -311,8 +311,8 @@ def test_few_rows_select_the_few_row_kernels():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
-    # 16-bit: the one-launch few-row kernel up to 32 rows below N = 12288, the
-    # strip kernel for 33-128 rows of a narrow B, the 64 x 128 tiles for wide B
+    # 16-bit: the one-launch few-row kernel (16-, 32- and 64-row workgroups),
+    # the 64 x 128 tiles for wide B, the strip kernel for wide B with short K
     expect16 = {(16, 4096, 4096): "fewrow_16x16x64", (1, 4096, 4096): "fewrow_8x16x64",
                 (8, 4096, 14336): "fewrow_8x16x64", (9, 4096, 4096): "fewrow_16x16x64",
                 (16, 4096, 14336): "fewrow_16x16x64", (16, 4096, 2048): "fewrow_16x32x32",
@@ -320,8 +320,10 @@ def test_few_rows_select_the_few_row_kernels():
                 (24, 4096, 4096): "fewrow_16x32x32", (16, 8192, 4096): "fewrow_16x32x32",
                 (16, 14336, 4096): "mfma16x16_64x128x32_adma", (32, 14336, 4096): "mfma16x16_64x128x32_adma",
                 (16, 14336, 512): "skinny_16x32x64", (16, 65536, 4096): "fewrow_16x32x32",
-                (16, 32768, 4096): "mfma16x16_64x128x32_adma", (64, 4096, 4096): "skinny_32x32x64",
-                (128, 4096, 4096): "skinny_64x32x32"}
+                (16, 32768, 4096): "mfma16x16_64x128x32_adma", (32, 8192, 4096): "fewrow_32x32x32",
+                (48, 4096, 4096): "fewrow_32x32x32", (64, 4096, 4096): "fewrow_32x32x32",
+                (64, 8192, 4096): "fewrow_64x32x32", (96, 4096, 4096): "fewrow_64x32x32",
+                (128, 4096, 4096): "fewrow_64x32x32", (128, 4096, 14336): "fewrow_64x32x32"}
     for (M, N, K), want in expect16.items():
         for dt in (1, 2):
             assert name(A, Bb, Cb, M, N, K, dt) == want, (M, N, K, dt)
@@ -515,7 +517,7 @@ def test_wide_few_rows_select_64x128_tiles_while_they_fit_one_wave():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
-    for M, N, K in [(40, 14336, 4096), (128, 14336, 4096), (64, 8192, 4096), (128, 8192, 8192)]:
+    for M, N, K in [(40, 14336, 4096), (128, 14336, 4096), (96, 8192, 4096), (128, 8192, 8192)]:
         for dt in (1, 2):
             assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_64x128x32_adma", (M, N, K, dt)
     # 448 tiles of 64 x 128: back to 128 x 128; up to 32 rows of a wide B the

@@ -122,7 +122,7 @@ def test_skinny_guards_untouched():
         check(A, B, "f16", out)
 
 
-@pytest.mark.parametrize("shape", [(64, 4096, 4096), (128, 4096, 4096), (48, 2048, 4096), (16, 14336, 512)])
+@pytest.mark.parametrize("shape", [(16, 14336, 512), (32, 14336, 256)])
 def test_few_row_shapes_in_the_selected_configuration(shape):
     M, N, K = shape
     A, B = make_operands(M, N, K, "bf16", "prefill", 630)
