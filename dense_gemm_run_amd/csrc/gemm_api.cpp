@@ -131,6 +131,7 @@ const Entry kTable[] = {
     {{57, 32, 32, 32, 2, 512, 0x6, 1, 1, "fewrow_32x32x32"}, kFewRow},
     {{58, 64, 16, 32, 2, 512, 0x6, 1, 1, "fewrow_64x16x32"}, kFewRow},
     {{59, 64, 32, 32, 2, 256, 0x6, 1, 1, "fewrow_64x32x32"}, kFewRow},
+    {{60, 32, 32, 128, 2, 256, 0x18, 1, 1, "fewrow8_32x32x128"}, kFewRow},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -234,7 +235,8 @@ bool accepts(const Entry& e, const Problem& p)
 //    18 TFLOP/s) - up to 32 rows the one-launch few-row kernel (A streamed
 //    beside B) below N = 12288 (10240 for 8-bit inputs), the 64 x 128 tiles
 //    above; from 33 rows the same kernel with 32- and 64-row workgroups for
-//    N < 8192 (33-64 rows up to N = 12288), the tiles for wider B;
+//    N < 8192 (33-64 rows up to N = 12288; 8-bit inputs: 33-64 rows below
+//    N = 10240), the tiles for wider B;
 //  * fp32 with 16-byte rows: the fp32 MFMA kernel (128 x 128 tiles from 1024
 //    of them, else 64 x 64);
 //  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
@@ -269,21 +271,23 @@ int select(const Problem& p)
     }
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
-        if (p.M <= 32 && p.N < 10240) {
+        if (p.M <= 64 && p.N < 10240) {
             // few rows: the one-launch few-row kernel, 32-column strips
-            // (8-row workgroups up to 8 rows; 16 columns for K >= 8192 up to
-            // 16 rows, for more strips, and from K = 12288 up to 8 rows too).
-            // (E4M3, graph-timed: 1-16 x 4096 x 4096 5.6-6.0 us against
-            // 6.4-7.7 on the strip kernel; 24-32 rows 7.5-7.6 against 9.0-9.6;
-            // 16 x 4096 x 14336 24.9 against 27.1; 16 x 8192 x 4096 10.9
-            // against 12.2 on the 64 x 128 tiles.)  From 33 rows and from N =
-            // 10240 the tiled rules below pick the 64 x 128 tiles (48-64 x
-            // 4096 x 4096: 10.3-10.4 us against 11.1-11.2 on the strip
-            // kernel; 4 x 11008 x 4096: 12.5 against 14.8; 16 x 14336 x
-            // 4096: 14.2 against 17.9).
+            // (8-row workgroups up to 8 rows, 32-row ones from 17 rows; 16
+            // columns for K >= 8192 up to 16 rows, for more strips, and from
+            // K = 12288 up to 8 rows too).  (E4M3, graph-timed: 1-16 x 4096 x
+            // 4096 5.6-6.2 us against 6.4-7.7 on the strip kernel; 24-64 rows
+            // 6.8-8.5 against 9.0-11.2; 16 x 4096 x 14336 24.9 against 27.1;
+            // 64 x 4096 x 14336 28.3 against 42.9 on the 64 x 128 tiles; 16
+            // and 32 x 8192 x 4096 10.9 and 11.8 against 12.2 and 13.1.)  From
+            // 65 rows and from N = 10240 the tiled rules below pick the 64 x
+            // 128 tiles (96-128 x 4096 x 4096: 10.4 us against 17.5; 4 x 11008
+            // x 4096: 12.5 against 14.8; 16 x 14336 x 4096: 14.2 against
+            // 17.9).
             if (p.M <= 16 && p.K >= 12288) return 52;
             if (p.M <= 8) return 55;
-            return p.M <= 16 && p.K >= 8192 ? 52 : 53;
+            if (p.M <= 16) return p.K >= 8192 ? 52 : 53;
+            return 60;
         }
         // at most 4 K-steps of 64: 128 x 128 tiles with A through registers,
         // for the same reason as the 16-bit short-K rule below (E4M3,
@@ -466,11 +470,12 @@ int select_ws(const Problem& p, int64_t ws_bytes, int& splits)
         s = split_count(t, steps, p.K, 32);
     } else if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[kSplitConfig8], p) || p.M > 128) return c;
-        // up to 16 rows with K and N at most 4096: the one-launch few-row
+        // up to 64 rows with K and N at most 4096: the one-launch few-row
         // kernel (E4M3: 16 x 4096 x 4096 6.0 against 6.5 us with 8 splits,
-        // 16 x 2048-3072 x 2048-4096 3.9-5.0 against 5.6-6.1; 1-8 rows x 4096
-        // x 4096 5.9-6.0 against 5.6-5.9, the one loss)
-        if (kTable[c].kind == kFewRow && p.M <= 16 && p.K <= 4096 && p.N <= 4096) return c;
+        // 24-64 rows 6.8-8.5 against 7.1-9.1, 16 x 2048-3072 x 2048-4096
+        // 3.9-5.0 against 5.6-6.1; 1-8 rows x 4096 x 4096 5.6-6.0 against
+        // 5.6-5.9)
+        if (kTable[c].kind == kFewRow && p.M <= 64 && p.K <= 4096 && p.N <= 4096) return c;
         const int64_t steps = (p.K + 63) / 64;
         if (steps < 32) return c;
         cfg = kSplitConfig8;

@@ -398,6 +398,7 @@ hipError_t launch_e(const Config& cfg, const LaunchArgs& a)
         DGR_LAUNCH(16, 16, 128, 8)
         DGR_LAUNCH(16, 32, 128, 4)
         DGR_LAUNCH(8, 32, 128, 4)
+        DGR_LAUNCH(32, 32, 128, 4)
     }
 #undef DGR_LAUNCH
     return hipErrorInvalidValue;

@@ -332,12 +332,13 @@ def test_few_rows_select_the_few_row_kernels():
                  (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4092, 2)]:
         n = name(*args)
         assert not n.startswith("skinny") and not n.startswith("fewrow"), args
-    # 8-bit: the 8-bit few-row configurations up to 32 rows below N = 12288
+    # 8-bit: the 8-bit few-row configurations up to 64 rows below N = 10240
     expect8 = {(1, 4096, 4096): "fewrow8_8x32x128", (8, 1024, 8192): "fewrow8_8x32x128",
                (8, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 4096): "fewrow8_16x32x128",
-               (32, 4096, 4096): "fewrow8_16x32x128", (16, 8192, 4096): "fewrow8_16x32x128",
+               (32, 4096, 4096): "fewrow8_32x32x128", (16, 8192, 4096): "fewrow8_16x32x128",
                (16, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 8192): "fewrow8_16x16x128",
-               (64, 4096, 4096): "fp8_64x128x64_adma", (16, 14336, 4096): "fp8_64x128x64_adma",
+               (64, 4096, 4096): "fewrow8_32x32x128", (24, 4096, 14336): "fewrow8_32x32x128",
+               (96, 4096, 4096): "fp8_64x128x64_adma", (16, 14336, 4096): "fp8_64x128x64_adma",
                (4, 11008, 4096): "fp8_64x128x64_adma"}
     for (M, N, K), want in expect8.items():
         for dt in (3, 4):
@@ -406,24 +407,25 @@ def test_workspace_sizes_follow_the_split_rule():
     assert L.gemm_workspace_size(16, 4096, 4096, 2) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(512, 4096, 4096, 2) == 0
     assert L.gemm_workspace_size(1024, 1024, 16384, 2) == 2 * 1024 * 1024 * 4
-    # 8-bit inputs up to 128 rows: 32 tiles, 64 K-steps of 64 -> 4 splits; K = 14336 -> 8
-    assert L.gemm_workspace_size(64, 4096, 4096, 3) == 4 * 64 * 4096 * 4
+    # 8-bit inputs up to 128 rows: 64 x 4096 x 8192 -> 8 splits of 16 K-steps of 64; K = 14336 -> 8
+    assert L.gemm_workspace_size(64, 4096, 8192, 3) == 8 * 64 * 4096 * 4
     assert L.gemm_workspace_size(16, 4096, 14336, 4) == 8 * 16 * 4096 * 4
     assert L.gemm_workspace_size(16, 14336, 4096, 3) == 2 * 16 * 14336 * 4
     # 8-bit tiles are 64 x 128: up to 64 rows each split keeps at least 16 K-steps
-    # (32 x 4096 x 4096: 4 splits), beyond that 32: 128 x 4096 x 4096 -> 2
-    assert L.gemm_workspace_size(32, 4096, 4096, 3) == 4 * 32 * 4096 * 4
+    # (32 x 8192 x 4096: 4 splits), beyond that 32: 128 x 4096 x 4096 -> 2
+    assert L.gemm_workspace_size(32, 8192, 4096, 3) == 4 * 32 * 8192 * 4
     assert L.gemm_workspace_size(128, 4096, 4096, 3) == 2 * 128 * 4096 * 4
     # 1 to 8 rows split too (8 splits of the 32 tiles of 64 x 128)
     assert L.gemm_workspace_size(8, 4096, 4096, 2) == 8 * 8 * 4096 * 4
     assert L.gemm_workspace_size(1, 4096, 4096, 1) == 8 * 1 * 4096 * 4
     # where the one-launch few-row kernel is faster: no split (16-bit K <= 2048, or
-    # K <= 4096 with N <= 2048; 8-bit up to 16 rows with K and N <= 4096)
+    # K <= 4096 with N <= 2048; 8-bit up to 64 rows with K and N <= 4096)
     for args in [(16, 2048, 2048, 2), (16, 4096, 2048, 1), (16, 2048, 4096, 2), (8, 2048, 2048, 2),
-                 (16, 4096, 4096, 3), (1, 2048, 4096, 4), (16, 3072, 3072, 3)]:
+                 (16, 4096, 4096, 3), (1, 2048, 4096, 4), (16, 3072, 3072, 3), (24, 4096, 4096, 3),
+                 (64, 4096, 4096, 3)]:
         assert L.gemm_workspace_size(*args) == 0, args
     assert L.gemm_workspace_size(16, 3072, 3072, 2) > 0
-    assert L.gemm_workspace_size(24, 4096, 4096, 3) > 0
+    assert L.gemm_workspace_size(96, 4096, 4096, 3) > 0
     # enough tiles, GEMV, fp32, K < 2048, K = 0, and 8-bit inputs beyond 128 rows: no split
     for args in [(4096, 4096, 4096, 1), (2048, 2048, 2048, 2), (256, 14336, 4096, 2),
                  (4096, 4, 4096, 2), (256, 4096, 4096, 0), (256, 4096, 4096, 3),
