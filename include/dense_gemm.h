@@ -198,8 +198,8 @@ gemm_status_t gemm_run_noalloc(gemm_handle_t h, const void* A, const void* B, vo
  * constant 100 MHz counter at entry and after its last store, and writes
  * clk = {clock0, clock1, real0, real1}: the shader clock in MHz is
  * 100 * (clock1 - clock0) / (real1 - real0).  The other kernels (generic,
- * strip, matrix-vector, short-K) leave clk untouched, so a caller clears it
- * first.  clk: device memory on the handle's device, 8-byte aligned,
+ * strip, few-row, matrix-vector, short-K) leave clk untouched, so a caller
+ * clears it first.  clk: device memory on the handle's device, 8-byte aligned,
  * 4 x uint64.  Errors as gemm_run, and GEMM_ERR_INVALID_VALUE for a NULL or
  * misaligned clk.
  * ------------------------------------------------------------------------- */
