@@ -1,7 +1,8 @@
-// Few-row products in one launch, with A streamed beside B: C = A·B for up to
-// 16 rows of A (a few tokens against a weight matrix B [K, N]), fp16/bf16 or
-// 8-bit (E4M3 / E5M2, bf16 C) inputs, rows 16-byte aligned (K and N multiples
-// of 16 bytes of A's and B's rows, A, B and C 16-byte aligned).
+// Few-row products in one launch, with A streamed beside B: C = A·B for a
+// few rows of A (up to 128 tokens against a weight matrix B [K, N]),
+// fp16/bf16 or 8-bit (E4M3 / E5M2, bf16 C) inputs, rows 16-byte aligned (K
+// and N multiples of 16 bytes of A's and B's rows, A, B and C 16-byte
+// aligned).
 //
 // The product is bound by streaming B once from HBM (chapter "Fast matrix
 // multiplication", section "Decode is a different problem: GEMV": coalesced
@@ -16,9 +17,10 @@
 // owning a contiguous K range and the workgroups of an XCD starting their
 // walks at different K-steps, 7.5-8.1 us.  This kernel is the latter:
 //
-//  * one workgroup of W wavefronts owns BMS rows (16, or 8 for products of
-//    at most 8 rows, which then load half the A bytes per K-step) and a
-//    strip of BN columns of C;
+//  * one workgroup of W wavefronts owns BMS rows (16; 8 for products of at
+//    most 8 rows, which then load half the A bytes per K-step; 32 or 64 for
+//    more rows, as 2 or 4 rows of 16x16 tiles) and a strip of BN columns of
+//    C;
 //  * wavefront w owns the contiguous K-steps [w*S, (w+1)*S) and walks them
 //    starting at a step that depends on the strip (so neighbouring
 //    workgroups read different columns of A and rows of B at any moment);
