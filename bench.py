@@ -45,6 +45,13 @@ of a size sweep (square 512^3 .. 8192^3, few-row products against the HBM
 roofline, the prefill projections) and prints one JSON line per (shape,
 configuration) plus the configuration gemm_run picks; it is the measurement
 behind the shape-class table.
+
+``--sweep-fewrow`` times, on a grid of 1-128 rows against weight matrices of
+1024-14336 columns, every configuration of the few-row class (the few-row
+and strip kernels and the 64 x 128 and 128 x 128 tiles), each as replays of
+a HIP graph of 10 launches, and prints one JSON line per shape with every
+time and gemm_run's pick, then a table of the pick against the fastest
+configuration; it is the measurement behind the few-row selection rule.
 """
 from __future__ import annotations
 
@@ -193,6 +200,103 @@ SWEEP_SHORT_K = [(2048, 2048, 64), (8192, 8192, 128), (4096, 4096, 256)]
 SWEEP_FEW_COLUMNS = [(14336, 1, 4096), (4096, 1, 14336), (4096, 2, 4096), (12288, 4, 4096)]
 
 
+# the few-row selection grid: rows x (N, K) of weight matrices
+SWEEP_FEWROW_ROWS = [1, 8, 16, 24, 32, 40, 48, 64, 96, 128]
+SWEEP_FEWROW_NK16 = [(1024, 4096), (1024, 8192), (1024, 14336), (2048, 2048), (2048, 4096), (2048, 8192),
+                     (2048, 14336), (3072, 3072), (3072, 8192), (4096, 1024), (4096, 2048), (4096, 4096),
+                     (5120, 5120), (6144, 4096), (7168, 4096), (8192, 4096), (11008, 4096), (12288, 4096),
+                     (13824, 5120)]
+SWEEP_FEWROW_NK8 = [(1024, 4096), (1024, 8192), (1024, 11008), (2048, 2048), (2048, 4096), (2048, 8192),
+                    (2048, 11008), (3072, 3072), (3072, 8192), (4096, 2048), (4096, 4096), (4096, 8192),
+                    (4096, 11008), (5120, 5120), (6144, 4096), (8192, 4096), (8192, 8192), (11008, 4096)]
+SWEEP_FEWROW_TILES = ("mfma16x16_64x128x32_adma", "mfma16x16_128x128x32_adma", "mfma16x16_128x128x32",
+                      "fp8_64x128x64_adma", "fp8_128x128x64_adma", "fp8_128x128x64")
+
+
+def _graph_time_us(fn, launches=10, warm_s=0.05, replays=5) -> float:
+    """Per-launch time of `launches` calls of `fn` (which launches on torch's
+    current stream) captured in one HIP graph, replayed `replays` times after
+    `warm_s` seconds of replays."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    t_end = time.perf_counter() + warm_s
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(replays):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / (replays * launches)
+
+
+def sweep_fewrow(dtype: str) -> int:
+    """Every few-row-class configuration on the few-row grid (N(0,1) inputs,
+    8-bit ones rounded to the format; per (N, K) one draw of 128 rows of A and
+    of B, seed 300, and the first M rows of that A), one JSON line per shape,
+    then the pick against the fastest configuration per shape and overall."""
+    import math
+    import torch
+    import dense_gemm_run_amd as dg
+    from dense_gemm_run_amd import _lib
+    from dense_gemm_run_amd.inputs import make_operands
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    h = dg.gemm_create()
+    eight_bit = dtype.startswith("fp8")
+    grid = SWEEP_FEWROW_NK8 if eight_bit else SWEEP_FEWROW_NK16
+    names = {c: dg.gemm_config_info(c)["name"] for c in range(dg.gemm_config_count())}
+    cands = [c for c, n in names.items()
+             if n.startswith(("fewrow", "skinny")) or n in SWEEP_FEWROW_TILES]
+    rows = []
+    for N, K in grid:
+        A, B = make_operands(max(SWEEP_FEWROW_ROWS), N, K, dtype, "normal", 300)
+        a_all, b = A.to(dev), B.to(dev)
+        for M in SWEEP_FEWROW_ROWS:
+            a = a_all[:M].contiguous()
+            code = dg.dtype_code(a.dtype)
+            c = torch.empty((M, N), dtype=dg.out_dtype(a.dtype), device=dev)
+            pick = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, code)
+
+            def run(cid, a=a, c=c, M=M, code=code):
+                return lambda: _lib.lib().gemm_run_config(h, a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                                          M, N, K, code, cid,
+                                                          torch.cuda.current_stream().cuda_stream)
+            times = {}
+            for cid in sorted(set(cands + [pick])):
+                if run(cid)() != 0:     # this configuration refuses the shape
+                    continue
+                times[cid] = round(_graph_time_us(run(cid)), 2)
+            best = min(times, key=times.get)
+            rec = {"dtype": dtype, "M": M, "N": N, "K": K, "pick": names[pick], "pick_us": times[pick],
+                   "best": names[best], "best_us": times[best],
+                   "us": {names[k]: v for k, v in times.items()}}
+            print(json.dumps(rec), flush=True)
+            rows.append(rec)
+            del a, c
+        del a_all, b
+    dg.gemm_destroy(h)
+    ratios = [r["pick_us"] / r["best_us"] for r in rows]
+    print("\n| M x N x K | picked | us | fastest | us | picked / fastest |")
+    print("|---|---|---|---|---|---|")
+    for r, q in zip(rows, ratios):
+        print(f"| {r['M']}x{r['N']}x{r['K']} | {r['pick']} | {r['pick_us']:.2f} | {r['best']} | "
+              f"{r['best_us']:.2f} | {q:.3f} |")
+    gm = math.exp(sum(math.log(q) for q in ratios) / len(ratios))
+    print(f"\n{dtype}: {len(rows)} shapes; picked / fastest: geometric mean {gm:.4f}, "
+          f"maximum {max(ratios):.3f}; within 5 %: {sum(q <= 1.05 for q in ratios)}", flush=True)
+    return 0
+
+
 def _time_us(fn, iters, stream) -> float:
     import torch
     for _ in range(3):
@@ -323,6 +427,8 @@ def main(argv=None) -> int:
     p.add_argument("--sweep", choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2"], default=None,
                    help="time every configuration on the shape sweep instead")
     p.add_argument("--sweep-iters", type=int, default=20)
+    p.add_argument("--sweep-fewrow", choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2"], default=None,
+                   help="time the few-row-class configurations on the few-row grid instead")
     p.add_argument("--sweep-vendor", action="store_true",
                    help="with --sweep: also time the vendor library (context)")
     args = p.parse_args(argv)
@@ -335,6 +441,8 @@ def main(argv=None) -> int:
 
     if args.sweep:
         return sweep(args.sweep, args.sweep_iters, args.sweep_vendor)
+    if args.sweep_fewrow:
+        return sweep_fewrow(args.sweep_fewrow)
 
     import torch
     import dense_gemm_run_amd as dg

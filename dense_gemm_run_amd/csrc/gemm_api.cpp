@@ -271,23 +271,37 @@ int select(const Problem& p)
     }
     if (p.dtype == kFP8E4M3 || p.dtype == kFP8E5M2) {
         if (!accepts(kTable[13], p) || p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
-        if (p.M <= 64 && p.N < 10240) {
-            // few rows: the one-launch few-row kernel, 32-column strips
-            // (8-row workgroups up to 8 rows, 32-row ones from 17 rows; 16
-            // columns for K >= 8192 up to 16 rows, for more strips, and from
-            // K = 12288 up to 8 rows too).  (E4M3, graph-timed: 1-16 x 4096 x
-            // 4096 5.6-6.2 us against 6.4-7.7 on the strip kernel; 24-64 rows
-            // 6.8-8.5 against 9.0-11.2; 16 x 4096 x 14336 24.9 against 27.1;
-            // 64 x 4096 x 14336 28.3 against 42.9 on the 64 x 128 tiles; 16
-            // and 32 x 8192 x 4096 10.9 and 11.8 against 12.2 and 13.1.)  From
-            // 65 rows and from N = 10240 the tiled rules below pick the 64 x
-            // 128 tiles (96-128 x 4096 x 4096: 10.4 us against 17.5; 4 x 11008
-            // x 4096: 12.5 against 14.8; 16 x 14336 x 4096: 14.2 against
-            // 17.9).
-            if (p.M <= 16 && p.K >= 12288) return 52;
-            if (p.M <= 8) return 55;
-            if (p.M <= 16) return p.K >= 8192 ? 52 : 53;
-            return 60;
+        // Few rows: the one-launch few-row kernel wherever one of its
+        // configurations fits one wave (at most 256 workgroups, one per CU: a
+        // partial second wave costs about as much as the first); else the
+        // tiled rules below (the 64 x 128 tiles).  Per row count (E4M3,
+        // graph-timed):
+        //  * up to 16 rows: 32-column strips, of 8 rows up to 8 rows (1-16 x
+        //    4096 x 4096 5.6-6.2 us against 6.4-7.7 on the strip kernel), and
+        //    16-column strips of 16 rows where K >= 8192 and they number
+        //    129-256 (1-16 x 3072 x 8192 11.8-12.5 against 17.4-18.6 on 32
+        //    columns; 16 x 4096 x 11008 19.9 against 21.7);
+        //  * 17-32 rows: two row blocks of 16 rows where they fill at most
+        //    192 CUs, or 256 from K = 8192 (24-32 x 1024 x 4096 5.3 against
+        //    6.0 on 32-row workgroups, 24-32 x 3072 x 8192 15.7 against 19.7),
+        //    else one of 32 rows (24-32 x 4096 x 4096 7.1 against 7.8);
+        //  * 33-64 rows: row blocks of 16 where they fill at most 192 CUs and K
+        //    < 8192 (40 x 2048^2 4.7 against 5.1; from K = 8192 three or more
+        //    blocks of 16 rows run up to 1.9 times slower), else of 32 rows;
+        //  * 65-128 rows: row blocks of 32 (96-128 x 2048 x 4096 7.3-8.1
+        //    against 10.7 on the 64 x 128 tiles);
+        //  * more workgroups than one wave: the 64 x 128 tiles (40-64 x 6144
+        //    x 4096 13.8-15.1 against 16.8-17.6 on 384 workgroups; 1-16 x 11008
+        //    x 4096 12.9-13.0 against 15.5-16.9).
+        const int64_t s16 = (p.N + 15) / 16 * p.batch, s32 = (p.N + 31) / 32 * p.batch;
+        if (p.M <= 16) {
+            if (p.K >= 8192 && s16 > 128 && s16 <= 256) return 52;
+            if (s32 <= 256) return p.M <= 8 ? 55 : 53;
+        } else if (p.M <= 128) {
+            const int64_t r16 = (p.M + 15) / 16 * s32, r32 = (p.M + 31) / 32 * s32;
+            if (p.M <= 32 && (r16 <= 192 || (r16 <= 256 && p.K >= 8192))) return 53;
+            if (p.M <= 64 && p.K < 8192 && r16 <= 192) return 53;
+            if (r32 <= 256) return 60;
         }
         // at most 4 K-steps of 64: 128 x 128 tiles with A through registers,
         // for the same reason as the 16-bit short-K rule below (E4M3,
@@ -324,42 +338,62 @@ int select(const Problem& p)
     if (!accepts(kTable[6], p)) return 0;
     if (p.M * p.N * p.K * p.batch < (int64_t)128 * 128 * 128) return 0;
     if (p.M <= 128) {
-        // Few rows: the one-launch few-row kernel (A streamed beside B), with
-        // workgroups of as many rows as keep about one workgroup per CU:
-        //  * up to 16 rows below N = 8192: 16-column strips with 64-deep
-        //    K-steps, 8-row workgroups up to 8 rows (32-column strips where
-        //    K <= 2048 leaves each wavefront few steps);
-        //  * up to 32 rows otherwise: 32-column strips of 16 rows, or of 32
-        //    rows from N = 8192 (17-32 rows);
-        //  * 33-64 rows: 32 x 32 below N = 8192, 64 x 32 up to N = 12288;
-        //  * 65-128 rows below N = 8192: 64 x 32;
-        //  * up to 32 rows from N = 12288 (K >= 1024) the 64 x 128 tiles while
-        //    they fit one wave, whose one pass already has enough workgroups;
-        //    the wider rows of 33-128 rows go to the tile rules below.
-        // (bf16, graph-timed: 1-16 x 4096 x 4096 7.4-8.8 us against 8.9-12.0
-        // on the strip kernel; 16 x 4096 x 14336 32.6 against 37.2; 24 and 32
-        // x 4096 x 4096 11.0 and 11.6 against 12.4 and 13.1; 32 x 8192 x 4096
-        // 15.1 on 32-row workgroups against 20.2 on 16-row ones; 48 and 64 x
-        // 4096 x 4096 13.1 and 13.9 against 15.7 and 17.0; 96 and 128 x 4096
-        // x 4096 16.5 and 18.1 against 20.6 and 22.5; 64 x 8192 x 4096 18.2
-        // against 22.7 on the tiles; 128 x 4096 x 14336 54.3 against 68.7;
-        // 16 x 14336 x 4096 23.2 on the tiles against 24.7 and 26.6.)
-        const bool wide = p.N >= 8192;
-        if (p.M <= 32) {
-            if (p.N >= 12288 && (p.N + 127) / 128 * p.batch <= 256) {
-                if (p.K >= 1024) return 37;
-                return p.M <= 16 ? 18 : 19;
-            }
-            if (p.M <= 16 && !wide) {
+        // Few rows: the one-launch few-row kernel (A streamed beside B)
+        // wherever one of its configurations fits one wave (at most 256
+        // workgroups, one per CU: a partial second wave costs about as much
+        // as the first), with as many workgroups as that allows, mostly.
+        // Per row count (bf16, graph-timed):
+        //  * up to 16 rows: 16-column strips with 64-deep K-steps, of 8 rows
+        //    up to 8 rows (1-16 x 4096 x 4096 7.8-9.2 us against 8.9-12.0 on
+        //    the strip kernel; 16 x 4096 x 14336 32.6 against 37.2), 32-deep
+        //    where K <= 3072 (1-16 x 3072^2 7.4-8.1 against 7.5-8.2), and
+        //    32-column strips where K <= 2048 from N = 4096 or where 16
+        //    columns take more than 256 workgroups (1-16 x 6144 x 4096
+        //    12.6-14.1 against 16.9-18.8 on 384 workgroups); up to 8 rows
+        //    also up to 384 strips of 32 (1 x 11008 x 4096 21.0 against 23.3
+        //    on the 64 x 128 tiles);
+        //  * 17-32 rows: two row blocks of 16 x 16 from K = 8192 (24-32 x
+        //    2048 x 8192 16.2-16.7 against 17.6-18.5 on 16 x 32), else of 16 x
+        //    32 (24-32 x 4096 x 4096 11.4-11.8 against 12.7-13.2 on 32 x 32),
+        //    else one of 32 x 32 (24-32 x 6144 x 4096 15.7-16.5 against
+        //    19.9-21.0);
+        //  * 33-64 rows: row blocks of 16 x 32 where K <= 3072 (40-48 x 2048^2
+        //    5.8-5.9 against 6.3-6.4 on 32 x 32), two of 32 x 16 from K = 8192
+        //    (40 x 2048 x 8192 19.2 against 20.2), else of 32 x 32, else
+        //    one of 64 x 32 (40-64 x 6144 x 4096 18.1-20.5 against 21.9-24.9
+        //    on 384 workgroups of 32 x 32);
+        //  * 65-128 rows: two row blocks of 64 x 32 (96-128 x 4096 x 4096
+        //    16.9-18.6 against 22.5-23.6 on the 64 x 128 tiles);
+        //  * more workgroups than one wave: the 64 x 128 tiles where they fit
+        //    one (96-128 x 6144 x 4096 23.0-25.3 against 28.5-32.1 on 384
+        //    workgroups of 64 x 32; 24-64 x 11008 x 4096 23.5-25.5 against
+        //    25.9-35.4), through the tile rules below from 33 rows; up to 32
+        //    rows below K = 1024 the strip kernel, and the few-row kernel in
+        //    several waves where the tiles do not fit one either.
+        const int64_t s16 = (p.N + 15) / 16 * p.batch, s32 = (p.N + 31) / 32 * p.batch;
+        if (p.M <= 16) {
+            if (s16 <= 256) {
                 if (p.K <= 2048 && p.N >= 4096) return 51;
-                // up to 8 rows, workgroups of 8 rows load half the A bytes
-                // (1-8 x 4096 x 4096: 7.4-8.2 against 7.9-8.5 us)
+                if (p.K <= 3072) return 49;
                 return p.M <= 8 ? 54 : 50;
             }
-            return p.M > 16 && wide ? 57 : 51;
+            if (s32 <= 256 || (p.M <= 8 && s32 <= 384)) return 51;
+        } else if (p.M <= 32) {
+            if (p.K >= 8192 && 2 * s16 <= 256) return 50;
+            if (2 * s32 <= 256) return 51;
+            if (s32 <= 256) return 57;
+        } else if (p.M <= 64) {
+            if (p.K <= 3072 && (p.M + 15) / 16 * s32 <= 256) return 51;
+            if (p.K >= 8192 && 2 * s16 <= 256) return 56;
+            if (2 * s32 <= 256) return 57;
+            if (s32 <= 256) return 59;
+        } else if (2 * s32 <= 256) {
+            return 59;
         }
-        if (!wide) return p.M <= 64 ? 57 : 59;
-        if (p.M <= 64 && p.N < 12288) return 59;
+        if (p.M <= 32) {
+            if ((p.N + 127) / 128 * p.batch <= 256) return p.K >= 1024 ? 37 : p.M <= 16 ? 18 : 19;
+            return p.M <= 16 ? 51 : 57;
+        }
     }
     // At most 128 K and at least 1024 tiles of 128 x 128: the persistent
     // short-K kernel, whose workgroups load their next tile while they store

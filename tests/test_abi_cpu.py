@@ -311,19 +311,28 @@ def test_few_rows_select_the_few_row_kernels():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
     name = lambda *args: dg.gemm_config_info(dg.gemm_select_config(*args))["name"]
-    # 16-bit: the one-launch few-row kernel (16-, 32- and 64-row workgroups),
-    # the 64 x 128 tiles for wide B, the strip kernel for wide B with short K
+    # 16-bit: the one-launch few-row kernel (8-, 16-, 32- and 64-row
+    # workgroups) in configurations that fit one wave of 256 workgroups, the
+    # 64 x 128 tiles where none does, the strip kernel for wide B with short K
     expect16 = {(16, 4096, 4096): "fewrow_16x16x64", (1, 4096, 4096): "fewrow_8x16x64",
                 (8, 4096, 14336): "fewrow_8x16x64", (9, 4096, 4096): "fewrow_16x16x64",
                 (16, 4096, 14336): "fewrow_16x16x64", (16, 4096, 2048): "fewrow_16x32x32",
-                (16, 2048, 2048): "fewrow_16x16x64", (32, 4096, 4096): "fewrow_16x32x32",
+                (16, 2048, 2048): "fewrow_16x16x32", (1, 3072, 3072): "fewrow_16x16x32",
+                (32, 4096, 4096): "fewrow_16x32x32",
                 (24, 4096, 4096): "fewrow_16x32x32", (16, 8192, 4096): "fewrow_16x32x32",
                 (16, 14336, 4096): "mfma16x16_64x128x32_adma", (32, 14336, 4096): "mfma16x16_64x128x32_adma",
                 (16, 14336, 512): "skinny_16x32x64", (16, 65536, 4096): "fewrow_16x32x32",
                 (16, 32768, 4096): "mfma16x16_64x128x32_adma", (32, 8192, 4096): "fewrow_32x32x32",
                 (48, 4096, 4096): "fewrow_32x32x32", (64, 4096, 4096): "fewrow_32x32x32",
                 (64, 8192, 4096): "fewrow_64x32x32", (96, 4096, 4096): "fewrow_64x32x32",
-                (128, 4096, 4096): "fewrow_64x32x32", (128, 4096, 14336): "fewrow_64x32x32"}
+                (128, 4096, 4096): "fewrow_64x32x32", (128, 4096, 14336): "fewrow_64x32x32",
+                # one wave: 192 strips of 32 columns rather than 384 of 16, and so on
+                (1, 6144, 4096): "fewrow_16x32x32", (16, 6144, 4096): "fewrow_16x32x32",
+                (24, 6144, 4096): "fewrow_32x32x32", (40, 6144, 4096): "fewrow_64x32x32",
+                (96, 6144, 4096): "mfma16x16_64x128x32_adma", (24, 11008, 4096): "mfma16x16_64x128x32_adma",
+                (1, 11008, 4096): "fewrow_16x32x32", (16, 11008, 4096): "mfma16x16_64x128x32_adma",
+                (24, 2048, 8192): "fewrow_16x16x64", (40, 2048, 8192): "fewrow_32x16x32",
+                (40, 2048, 2048): "fewrow_16x32x32"}
     for (M, N, K), want in expect16.items():
         for dt in (1, 2):
             assert name(A, Bb, Cb, M, N, K, dt) == want, (M, N, K, dt)
@@ -332,14 +341,17 @@ def test_few_rows_select_the_few_row_kernels():
                  (A, Bb, Cb, 16, 4096, 4096, 0), (A, Bb, Cb, 16, 4096, 4092, 2)]:
         n = name(*args)
         assert not n.startswith("skinny") and not n.startswith("fewrow"), args
-    # 8-bit: the 8-bit few-row configurations up to 64 rows below N = 10240
+    # 8-bit: the 8-bit few-row configurations where one fits one wave
     expect8 = {(1, 4096, 4096): "fewrow8_8x32x128", (8, 1024, 8192): "fewrow8_8x32x128",
                (8, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 4096): "fewrow8_16x32x128",
                (32, 4096, 4096): "fewrow8_32x32x128", (16, 8192, 4096): "fewrow8_16x32x128",
                (16, 4096, 14336): "fewrow8_16x16x128", (16, 4096, 8192): "fewrow8_16x16x128",
-               (64, 4096, 4096): "fewrow8_32x32x128", (24, 4096, 14336): "fewrow8_32x32x128",
+               (64, 4096, 4096): "fewrow8_32x32x128", (24, 4096, 14336): "fewrow8_16x32x128",
                (96, 4096, 4096): "fp8_64x128x64_adma", (16, 14336, 4096): "fp8_64x128x64_adma",
-               (4, 11008, 4096): "fp8_64x128x64_adma"}
+               (4, 11008, 4096): "fp8_64x128x64_adma", (96, 2048, 4096): "fewrow8_32x32x128",
+               (40, 6144, 4096): "fp8_64x128x64_adma", (16, 8192, 8192): "fewrow8_16x32x128",
+               (1, 3072, 8192): "fewrow8_16x16x128", (24, 1024, 4096): "fewrow8_16x32x128",
+               (40, 2048, 8192): "fewrow8_32x32x128", (40, 2048, 2048): "fewrow8_16x32x128"}
     for (M, N, K), want in expect8.items():
         for dt in (3, 4):
             assert name(A, Bb, Cb, M, N, K, dt) == want, (M, N, K, dt)

@@ -162,22 +162,28 @@ def test_full_size_sixteen_tokens_whole(dtype):
         check(A, B, dtype, c)
 
 
-@pytest.mark.parametrize("shape", [(16, 4096, 4096), (1, 4096, 4096), (24, 4096, 4096), (16, 4096, 14336),
-                                   (16, 8192, 4096), (16, 4096, 2048), (32, 8192, 4096), (48, 4096, 4096),
-                                   (64, 2048, 4096), (96, 4096, 4096), (128, 4096, 4096), (100, 4096, 1000)])
-def test_few_row_shapes_in_the_selected_configuration(shape):
-    """gemm_run's choice for few rows of a B narrower than 8192 columns (and
-    up to 32 rows below 12288; 8-bit up to 64 rows below 10240) is this
-    kernel; the product is compared with the oracle whole."""
+SELECTED16 = [(16, 4096, 4096), (1, 4096, 4096), (24, 4096, 4096), (16, 4096, 14336), (16, 8192, 4096),
+              (16, 4096, 2048), (32, 8192, 4096), (48, 4096, 4096), (64, 2048, 4096), (96, 4096, 4096),
+              (128, 4096, 4096), (100, 4096, 1000), (1, 6144, 4096), (40, 6144, 4096), (24, 2048, 8192),
+              (40, 2048, 8192), (1, 11008, 4096), (3, 3072, 3072)]
+SELECTED8 = [(16, 4096, 4096), (1, 4096, 4096), (24, 4096, 4096), (16, 4096, 14336), (16, 8192, 4096),
+             (16, 4096, 2048), (32, 8192, 4096), (48, 4096, 4096), (64, 2048, 4096), (96, 2048, 4096),
+             (1, 3072, 8192), (24, 1024, 4096), (40, 2048, 2048)]
+
+
+@pytest.mark.parametrize("dtype,shape", [("bf16", s) for s in SELECTED16] + [("fp8_e4m3", s) for s in SELECTED8])
+def test_few_row_shapes_in_the_selected_configuration(dtype, shape):
+    """gemm_run's choice for few rows where one of the kernel's configurations
+    fits one wave of workgroups (up to 8 rows, 16-bit, also 11008 columns in
+    344 strips) is this kernel; the product is compared with the oracle
+    whole."""
     M, N, K = shape
-    for dtype, code in (("bf16", 2), ("fp8_e4m3", 3)):
-        if code == 3 and M > 64:
-            continue
-        A, B = make_operands(M, N, K, dtype, "prefill" if code == 2 else "normal", 770 + M)
-        a, b = A.cuda(), B.cuda()
-        c = dg.gemm(a, b)
-        torch.cuda.synchronize()
-        cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, code)
-        note(f"[fewrow] selected {dg.gemm_config_info(cid)['name']} for {dtype} {shape}")
-        assert dg.gemm_config_info(cid)["name"].startswith("fewrow")
-        check(A, B, dtype, c)
+    code = 3 if dtype.startswith("fp8") else 2
+    A, B = make_operands(M, N, K, dtype, "prefill" if code == 2 else "normal", 770 + M)
+    a, b = A.cuda(), B.cuda()
+    c = dg.gemm(a, b)
+    torch.cuda.synchronize()
+    cid = dg.gemm_select_config(a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K, code)
+    note(f"[fewrow] selected {dg.gemm_config_info(cid)['name']} for {dtype} {shape}")
+    assert dg.gemm_config_info(cid)["name"].startswith("fewrow")
+    check(A, B, dtype, c)
