@@ -230,13 +230,13 @@ bool accepts(const Entry& e, const Problem& p)
 // few-row products and the prefill projections):
 //  * N <= 4: the matrix-vector kernel (it streams A at HBM bandwidth);
 //  * M <= 128 (few rows, B streamed once): kernels of N/16 or N/32
-//    workgroups, one per strip of B's columns, which fill the chip where the
-//    tiled kernels have a few dozen tiles (M = 16, N = K = 4096: 44 against
-//    18 TFLOP/s) - up to 32 rows the one-launch few-row kernel (A streamed
-//    beside B) below N = 12288 (10240 for 8-bit inputs), the 64 x 128 tiles
-//    above; from 33 rows the same kernel with 32- and 64-row workgroups for
-//    N < 8192 (33-64 rows up to N = 12288; 8-bit inputs: 33-64 rows below
-//    N = 10240), the tiles for wider B;
+//    workgroups per row block, one per strip of B's columns, which fill the
+//    chip where the tiled kernels have a few dozen tiles (M = 16, N = K =
+//    4096: 44 against 18 TFLOP/s) - the one-launch few-row kernel (A
+//    streamed beside B) in the workgroup shape that fills the most CUs
+//    within one wave of 256 workgroups, the 64 x 128 tiles where no shape
+//    fits one wave (the rules below, from a sweep over 1-128 rows, bench.py
+//    --sweep-fewrow);
 //  * fp32 with 16-byte rows: the fp32 MFMA kernel (128 x 128 tiles from 1024
 //    of them, else 64 x 64);
 //  * K <= 128 over at least 1024 tiles of 128 x 128: the persistent short-K
