@@ -360,6 +360,36 @@ def test_few_rows_select_the_few_row_kernels():
         assert not n.startswith("skinny") and not n.startswith("fewrow"), (M, N, K)
 
 
+def test_few_row_picks_fit_one_wave():
+    """Over a grid of 1-128 rows, the few-row kernel is picked in a shape
+    whose workgroups fit one wave of 256 (one per CU) whenever one of its
+    shapes does; more only up to 8 rows (16-bit, at most 384 strips of 32
+    columns) and up to 32 rows where the 64 x 128 tiles do not fit one wave
+    either."""
+    Cb = C + (1 << 34)
+    Bb = A + (1 << 33)
+    cd = lambda a, b: -(-a // b)
+    fewrow = {c: dg.gemm_config_info(c) for c in range(dg.gemm_config_count())
+              if dg.gemm_config_info(c)["name"].startswith("fewrow")}
+    for dt in (2, 3):
+        eight = dt == 3
+        shapes_ok = [c for c, i in fewrow.items() if (i["dtype_mask"] == 0x18) == eight]
+        for M in (1, 5, 8, 9, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128):
+            for N in (512, 1024, 2048, 3072, 4096, 5120, 6144, 8192, 11008, 12288, 14336, 28672):
+                for K in (1024, 2048, 4096, 8192, 14336):
+                    cid = dg.gemm_select_config(A, Bb, Cb, M, N, K, dt)
+                    fits = [c for c in shapes_ok
+                            if cd(M, fewrow[c]["bm"]) * cd(N, fewrow[c]["bn"]) <= 256]
+                    if cid in fewrow:
+                        wgs = cd(M, fewrow[cid]["bm"]) * cd(N, fewrow[cid]["bn"])
+                        assert (wgs <= 256 or (not eight and M <= 8 and wgs <= 384)
+                                or (not fits and M <= 32 and cd(N, 128) > 256)), (M, N, K, dt, wgs)
+                    elif fits:
+                        # a one-wave few-row shape exists: only the generic kernel
+                        # (tiny products) may take its place
+                        assert cid == 0 and M * N * K < 128 ** 3, (M, N, K, dt, cid)
+
+
 def test_192_row_tiles_where_256_leaves_a_partial_wave():
     Cb = C + (1 << 34)
     Bb = A + (1 << 33)
