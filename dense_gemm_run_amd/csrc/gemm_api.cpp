@@ -132,6 +132,10 @@ const Entry kTable[] = {
     {{58, 64, 16, 32, 2, 512, 0x6, 1, 1, "fewrow_64x16x32"}, kFewRow},
     {{59, 64, 32, 32, 2, 256, 0x6, 1, 1, "fewrow_64x32x32"}, kFewRow},
     {{60, 32, 32, 128, 2, 256, 0x18, 1, 1, "fewrow8_32x32x128"}, kFewRow},
+    // the 16x16x32 kernel at 256 x 256 with A staged two K-steps at a time
+    // (whole cache lines per A load)
+    {{61, 256, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_256x256x32_apair", 2}, kMfma16x16},
+    {{62, 192, 256, 32, 4, 256, 0x6, 1, 1, "mfma16x16_192x256x32_apair", 2}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -252,7 +256,8 @@ bool accepts(const Entry& e, const Problem& p)
 //  * otherwise the 16x16x32 kernel at 128 x 128, which gives 4x the tiles
 //    (2048^3: 842 TFLOP/s against 383 at 256 x 256);
 //  * each of these tiled choices in its variant with A loaded direct to
-//    LDS (configs 29-31).
+//    LDS (configs 29-31), the 256 x 256 and 192 x 256 ones with A staged two
+//    K-steps at a time (configs 61, 62).
 // The 32x32x16 configurations and the 256 x 128 tiles were never the fastest
 // in the sweep and stay available through gemm_run_config.
 int select(const Problem& p)
@@ -425,12 +430,18 @@ int select(const Problem& p)
     const int64_t t192 = ((p.M + 191) / 192) * ((p.N + 255) / 256) * p.batch;
     const int64_t w256 = (t256 + 255) / 256, w192 = (t192 + 255) / 256;
     const bool rows192 = w192 * 80 < w256 * 95;
-    // A direct to LDS (one ring with B), also where the operands overflow the
-    // 256 MB Infinity Cache: with its loads spread over the K-step it leads
-    // the A-through-registers configuration there too (bf16
-    // 8192 x 4096 x 14336: 676 against 709 us in the kernel trace; 4096^3:
-    // 105 against 110 us)
-    return rows192 ? 31 : 29;
+    // A direct to LDS, staged two K-steps at a time so that every A load
+    // reads whole cache lines (configs 61, 62), also where the operands
+    // overflow the 256 MB Infinity Cache.  Median of five 200-step blocks
+    // against the one-K-step A ring (29, 31), same box, alternating: fp16
+    // 4096^3 1352-1358 against 1318-1320 TFLOP/s, bf16 8192^3 1524-1528
+    // against 1507, the prefill projections QKV 1454 against 1430, out
+    // 1424-1435 against 1406-1412, up 1437-1439 against 1415-1416, down
+    // 1463-1465 against 1430, batched 16 x 2048^3 1361-1363 against 1344-1345,
+    // 3072^3 on 192 x 256 tiles 1131-1141 against 1107-1121.  (The ring with
+    // A direct to LDS led the A-through-registers configuration by 3-5 % on
+    // the same products.)
+    return rows192 ? 62 : 61;
 }
 
 // ---- split K (gemm_run_ws)

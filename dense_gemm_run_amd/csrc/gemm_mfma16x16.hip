@@ -560,6 +560,262 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_kernel(
     clock_sample(clk, 1);
 }
 
+// A staged two K-steps at a time (256 x 256 tiles, fp16/bf16, one product per
+// workgroup, no split): otherwise the schedule of the A-direct kernel above.
+//
+// A 32-deep K-step of A is 64 bytes of each of the tile's rows, so a 1 KB
+// load of it covers 16 rows and touches 16 cache lines for half their bytes;
+// staging A for two K-steps at once makes each row 128 bytes and each load
+// 8 whole lines, as B's loads already are (a copy of the A-direct kernel
+// whose A loads read whole aligned lines in this pattern ran 94.7-94.9
+// against 97.3-97.5 us at 4096^3 on MI355X, same box, alternating).
+//
+//  * LDS: two A slots of [BM][64] (128-byte rows, 16-byte pieces XOR-ed by
+//    (row/2)%8, the layout of the 64-deep K-step kernels), slot p%2 for the
+//    K-steps 2p, 2p+1; four B stages of [32][BN] (B's layout above), stage
+//    s%4 for K-step s.  128 KB at 256 x 256, as the A-direct ring.
+//  * Loads: every half K-step issues the same number of loads per
+//    wavefront, spread over its MFMAs.  K-step it (odd): before its barrier,
+//    B of K-step it+3; after it, the first half of the A pair of K-steps
+//    it+3, it+4.  K-step it (even): before its barrier, the second half of
+//    the A pair of K-steps it+2, it+3; after it, B of K-step it+3.  A stage
+//    or slot is refilled only after the barrier that follows the last read of
+//    its previous contents.
+//  * Counted waits: before barrier it the wavefront's loads for K-step it+1
+//    (whose fragments are read after the barrier) must have landed, which
+//    leaves 2*B_LOADS of its loads in flight for odd it and B_LOADS + A_LOADS
+//    for even it (A_LOADS per half pair).  Measured on MI355X, requiring the
+//    loads half a K-step earlier than the A-direct ring does cost nothing.
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_mfma16x16_pair_kernel(
+    const T* A, const T* B, T* C, int M, int N, int K, int group_m, int xcd_remap, Batch bt, unsigned long long* clk)
+{
+    clock_sample(clk, 0);
+    constexpr int NW = 4, BK = 32;
+    constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block (2 x 2 wavefronts)
+    constexpr int FM = WM / 16, FN = WN / 16;
+    constexpr int NT = FM * FN;                  // MFMAs per wavefront per K-step
+    constexpr int BAR = NT / 2;                  // MFMAs of a K-step before its barrier
+    constexpr int ROW_P = 2 * BK * 2;            // bytes of an A row of a K-step pair
+    constexpr int PAIR_BYTES = BM * ROW_P;
+    constexpr int ROW_B = BN * 2;
+    constexpr int B_BYTES = BK * ROW_B;
+    constexpr int A_LOADS2 = PAIR_BYTES / 1024 / NW;   // A loads per wavefront per pair
+    constexpr int AH = A_LOADS2 / 2;                    // ... per half pair
+    constexpr int B_LOADS = B_BYTES / 1024 / NW;        // B loads per wavefront per K-step
+    constexpr int NR = FM + FN;                         // operand fragments per K-step
+    static_assert(AH >= 1 && A_LOADS2 % 2 == 0 && B_LOADS >= 1, "tile too small");
+    static_assert(ROW_B % 256 == 0, "B rows must be whole bank windows");
+    static_assert(2 * PAIR_BYTES + 4 * B_BYTES <= 160 * 1024, "LDS");
+    // Every slot and stage is an LDS object of its own (the compiler tracks
+    // direct-to-LDS loads per object).
+    __shared__ __attribute__((aligned(1024))) unsigned char pa0[PAIR_BYTES], pa1[PAIR_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char pb0[B_BYTES], pb1[B_BYTES], pb2[B_BYTES], pb3[B_BYTES];
+    auto a_slot = [&](int p) __attribute__((always_inline)) { return (lds_byte*)(p == 0 ? pa0 : pa1); };
+    auto b_stage = [&](int st) __attribute__((always_inline)) {
+        return (lds_byte*)(st == 0 ? pb0 : st == 1 ? pb1 : st == 2 ? pb2 : pb3);
+    };
+
+    const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, xcd_remap != 0, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K * 2u);
+
+    // A load j of a pair (j < A_LOADS2): 1 KB = 8 rows of 128 bytes; lane ->
+    // row 8*(wave*A_LOADS2 + j) + lane/8, physical piece lane%8 holding
+    // logical piece (lane%8) ^ swz_a<64>(row): global (m0+row)*K + k0 + 8*piece
+    // (kOOB for rows >= M and, per pair, pieces at or past K).
+    unsigned a_voff[A_LOADS2];
+    int a_kp[A_LOADS2];
+#pragma unroll
+    for (int j = 0; j < A_LOADS2; ++j) {
+        const int row = 8 * (wave * A_LOADS2 + j) + lane / 8;
+        const int piece = (lane % 8) ^ swz_a<2 * BK>(row);
+        a_voff[j] = (m0 + row) < M ? ((unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 8u) * 2u : kOOB;
+        a_kp[j] = piece * 8;
+    }
+    // B load j of a K-step: as in the kernel above.
+    unsigned b_voff[B_LOADS];
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+        const int byte = 1024 * (wave * B_LOADS + j) + lane * 16;
+        const int k = byte / ROW_B;
+        const int piece = ((byte % ROW_B) / 16) ^ swz_b<BN>(k);
+        const int col = n0 + piece * 8;
+        b_voff[j] = col < N ? ((unsigned)k * (unsigned)N + (unsigned)col) * 2u : kOOB;
+    }
+    // A pair starting at K k0_in, load j -> slot p.
+    auto load_a = [&](int p, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (void __attribute__((address_space(3)))*)(a_slot(p) + (wave * A_LOADS2 + j) * 1024), 16, off,
+            (k0 < K ? k0 : 0) * 2, 0, 0);
+    };
+    // B rows of the K-step at k0_in, load j -> stage st.
+    auto load_b = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const int krem = K - k0;
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
+        const __amdgpu_buffer_rsrc_t rbk =
+            make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N * 2u);
+        const unsigned off = b_voff[j];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rbk, (void __attribute__((address_space(3)))*)(b_stage(st) + (wave * B_LOADS + j) * 1024), 16, off, 0,
+            0, 0);
+    };
+
+    // Operand reads: A fragment of K-step h of a pair (h = 0, 1), tile bi:
+    // row wm*WM + 16*bi + lane%16, logical piece 4*h + lane/16; B as above.
+    int a_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        a_rd[h] = (wm * WM + (lane & 15)) * ROW_P + (((4 * h + (lane >> 4)) ^ swz_a<2 * BK>(lane & 15)) * 16);
+    int b_rd[FN];
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) {
+        const int g16 = lane & 15;
+        const int k = 8 * (lane >> 4) + (g16 >> 2);
+        const int n = wn * WN + 16 * bj + 4 * (g16 & 3);
+        const int piece = (n >> 3) ^ swz_b<BN>(k);
+        b_rd[bj] = k * ROW_B + piece * 16 + (n & 7) * 2;
+    }
+    f32x4 acc[FM][FN];
+    u32x4 fa[2][FM], fb[2][FN];
+    // Fragment o of K-step s's operands (B tiles first, then A tiles) ->
+    // register set `set`; s's pair slot is (s/2)%2, its half s%2, its B
+    // stage s%4 (all literals below).
+    auto read_frag = [&](int set, int slot, int h, int stb, int o) __attribute__((always_inline)) {
+        if (o < FN) {
+            const lds_byte* p = b_stage(stb) + b_rd[o];
+            const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)p);
+            const s16x4 h1 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p + 4 * ROW_B));
+            fb[set][o] = __builtin_bit_cast(u32x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            fa[set][o - FN] = *(const u32x4 __attribute__((address_space(3)))*)(a_slot(slot) + a_rd[h] +
+                                                                                (o - FN) * 16 * ROW_P);
+        }
+    };
+
+    // ---- prologue: what K-steps -3 .. -1 would have issued: the A pair of
+    // K-steps 0, 1 (slot 0), B of K-steps 0, 1, 2, the first half of the A
+    // pair of K-steps 2, 3 (slot 1).  Then K-step 0's operands: the A pair
+    // (0, 1) and B of K-step 0 must have landed.
+#pragma unroll
+    for (int j = 0; j < A_LOADS2; ++j) load_a(0, 0, j);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+        for (int j = 0; j < B_LOADS; ++j) load_b(s, s * BK, j);
+        asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int j = 0; j < AH; ++j) load_a(1, 2 * BK, j);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * B_LOADS + AH));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int o = 0; o < NR; ++o) read_frag(0, 0, 0, 0, o);
+
+    auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
+    // K-step it (q = it % 4): MFMAs 0 .. BAR-1 with this half's loads, the
+    // counted wait and the barrier, then MFMAs BAR .. NT-1 with the second
+    // half's loads and the operand reads of K-step it+1 (loads at evenly
+    // spaced operations, reads in between).
+    auto kstep = [&](auto q_c, int it, const bool first) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        constexpr int set = q & 1;
+        constexpr int n1 = (q & 1) ? B_LOADS : AH;   // odd: B of it+3; even: A pair (it+2, it+3), 2nd half
+        constexpr int n2 = (q & 1) ? AH : B_LOADS;   // odd: A pair (it+3, it+4), 1st half; even: B of it+3
+        constexpr unsigned kWaitBar = waitcnt_vm((q & 1) ? 2 * B_LOADS : B_LOADS + 2 * AH);
+        auto load1 = [&](int o) __attribute__((always_inline)) {
+            if (q & 1)
+                load_b((q + 3) % 4, (it + 3) * BK, o);
+            else
+                load_a((q / 2 + 1) % 2, (it + 2) * BK, AH + o);
+        };
+        auto load2 = [&](int o) __attribute__((always_inline)) {
+            if (q & 1)
+                load_a(((q + 3) / 2) % 2, (it + 3) * BK, o);
+            else
+                load_b((q + 3) % 4, (it + 3) * BK, o);
+        };
+        auto mfma = [&](int x) __attribute__((always_inline)) {
+            if (first)
+                Mfma16x16<T>::first(acc[x / FN][x % FN], fb[set][x % FN], fa[set][x / FN]);
+            else
+                Mfma16x16<T>::acc(acc[x / FN][x % FN], fb[set][x % FN], fa[set][x / FN]);
+        };
+#pragma unroll
+        for (int x = 0; x < BAR; ++x) {
+            mfma(x);
+#pragma unroll
+            for (int o = op_lo(x, n1, BAR); o < op_lo(x + 1, n1, BAR); ++o) load1(o);
+        }
+        // every load of this half was issued above (keep the compiler from
+        // sinking any past the count)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitBar);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's reads of the stages done
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        constexpr int nops2 = n2 + NR;
+#pragma unroll
+        for (int x = BAR; x < NT; ++x) {
+            mfma(x);
+#pragma unroll
+            for (int o = op_lo(x - BAR, nops2, NT - BAR); o < op_lo(x + 1 - BAR, nops2, NT - BAR); ++o) {
+                const int nld = (o * n2) / nops2 + 1;   // loads at operations 0 .. o
+                if (o == 0 || (o * n2) / nops2 != ((o - 1) * n2) / nops2)
+                    load2(nld - 1);
+                else
+                    read_frag(set ^ 1, ((q + 1) / 2) % 2, (q + 1) & 1, (q + 1) % 4, o - nld);
+            }
+        }
+    };
+    // K-steps, rounded up to the 4-step unroll (the extra steps multiply the
+    // zeros their loads brought in).
+    const int nk = cdiv_i(cdiv_i(K, BK), 4) * 4;
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    using Q3 = std::integral_constant<int, 3>;
+    kstep(Q0{}, 0, true);
+    kstep(Q1{}, 1, false);
+    kstep(Q2{}, 2, false);
+    kstep(Q3{}, 3, false);
+    for (int it = 4; it < nk; it += 4) {
+        kstep(Q0{}, it, false);
+        kstep(Q1{}, it + 1, false);
+        kstep(Q2{}, it + 2, false);
+        kstep(Q3{}, it + 3, false);
+    }
+
+    // ---- epilogue: as in the kernel above (the last row of tiles was
+    // written by the most recent MFMAs; each wavefront stages its block
+    // through one B stage of its own)
+    static_assert(FN == 8, "the wait below lists the last row's tiles");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]),
+                   "+a"(acc[FM - 1][4]), "+a"(acc[FM - 1][5]), "+a"(acc[FM - 1][6]), "+a"(acc[FM - 1][7]));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    constexpr int RP_MAX = B_BYTES / (WN * 2);
+    constexpr int RP = WM % RP_MAX == 0 ? RP_MAX : WM % 48 == 0 && RP_MAX >= 48 ? 48 : 16;
+    store_c_block<T, WM, WN, RP * WN * 2>(acc, b_stage(wave), lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
+    clock_sample(clk, 1);
+}
+
 template <typename T>
 hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
 {
@@ -569,6 +825,18 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
+    if (cfg.sched == 2) {   // A staged two K-steps at a time: 256 x 256 or 192 x 256, one pass only
+        if (a.splits > 1 || cfg.bn != 256 || cfg.bk != 32) return hipErrorInvalidValue;
+        if (cfg.bm == 256)
+            hipLaunchKernelGGL((gemm_mfma16x16_pair_kernel<T, 256, 256>), grid, block, 0, a.stream, A, B, C, a.M,
+                               a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else if (cfg.bm == 192)
+            hipLaunchKernelGGL((gemm_mfma16x16_pair_kernel<T, 192, 256>), grid, block, 0, a.stream, A, B, C, a.M,
+                               a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 only
         if (a.splits > 1) {
             if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 32)

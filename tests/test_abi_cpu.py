@@ -397,15 +397,15 @@ def test_192_row_tiles_where_256_leaves_a_partial_wave():
     # 144 tiles of 256 x 256 -> one wave of 192 x 256; 576 (2.25 waves) -> 768 (3 whole waves)
     for M, N, K in [(3072, 3072, 3072), (6144, 6144, 6144)]:
         for dt in (1, 2):
-            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_192x256x32_adma", (M, N, K)
+            assert name(A, Bb, Cb, M, N, K, dt) == "mfma16x16_192x256x32_apair", (M, N, K)
     # whole waves of 256 x 256 tiles keep them
     for M, N, K in [(4096, 4096, 4096), (8192, 8192, 8192), (8192, 12288, 4096), (8192, 14336, 4096),
                     (5120, 5120, 5120)]:
-        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_256x256x32_adma", (M, N, K)
+        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_256x256x32_apair", (M, N, K)
     # operands beyond the 256 MB Infinity Cache: A direct to LDS as well
-    assert name(A, Bb, Cb, 8192, 4096, 14336, 2) == "mfma16x16_256x256x32_adma"
-    assert name(A, Bb, Cb, 12288, 12288, 12288, 2) == "mfma16x16_256x256x32_adma"
-    assert name(A, Bb, Cb, 6144, 6144, 16384, 2) == "mfma16x16_192x256x32_adma"
+    assert name(A, Bb, Cb, 8192, 4096, 14336, 2) == "mfma16x16_256x256x32_apair"
+    assert name(A, Bb, Cb, 12288, 12288, 12288, 2) == "mfma16x16_256x256x32_apair"
+    assert name(A, Bb, Cb, 6144, 6144, 16384, 2) == "mfma16x16_192x256x32_apair"
     # fewer than 128 tiles: 128 x 128, A direct to LDS
     assert name(A, Bb, Cb, 2048, 2048, 2048, 1) == "mfma16x16_128x128x32_adma"
     info = dg.gemm_config_info(28)
@@ -549,7 +549,7 @@ def test_short_k_selects_128x128_tiles_with_a_through_registers():
     info = dg.gemm_config_info(48)
     assert (info["bm"], info["bn"], info["bk"], info["dtype_mask"], info["threads"]) == (128, 128, 128, 6, 256)
     # from K = 264 on, the tile-count rules again
-    assert name(A, Bb, Cb, 8192, 8192, 264, 2) == "mfma16x16_256x256x32_adma"
+    assert name(A, Bb, Cb, 8192, 8192, 264, 2) == "mfma16x16_256x256x32_apair"
     assert name(A, Bb, Cb, 8192, 8192, 512, 3) == "fp8_256x256x64_adma"
     # few rows keep the few-row kernels, few columns the vector kernel
     assert name(A, Bb, Cb, 16, 4096, 128, 2).startswith("fewrow")

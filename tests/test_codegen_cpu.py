@@ -431,3 +431,83 @@ def test_few_row_kernel_structure(tmp_path):
         waits = {int(x) for x in re.findall(r"s_waitcnt[^\n]*vmcnt\((\d+)\)", body)}
         assert waits <= {t * per_step for t in range(4)}, (name, sorted(waits), per_step)
         assert 3 * per_step in waits, (name, sorted(waits))
+
+
+# ---- the 16x16x32 kernel with A staged two K-steps at a time
+
+@pytest.fixture(scope="module")
+def pair_kernels(tmp_path_factory):
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    out = tmp_path_factory.mktemp("asm_pair") / "m16.s"
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_mfma16x16.hip"),
+                        "-o", str(out)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = out.read_text().split("\n")
+    found = {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_Z\S*gemm_mfma16x16_pair_kernel\S*?Li(\d+)ELi(\d+)E\S*):", l)
+        if m:
+            end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+            found[m.group(1)] = (int(m.group(2)), int(m.group(3)), lines[i:end])
+    scratch = {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^\s*\.amdhsa_kernel (\S+)", l)
+        if m and m.group(1) in found:
+            for l2 in lines[i:i + 80]:
+                m2 = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", l2)
+                if m2:
+                    scratch[m.group(1)] = int(m2.group(1))
+                    break
+    # {f16, bf16} x {256 x 256, 192 x 256}
+    assert len(found) == 4, sorted(found)
+    return found, scratch
+
+
+def test_pair_kernel_loads_and_counted_waits(pair_kernels):
+    """Per wavefront: AH = bm/64 A loads per half K-step pair and 4 B loads
+    per K-step; odd K-steps issue B before their barrier and half an A pair
+    after it, even K-steps the other half of the pair before and B after;
+    the wait before barrier it leaves 2*4 loads in flight (odd it) or
+    4 + 2*AH (even it), and the prologue 2*4 + AH."""
+    found, _ = pair_kernels
+    for name, (bm, bn, body) in found.items():
+        ah, bl = bm // 64, bn // 64
+        ev = events(body)
+        bars = [i for i, e in enumerate(ev) if e == "B"]
+        # prologue, 4 peeled K-steps, 4 in the loop body, epilogue
+        assert len(bars) == 10, (name, len(bars))
+        pro = [e for e in ev[:bars[0]] if e in ("g", "L")]
+        assert pro == ["L"] * (2 * ah + 3 * bl + ah), (name, pro)
+        pro_waits = [e[1] for e in ev[:bars[0]] if isinstance(e, tuple)]
+        assert pro_waits and pro_waits[-1] == 2 * bl + ah, (name, pro_waits)
+        for k in range(8):                     # K-step k's barrier is bars[k + 1]
+            seg = ev[bars[k] + 1:bars[k + 1]]
+            got = [e for e in seg if e in ("g", "L")]
+            q = k % 4
+            first_half = bl if q & 1 else ah
+            prev_second = 0 if k == 0 else (ah if (k - 1) & 1 else bl)
+            assert got == ["L"] * (prev_second + first_half), (name, k, got)
+            waits = [e[1] for e in seg if isinstance(e, tuple)]
+            assert waits and waits[-1] == (2 * bl if q & 1 else bl + 2 * ah), (name, k, waits)
+
+
+def test_pair_kernel_accumulators_stay_in_place_without_scratch(pair_kernels):
+    found, scratch = pair_kernels
+    for name, (bm, bn, body) in found.items():
+        assert scratch[name] == 0, (name, scratch[name])
+        text = [x.strip() for x in body]
+        mfma = [x for x in text if x.startswith("v_mfma_f32_16x16x32")]
+        per_step = (bm // 2 // 16) * (bn // 2 // 16)
+        assert len(mfma) == 8 * per_step, (name, len(mfma))
+        ops_of = lambda x: [o.strip().split()[0] for o in x.split(None, 1)[1].split(",")]
+        assert sum(1 for x in mfma if ops_of(x)[3] == "0") == per_step, name
+        for x in mfma:
+            ops = ops_of(x)
+            assert ops[3] in (ops[0], "0"), x
+        first = next(i for i, x in enumerate(text) if x.startswith("v_mfma"))
+        last = max(i for i, x in enumerate(text) if x.startswith("v_mfma"))
+        assert not [x for x in text[first:last]
+                    if x.startswith(("v_accvgpr_write", "v_accvgpr_mov", "v_accvgpr_read"))], name

@@ -169,7 +169,8 @@ def split_configs():
     out = []
     for c in range(dg.gemm_config_count()):
         n = dg.gemm_config_info(c)["name"]
-        if n.startswith("mfma16x16") and (not n.endswith("_adma") or "_128x128x" in n or "_64x128x" in n):
+        if n.startswith("mfma16x16") and not n.endswith("_apair") and (
+                not n.endswith("_adma") or "_128x128x" in n or "_64x128x" in n):
             out.append(c)
     return out
 
