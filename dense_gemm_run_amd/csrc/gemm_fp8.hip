@@ -476,6 +476,246 @@ __global__ __launch_bounds__(256, BM * BN >= 192 * 256 ? 1 : 2) void gemm_fp8_ke
     clock_sample(clk, 1);
 }
 
+// A staged two K-steps at a time (256 x 256 and 192 x 256 tiles, one product
+// per workgroup, no split): the scheme of the 16-bit A-pair kernel
+// (gemm_mfma16x16.hip) with this kernel's 64-deep K-steps, fragments and
+// epilogue.  A 64-deep K-step of one-byte A is 64 bytes of each row, so a
+// 1 KB load of it touches 16 cache lines for half their bytes; two K-steps
+// at once make each row 128 bytes and each A load 8 whole lines (a copy of
+// the A-direct kernel reading A in this pattern ran E4M3 4096^3 in 48.3
+// against 50.2-50.3 us on MI355X, same box, alternating).
+//  * LDS: two A slots of [BM][128 B] (the 128-byte-row layout above, pieces
+//    XOR-ed by (row/2)%8), K-steps 2p, 2p+1 in slot p%2; four B stages of
+//    [64][BN], K-step s in stage s%4.
+//  * Loads and counted waits as in the 16-bit A-pair kernel: an odd K-step
+//    issues B of K-step it+3 before its barrier and the first half of the A
+//    pair (it+3, it+4) after it; an even K-step the second half of the pair
+//    (it+2, it+3) before and B of it+3 after; before barrier it the loads
+//    for K-step it+1 have landed, leaving 2*B_LOADS loads in flight (odd it)
+//    or B_LOADS + A_LOADS per half pair (even it).
+template <int FMT, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_pair_kernel(const unsigned char* A, const unsigned char* B,
+                                                               __bf16* C, int M, int N, int K, int group_m,
+                                                               int xcd_remap, Batch bt, unsigned long long* clk)
+{
+    clock_sample(clk, 0);
+    constexpr int NW = 4, BK = 64;
+    constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block (2 x 2 wavefronts)
+    constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 tiles per wavefront
+    constexpr int NT = FM * FN;                  // MFMAs per wavefront per K-step
+    constexpr int BAR = NT / 2;                  // MFMAs of a K-step before its barrier
+    constexpr int ROW_P = 2 * BK;                // bytes of an A row of a K-step pair
+    constexpr int PAIR_BYTES = BM * ROW_P;
+    constexpr int ROW_B = BN;
+    constexpr int B_BYTES = BK * ROW_B;
+    constexpr int A_LOADS2 = PAIR_BYTES / 1024 / NW;   // A loads per wavefront per pair
+    constexpr int AH = A_LOADS2 / 2;                    // ... per half pair
+    constexpr int B_LOADS = B_BYTES / 1024 / NW;        // B loads per wavefront per K-step
+    constexpr int NR = FM + FN;                         // operand fragments per K-step
+    static_assert((BM == 256 || BM == 192) && BN == 256, "tile");
+    static_assert(AH >= 1 && A_LOADS2 % 2 == 0 && B_LOADS >= 1, "tile too small");
+    static_assert(2 * PAIR_BYTES + 4 * B_BYTES <= 160 * 1024, "LDS");
+    // Every slot and stage is an LDS object of its own.
+    __shared__ __attribute__((aligned(1024))) unsigned char pa0[PAIR_BYTES], pa1[PAIR_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char pb0[B_BYTES], pb1[B_BYTES], pb2[B_BYTES], pb3[B_BYTES];
+    auto a_slot = [&](int p) __attribute__((always_inline)) { return (lds_byte*)(p == 0 ? pa0 : pa1); };
+    auto b_stage = [&](int st) __attribute__((always_inline)) {
+        return (lds_byte*)(st == 0 ? pb0 : st == 1 ? pb1 : st == 2 ? pb2 : pb3);
+    };
+
+    const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, xcd_remap != 0, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K);
+
+    // A load j of a pair: 8 rows of 128 bytes; lane -> row
+    // 8*(wave*A_LOADS2 + j) + lane/8, physical piece lane%8 holding logical
+    // piece (lane%8) ^ swz_a<128>(row) (kOOB for rows >= M and, per pair,
+    // pieces at or past K).
+    unsigned a_voff[A_LOADS2];
+    int a_kp[A_LOADS2];
+#pragma unroll
+    for (int j = 0; j < A_LOADS2; ++j) {
+        const int row = 8 * (wave * A_LOADS2 + j) + lane / 8;
+        const int piece = (lane % 8) ^ swz_a<2 * BK>(row);
+        a_voff[j] = (m0 + row) < M ? (unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 16u : kOOB;
+        a_kp[j] = piece * 16;
+    }
+    // B load j of a K-step: as in the kernel above.
+    unsigned b_voff[B_LOADS];
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+        const int byte = 1024 * (wave * B_LOADS + j) + lane * 16;
+        const int k = byte / ROW_B;
+        const int piece = ((byte % ROW_B) / 16) ^ swz_b<BN>(k);
+        const int col = n0 + piece * 16;
+        b_voff[j] = col < N ? (unsigned)k * (unsigned)N + (unsigned)col : kOOB;
+    }
+    auto load_a = [&](int p, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (void __attribute__((address_space(3)))*)(a_slot(p) + (wave * A_LOADS2 + j) * 1024), 16, off,
+            k0 < K ? k0 : 0, 0, 0);
+    };
+    auto load_b = [&](int st, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const int krem = K - k0;
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
+        const __amdgpu_buffer_rsrc_t rbk = make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N);
+        const unsigned off = b_voff[j];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rbk, (void __attribute__((address_space(3)))*)(b_stage(st) + (wave * B_LOADS + j) * 1024), 16, off, 0,
+            0, 0);
+    };
+
+    // Operand reads: A fragment of K-step h of a pair, tile bi: row wm*WM +
+    // 32*bi + lane%32, logical pieces 4*h + 2*(lane/32) and the next; B as
+    // in the kernel above.
+    int a_rd[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            a_rd[h][i] = (wm * WM + (lane & 31)) * ROW_P + (((4 * h + 2 * (lane >> 5) + i) ^ swz_a<2 * BK>(lane & 31)) * 16);
+    int b_rd[FN];
+#pragma unroll
+    for (int bj = 0; bj < FN; ++bj) {
+        const int G = lane >> 4, r = (lane & 15) >> 1, q = lane & 1;
+        const int piece = (wn * WN + 32 * bj + 16 * (G & 1)) / 16;
+        b_rd[bj] = (32 * (G >> 1) + r) * ROW_B + ((piece ^ swz_b<BN>(r)) * 16) + 8 * q;
+    }
+    f32x16 acc[FM][FN];
+    u32x8 fa[2][FM], fb[2][FN];
+    auto read_frag = [&](int set, int slot, int h, int stb, int o) __attribute__((always_inline)) {
+        if (o < FN) {
+            const lds_byte* p = b_stage(stb) + b_rd[o];
+            i32x2 hh[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hh[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (i32x2 __attribute__((address_space(3)))*)(p + 8 * i * ROW_B));
+            const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_shufflevector(hh[0], hh[1], 0, 1, 2, 3));
+            const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_shufflevector(hh[2], hh[3], 0, 1, 2, 3));
+            fb[set][o] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+            const lds_byte* base = a_slot(slot) + (o - FN) * 32 * ROW_P;
+            const u32x4 lo = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[h][0]);
+            const u32x4 hi = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[h][1]);
+            fa[set][o - FN] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
+    // ---- prologue: what K-steps -3 .. -1 would have issued (the A pair of
+    // K-steps 0, 1; B of K-steps 0, 1, 2; the first half of the A pair of
+    // K-steps 2, 3), then K-step 0's operands.
+#pragma unroll
+    for (int j = 0; j < A_LOADS2; ++j) load_a(0, 0, j);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+        for (int j = 0; j < B_LOADS; ++j) load_b(s, s * BK, j);
+        asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int j = 0; j < AH; ++j) load_a(1, 2 * BK, j);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * B_LOADS + AH));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int o = 0; o < NR; ++o) read_frag(0, 0, 0, 0, o);
+
+    auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
+    // K-step it (q = it % 4): MFMAs 0 .. BAR-1 with this half's loads, the
+    // counted wait and the barrier, then MFMAs BAR .. NT-1 with the second
+    // half's loads and the operand reads of K-step it+1.
+    auto kstep = [&](auto q_c, int it, const bool first) __attribute__((always_inline)) {
+        constexpr int q = decltype(q_c)::value;
+        constexpr int set = q & 1;
+        constexpr int n1 = (q & 1) ? B_LOADS : AH;
+        constexpr int n2 = (q & 1) ? AH : B_LOADS;
+        constexpr unsigned kWaitBar = waitcnt_vm((q & 1) ? 2 * B_LOADS : B_LOADS + 2 * AH);
+        auto load1 = [&](int o) __attribute__((always_inline)) {
+            if (q & 1)
+                load_b((q + 3) % 4, (it + 3) * BK, o);
+            else
+                load_a((q / 2 + 1) % 2, (it + 2) * BK, AH + o);
+        };
+        auto load2 = [&](int o) __attribute__((always_inline)) {
+            if (q & 1)
+                load_a(((q + 3) / 2) % 2, (it + 3) * BK, o);
+            else
+                load_b((q + 3) % 4, (it + 3) * BK, o);
+        };
+        auto mfma = [&](int x) __attribute__((always_inline)) {
+            if (first)
+                MfmaFp8<FMT>::first(acc[x / FN][x % FN], fb[set][x % FN], fa[set][x / FN]);
+            else
+                MfmaFp8<FMT>::acc(acc[x / FN][x % FN], fb[set][x % FN], fa[set][x / FN]);
+        };
+#pragma unroll
+        for (int x = 0; x < BAR; ++x) {
+            mfma(x);
+#pragma unroll
+            for (int o = op_lo(x, n1, BAR); o < op_lo(x + 1, n1, BAR); ++o) load1(o);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(kWaitBar);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        constexpr int nops2 = n2 + NR;
+#pragma unroll
+        for (int x = BAR; x < NT; ++x) {
+            mfma(x);
+#pragma unroll
+            for (int o = op_lo(x - BAR, nops2, NT - BAR); o < op_lo(x + 1 - BAR, nops2, NT - BAR); ++o) {
+                const int nld = (o * n2) / nops2 + 1;
+                if (o == 0 || (o * n2) / nops2 != ((o - 1) * n2) / nops2)
+                    load2(nld - 1);
+                else
+                    read_frag(set ^ 1, ((q + 1) / 2) % 2, (q + 1) & 1, (q + 1) % 4, o - nld);
+            }
+        }
+    };
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    using Q3 = std::integral_constant<int, 3>;
+    const int nk = cdiv_i(cdiv_i(K, BK), 4) * 4;
+    kstep(Q0{}, 0, true);
+    kstep(Q1{}, 1, false);
+    kstep(Q2{}, 2, false);
+    kstep(Q3{}, 3, false);
+    for (int it = 4; it < nk; it += 4) {
+        kstep(Q0{}, it, false);
+        kstep(Q1{}, it + 1, false);
+        kstep(Q2{}, it + 2, false);
+        kstep(Q3{}, it + 3, false);
+    }
+
+    // ---- epilogue: as in the kernel above
+    static_assert(FN == 4, "the wait below lists the last row's tiles");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    constexpr int BLOCK = WM * WN * 2;
+    constexpr int CWB = B_BYTES < BLOCK ? B_BYTES : BLOCK;
+    constexpr int CW = WM % (CWB / (WN * 2)) == 0 ? CWB : 32 * WN * 2;
+    store_c_block_32x32<__bf16, WM, WN, CW>(acc, b_stage(wave), lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
+    clock_sample(clk, 1);
+}
+
 template <int FMT>
 hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
 {
@@ -485,6 +725,18 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
+    if (cfg.sched == 2) {   // A staged two K-steps at a time: 256 x 256 or 192 x 256, one pass only
+        if (a.splits > 1 || cfg.bn != 256 || cfg.bk != 64) return hipErrorInvalidValue;
+        if (cfg.bm == 256)
+            hipLaunchKernelGGL((gemm_fp8_pair_kernel<FMT, 256, 256>), grid, block, 0, a.stream, A, B, C, a.M, a.N,
+                               a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else if (cfg.bm == 192)
+            hipLaunchKernelGGL((gemm_fp8_pair_kernel<FMT, 192, 256>), grid, block, 0, a.stream, A, B, C, a.M, a.N,
+                               a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (cfg.sched == 1) {   // A direct to LDS as well; split K at 128 x 128 and 64 x 128 only
         if (a.splits > 1) {
             if (cfg.bm == 128 && cfg.bn == 128 && cfg.bk == 64)

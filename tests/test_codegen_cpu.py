@@ -433,47 +433,59 @@ def test_few_row_kernel_structure(tmp_path):
         assert 3 * per_step in waits, (name, sorted(waits))
 
 
-# ---- the 16x16x32 kernel with A staged two K-steps at a time
+# ---- the kernels with A staged two K-steps at a time (16-bit: 16x16x32
+# MFMAs, 32-deep K-steps; 8-bit: 32x32x64 MFMAs, 64-deep K-steps)
+
+PAIR_FAMILIES = {
+    # source, kernel-name pattern (-> bm, bn), MFMA mnemonic, MFMA tile edge,
+    # bytes of an A row per K-step (= bytes of a B row per K-step / (bn / 64))
+    "mfma16x16": ("gemm_mfma16x16.hip", r"gemm_mfma16x16_pair_kernel\S*?Li(\d+)ELi(\d+)E", "v_mfma_f32_16x16x32", 16, 2),
+    "fp8": ("gemm_fp8.hip", r"gemm_fp8_pair_kernelILi\d+ELi(\d+)ELi(\d+)E", "v_mfma_f32_32x32x64_f8f6f4", 32, 1),
+}
+
 
 @pytest.fixture(scope="module")
 def pair_kernels(tmp_path_factory):
     if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
         pytest.skip("hipcc not available")
     from dense_gemm_run_amd import build as lib_build
-    out = tmp_path_factory.mktemp("asm_pair") / "m16.s"
     flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
-    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_mfma16x16.hip"),
-                        "-o", str(out)], capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr
-    lines = out.read_text().split("\n")
-    found = {}
-    for i, l in enumerate(lines):
-        m = re.match(r"^(_Z\S*gemm_mfma16x16_pair_kernel\S*?Li(\d+)ELi(\d+)E\S*):", l)
-        if m:
-            end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
-            found[m.group(1)] = (int(m.group(2)), int(m.group(3)), lines[i:end])
-    scratch = {}
-    for i, l in enumerate(lines):
-        m = re.match(r"^\s*\.amdhsa_kernel (\S+)", l)
-        if m and m.group(1) in found:
-            for l2 in lines[i:i + 80]:
-                m2 = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", l2)
-                if m2:
-                    scratch[m.group(1)] = int(m2.group(1))
-                    break
-    # {f16, bf16} x {256 x 256, 192 x 256}
-    assert len(found) == 4, sorted(found)
+    tmp = tmp_path_factory.mktemp("asm_pair")
+    found, scratch = {}, {}
+    for fam, (src, pat, mnem, edge, ebytes) in PAIR_FAMILIES.items():
+        out = tmp / (fam + ".s")
+        r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        lines = out.read_text().split("\n")
+        here = {}
+        for i, l in enumerate(lines):
+            m = re.match(r"^(_Z\S*" + pat + r"\S*):", l)
+            if m:
+                end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+                here[m.group(1)] = (int(m.group(2)), int(m.group(3)), lines[i:end], mnem, edge, ebytes)
+        for i, l in enumerate(lines):
+            m = re.match(r"^\s*\.amdhsa_kernel (\S+)", l)
+            if m and m.group(1) in here:
+                for l2 in lines[i:i + 80]:
+                    m2 = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", l2)
+                    if m2:
+                        scratch[m.group(1)] = int(m2.group(1))
+                        break
+        # 16-bit: {f16, bf16} x {256 x 256, 192 x 256}; 8-bit: {E4M3, E5M2} x the same
+        assert len(here) == 4, (fam, sorted(here))
+        found.update(here)
     return found, scratch
 
 
 def test_pair_kernel_loads_and_counted_waits(pair_kernels):
-    """Per wavefront: AH = bm/64 A loads per half K-step pair and 4 B loads
-    per K-step; odd K-steps issue B before their barrier and half an A pair
-    after it, even K-steps the other half of the pair before and B after;
-    the wait before barrier it leaves 2*4 loads in flight (odd it) or
-    4 + 2*AH (even it), and the prologue 2*4 + AH."""
+    """Per wavefront: AH = bm/64 A loads per half K-step pair (a pair is bm
+    rows of 128 bytes) and 4 B loads per K-step; odd K-steps issue B before
+    their barrier and half an A pair after it, even K-steps the other half
+    of the pair before and B after; the wait before barrier it leaves 2*4
+    loads in flight (odd it) or 4 + 2*AH (even it), and the prologue 2*4 + AH."""
     found, _ = pair_kernels
-    for name, (bm, bn, body) in found.items():
+    for name, (bm, bn, body, _, _, _) in found.items():
         ah, bl = bm // 64, bn // 64
         ev = events(body)
         bars = [i for i, e in enumerate(ev) if e == "B"]
@@ -496,11 +508,11 @@ def test_pair_kernel_loads_and_counted_waits(pair_kernels):
 
 def test_pair_kernel_accumulators_stay_in_place_without_scratch(pair_kernels):
     found, scratch = pair_kernels
-    for name, (bm, bn, body) in found.items():
+    for name, (bm, bn, body, mnem, edge, _) in found.items():
         assert scratch[name] == 0, (name, scratch[name])
         text = [x.strip() for x in body]
-        mfma = [x for x in text if x.startswith("v_mfma_f32_16x16x32")]
-        per_step = (bm // 2 // 16) * (bn // 2 // 16)
+        mfma = [x for x in text if x.startswith(mnem)]
+        per_step = (bm // 2 // edge) * (bn // 2 // edge)
         assert len(mfma) == 8 * per_step, (name, len(mfma))
         ops_of = lambda x: [o.strip().split()[0] for o in x.split(None, 1)[1].split(",")]
         assert sum(1 for x in mfma if ops_of(x)[3] == "0") == per_step, name
