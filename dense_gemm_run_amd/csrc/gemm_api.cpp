@@ -139,6 +139,8 @@ const Entry kTable[] = {
     // the 8-bit kernel with A staged two K-steps at a time
     {{63, 256, 256, 64, 4, 256, 0x18, 1, 1, "fp8_256x256x64_apair", 2}, kFp8},
     {{64, 192, 256, 64, 4, 256, 0x18, 1, 1, "fp8_192x256x64_apair", 2}, kFp8},
+    {{65, 256, 256, 128, 4, 256, 0x18, 1, 1, "fp8_256x256x128_k128", 3}, kFp8},
+    {{66, 192, 256, 128, 4, 256, 0x18, 1, 1, "fp8_192x256x128_k128", 3}, kFp8},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -329,16 +331,18 @@ int select(const Problem& p)
         // a partial last wave of 256 x 256 tiles: 192 x 256 where its waves
         // cost less, by the 16-bit rule below
         const int64_t t192 = ((p.M + 191) / 192) * ((p.N + 255) / 256) * p.batch;
-        // The 256 x 256 and 192 x 256 tiles with A direct to LDS take A two
-        // K-steps at a time (configs 63, 64; whole cache lines per A load).
-        // Median of five 200-launch blocks against the one-K-step ring (32,
-        // 39), same box, alternating: E4M3 4096^3 50.8-51.0 against
-        // 52.7-53.2 us, E5M2 4096^3 49.9 against 51.0-51.2, E4M3 8192^3
-        // 370.6-372.6 against 378.1-379.7, 8192 x 12288 x 4096 296.4-297.2
-        // against 302.8-303.3; on 192 x 256 tiles 3072^3 26.9-27.2 against
-        // 27.5-27.7, 6144^3 168.1-168.5 against 170.6-170.7.
-        if (t256 >= 128 && ((t192 + 255) / 256) * 80 < ((t256 + 255) / 256) * 95) return 64;
-        return t256 >= 256 ? 63 : t256 >= 128 ? 13 : t64 <= 256 ? 38 : 33;
+        // The 256 x 256 and 192 x 256 tiles run 128-deep K-steps on the
+        // 16 x 16 x 128 MFMA (configs 65, 66).  Median of five 200-launch
+        // blocks against the A-pair kernel with 64-deep K-steps on the
+        // 32 x 32 x 64 MFMA (63, 64), same box, alternating: E4M3 4096^3
+        // 49.6 against 50.7-50.8 us, E5M2 4096^3 48.4-48.6 against 49.5,
+        // E4M3 8192^3 356.1-357.9 against 371.5-371.7, 8192 x 12288 x 4096
+        // 287.5-288.3 against 297.1-297.2; on 192 x 256 tiles 3072^3
+        // 25.7-25.9 against 26.8-26.9, 6144^3 159.3-159.9 against
+        // 167.0-168.0.  The A-pair kernel itself beat the one-K-step ring (32,
+        // 39) by 1.6-2.4 % on the same shapes.
+        if (t256 >= 128 && ((t192 + 255) / 256) * 80 < ((t256 + 255) / 256) * 95) return 66;
+        return t256 >= 256 ? 65 : t256 >= 128 ? 13 : t64 <= 256 ? 38 : 33;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) {
         // Timed on bf16 shapes with M 2K-28K, K 2K-14K, N 1-4.  A K-slice

@@ -35,6 +35,8 @@ constexpr unsigned waitcnt_vm(unsigned n)
 }
 // ... and the one that waits for all of this wavefront's LDS operations.
 constexpr unsigned kWaitLgkm0 = 15u | (7u << 4) | (0u << 8) | (3u << 14);
+// ... and the one that waits until at most n (<= 15) of them are outstanding.
+constexpr unsigned waitcnt_lgkm(unsigned n) { return 15u | (7u << 4) | ((n > 15u ? 15u : n) << 8) | (3u << 14); }
 
 // Measurement aid: when `clk` is set, thread 0 of workgroup 0 records the
 // counter that ticks with the shader clock and the constant 100 MHz counter,
@@ -64,6 +66,59 @@ template <> __device__ __forceinline__ unsigned pack2<__bf16>(float a, float b)
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     b2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(unsigned, v);
+}
+
+// Epilogue: one wavefront's WM x WN block of fp32 accumulators (tile (bi,
+// bj): lane l holds row 16*bi + l%16, columns 16*bj + 4*(l/16) .. +3) is
+// rounded to the output type and written to C at (row0, col0) through the
+// wavefront's own LDS region `cw` of CW_BYTES: RP rows at a time are staged
+// there and read back as whole row segments for 16-byte stores, skipping
+// rows >= M and columns >= N.
+template <typename T, int WM, int WN, int CW_BYTES>
+__device__ __forceinline__ void store_c_block(const f32x4 (&acc)[WM / 16][WN / 16], lds_byte* cw,
+                                              int lane, int row0, int col0, int M, int N, T* C)
+{
+    constexpr int FN = WN / 16;
+    constexpr int PR = WN / 8;           // 16-byte pieces per C row
+    constexpr int W = 128 / WN;          // C rows per 256-byte bank window
+    constexpr int RP = CW_BYTES / (WN * 2);   // rows per pass
+    static_assert(W >= 1 && PR <= 16, "wavefront block too wide");
+    static_assert(RP % 16 == 0 && WM % RP == 0, "passes must hold whole tile rows");
+    // piece p of row r sits at p ^ ((r / W) % PR): the 16 rows one
+    // half-wavefront writes (8 bytes per lane, two lanes per piece) and the
+    // rows one 16-lane group reads back each cover 16 different bank groups.
+    const int q = lane % PR;
+    const int col = col0 + q * 8;
+#pragma unroll
+    for (int pass = 0; pass < WM / RP; ++pass) {
+        if (pass) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // previous pass read back
+#pragma unroll
+        for (int bi = pass * RP / 16; bi < (pass + 1) * RP / 16; ++bi) {
+            const int r = 16 * bi + (lane & 15) - pass * RP;
+            const int sw = (r / W) & (PR - 1);
+#pragma unroll
+            for (int bj = 0; bj < FN; ++bj) {
+                const int p = (2 * bj + (lane >> 5)) ^ sw;
+                const int h = (lane >> 4) & 1;
+                u32x2 v;
+                v[0] = pack2<T>(acc[bi][bj][0], acc[bi][bj][1]);
+                v[1] = pack2<T>(acc[bi][bj][2], acc[bi][bj][3]);
+                *(u32x2 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16 + h * 8) = v;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wavefront's LDS writes done
+#pragma unroll 4
+        for (int it = 0; it < RP * PR / 64; ++it) {
+            const int r = it * (64 / PR) + lane / PR;
+            const int p = q ^ ((r / W) & (PR - 1));
+            const u32x4 v = *(const u32x4 __attribute__((address_space(3)))*)(cw + r * (WN * 2) + p * 16);
+            const int row = row0 + pass * RP + r;
+            // non-temporal: C is not read again, and streaming it past the
+            // caches leaves them to the A and B tiles other workgroups still
+            // need (bf16 8192^3: 760 against 787 us)
+            if (row < M && col < N) __builtin_nontemporal_store(v, (u32x4*)(C + (size_t)row * N + col));
+        }
+    }
 }
 
 // Epilogue of the 32x32 MFMA kernels: one wavefront's WM x WN block of fp32

@@ -94,6 +94,32 @@ template <> struct MfmaFp8<1> {
     }
 };
 
+// c += b-fragment x a-fragment, 16 x 16 x 128 (each lane: 32 consecutive K
+// of one row of A and of one column of B; C as in the 16-bit 16x16 kernels:
+// lane l holds row l%16, columns 4*(l/16) .. +3).  Wait states as for the
+// 32 x 32 form above.
+template <int FMT> struct MfmaFp8x16;
+template <> struct MfmaFp8x16<0> {
+    static __device__ __forceinline__ void acc(f32x4& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+    }
+    static __device__ __forceinline__ void first(f32x4& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0" : "=a"(c) : "v"(b), "v"(a));
+    }
+};
+template <> struct MfmaFp8x16<1> {
+    static __device__ __forceinline__ void acc(f32x4& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(c) : "v"(b), "v"(a));
+    }
+    static __device__ __forceinline__ void first(f32x4& c, const u32x8& b, const u32x8& a)
+    {
+        asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, 0 cbsz:1 blgp:1" : "=a"(c) : "v"(b), "v"(a));
+    }
+};
+
 template <int BK> __device__ __forceinline__ int swz_a(int row)
 {
     return BK == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
@@ -716,6 +742,257 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_pair_kernel(const unsigned ch
     clock_sample(clk, 1);
 }
 
+// 128-deep K-steps on 16 x 16 x 128 MFMAs (256 x 256 and 192 x 256 tiles,
+// one product per workgroup, no split).  Each wavefront owns WM x 128 of the
+// tile as (WM/16) x 8 tiles of 16 x 16; one K-step is (WM/16) x 8 MFMAs,
+// issued row of tiles by row of tiles.
+//  * LDS: two A slots of [BM][128 B] (128-byte rows, pieces XOR-ed by
+//    (row/2)%8) and two B stages of [128][BN] (256-byte rows, piece p of row
+//    k at p ^ (2*(k%8) + (k/32)%2)); K-step t in slot and stage t%2.
+//  * Registers: the B fragments of a K-step stay in one of two register
+//    sets for the whole K-step; A fragments are read two rows of tiles
+//    ahead of their MFMAs; the transpose reads of the next K-step's B
+//    fragments are spread one or two per MFMA.
+//  * K-step t: rows 0 .. MB-1 issue the A loads of K-step t+1 (into the
+//    other slot, free since the end of K-step t-1); barrier M(t) once the B
+//    loads of K-step t+1 have landed; rows MB .. FM-1 issue the B loads of
+//    K-step t+2 (into this K-step's stage, whose fragments were read before
+//    M(t)) and read the B fragments of K-step t+1; barrier E(t) after row
+//    FM-2, once the A loads of K-step t+1 have landed and this K-step's A
+//    reads are done; row FM-1 reads A fragments 0 and 1 of K-step t+1.
+template <int FMT, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_k128_kernel(const unsigned char* A, const unsigned char* B,
+                                                               __bf16* C, int M, int N, int K, int group_m,
+                                                               int xcd_remap, Batch bt, unsigned long long* clk)
+{
+    clock_sample(clk, 0);
+    constexpr int NW = 4, BK = 128;
+    constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront block (2 x 2 wavefronts)
+    constexpr int FM = WM / 16, FN = WN / 16;    // 16x16 tiles per wavefront
+    constexpr int MB = FM / 2 - 1;               // rows of tiles before barrier M
+    constexpr int ROW_A = BK;
+    constexpr int A_BYTES = BM * ROW_A;
+    constexpr int ROW_B = BN;
+    constexpr int B_BYTES = BK * ROW_B;
+    constexpr int A_LOADS = A_BYTES / 1024 / NW;   // A loads per wavefront per K-step
+    constexpr int B_LOADS = B_BYTES / 1024 / NW;   // B loads per wavefront per K-step
+    constexpr int NX = MB * FN;                    // MFMAs before barrier M
+    constexpr int NY = (FM - MB) * FN;             // MFMAs after it
+    constexpr int NYE = (FM - 1 - MB) * FN;        // ... of them before barrier E
+    static_assert((BM == 256 || BM == 192) && BN == 256, "tile");
+    static_assert(2 * A_BYTES + 2 * B_BYTES <= 160 * 1024, "LDS");
+    static_assert(FM - 1 > MB + 1, "A reads of the last rows must precede barrier E");
+    __shared__ __attribute__((aligned(1024))) unsigned char sa0[A_BYTES], sa1[A_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char sb0[B_BYTES], sb1[B_BYTES];
+    auto a_slot = [&](int p) __attribute__((always_inline)) { return (lds_byte*)(p == 0 ? sa0 : sa1); };
+    auto b_stage = [&](int p) __attribute__((always_inline)) { return (lds_byte*)(p == 0 ? sb0 : sb1); };
+    auto swz_b16 = [](int k) __attribute__((always_inline)) { return 2 * (k & 7) + ((k >> 5) & 1); };
+
+    const int tiles_m = cdiv_i(M, BM), tiles_n = cdiv_i(N, BN);
+    int b, tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, bt.count, group_m, xcd_remap != 0, b, tm, tn);
+    A += b * bt.sa;
+    B += b * bt.sb;
+    C += b * bt.sc;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (unsigned)M * (unsigned)K);
+
+    // A load j: 8 rows of 128 bytes; lane -> row 8*(wave*A_LOADS + j) +
+    // lane/8, physical piece lane%8 holding logical piece (lane%8) ^
+    // swz_a<128>(row) (kOOB for rows >= M and pieces at or past K).
+    unsigned a_voff[A_LOADS];
+    int a_kp[A_LOADS];
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) {
+        const int row = 8 * (wave * A_LOADS + j) + lane / 8;
+        const int piece = (lane % 8) ^ swz_a<BK>(row);
+        a_voff[j] = (m0 + row) < M ? (unsigned)(m0 + row) * (unsigned)K + (unsigned)piece * 16u : kOOB;
+        a_kp[j] = piece * 16;
+    }
+    // B load j: 4 rows of 256 bytes; lane -> row k = byte/256 of the K-step,
+    // physical piece (byte%256)/16 holding columns n0 + 16*(piece ^
+    // swz_b16(k)) .. +15 (kOOB past N; rows past K lie outside the range of
+    // the K-step's buffer resource).
+    unsigned b_voff[B_LOADS];
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) {
+        const int byte = 1024 * (wave * B_LOADS + j) + lane * 16;
+        const int k = byte / ROW_B;
+        const int piece = ((byte % ROW_B) / 16) ^ swz_b16(k);
+        const int col = n0 + piece * 16;
+        b_voff[j] = col < N ? (unsigned)k * (unsigned)N + (unsigned)col : kOOB;
+    }
+    auto load_a = [&](int p, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const unsigned off = a_kp[j] < K - k0 ? a_voff[j] : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (void __attribute__((address_space(3)))*)(a_slot(p) + (wave * A_LOADS + j) * 1024), 16, off,
+            k0 < K ? k0 : 0, 0, 0);
+    };
+    auto load_b = [&](int p, int k0_in, int j) __attribute__((always_inline)) {
+        const int k0 = __builtin_amdgcn_readfirstlane(k0_in);
+        const int krem = K - k0;
+        const int rows = __builtin_amdgcn_readfirstlane(krem < 0 ? 0 : (krem > BK ? BK : krem));
+        const __amdgpu_buffer_rsrc_t rbk = make_rsrc(B + (size_t)(k0 < K ? k0 : 0) * N, (unsigned)rows * (unsigned)N);
+        const unsigned off = b_voff[j];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rbk, (void __attribute__((address_space(3)))*)(b_stage(p) + (wave * B_LOADS + j) * 1024), 16, off, 0, 0,
+            0);
+    };
+
+    // A fragment of tile row i: row wm*WM + 16*i + lane%16, logical pieces
+    // 2*(lane/16) and the next (K 32*(lane/16) .. +31); the swizzle depends
+    // on lane%16 only, so row i is 16*i rows further.
+    int a_rd[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        a_rd[h] = (wm * WM + (lane & 15)) * ROW_A + (((2 * (lane >> 4) + h) ^ swz_a<BK>(lane & 15)) * 16);
+    // B fragment of tile column j: four transpose reads of 8 rows x 16
+    // columns; lane -> column wn*WN + 16*j + lane%16, K 32*(lane/16) .. +31
+    // (read i covers K 32*(lane/16) + 8*i .. +7, one row further by 8).
+    int b_rd[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int k = 32 * (lane >> 4) + ((lane & 15) >> 1);
+        const int piece = (wn * WN + 16 * j) / 16;
+        b_rd[j] = k * ROW_B + ((piece ^ swz_b16(k)) * 16) + 8 * (lane & 1);
+    }
+    f32x4 acc[FM][FN];
+    u32x8 fa[FM], fb[2][FN];
+    auto read_a = [&](int slot, int i) __attribute__((always_inline)) {
+        const lds_byte* base = a_slot(slot) + i * 16 * ROW_A;
+        const u32x4 lo = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[0]);
+        const u32x4 hi = *(const u32x4 __attribute__((address_space(3)))*)(base + a_rd[1]);
+        fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // part i (K 32*(lane/16) + 8*i .. +7) of the B fragment of tile column j
+    auto read_b = [&](int set, int stage, int j, int i) __attribute__((always_inline)) {
+        const lds_byte* p = b_stage(stage) + b_rd[j] + 8 * i * ROW_B;
+        const u32x2 h = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 __attribute__((address_space(3)))*)p));
+        fb[set][j][2 * i] = h.x;
+        fb[set][j][2 * i + 1] = h.y;
+    };
+
+    // ---- prologue: the A and B loads of K-step 0, the B loads of K-step 1;
+    // once K-step 0's have landed, its B fragments and A fragments 0 and 1.
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j) load_a(0, 0, j);
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) load_b(0, 0, j);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j) load_b(1, BK, j);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(B_LOADS));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int r = 0; r < 4 * FN; ++r) read_b(0, 0, r / 4, r % 4);
+    read_a(0, 0);
+    read_a(0, 1);
+
+    auto op_lo = [](int pos, int n, int span) __attribute__((always_inline)) { return (pos * n + span - 1) / span; };
+    // K-step t, s = t % 2 (slot, stage and B register set of K-step t).
+    auto kstep = [&](auto s_c, int t, auto first_c) __attribute__((always_inline)) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr bool first = decltype(first_c)::value;
+        // B loads of K-step t+2 issued before barrier E
+        constexpr int NBE = op_lo(NYE, B_LOADS, NY);
+        // The 4*FN transpose reads of K-step t+1's B fragments, spread over
+        // the NY MFMAs after barrier M (read r: fragment r/4, part r%4).
+        constexpr int NBR = 4 * FN;
+        // LDS reads each barrier must see completed: at M, every read of
+        // this K-step's B stage (issued before the MB A-fragment reads of
+        // rows 0 .. MB-1, two operations each); at E, every read of this
+        // K-step's A slot (the last, fragment FM-1, at MFMA YA after M; after
+        // it only B reads, those of MFMAs YA+1 .. NYE-1).  LDS operations
+        // complete in order.
+        constexpr int YA = (FM - 3 - MB) * FN + FN / 2;
+        constexpr int NRE = op_lo(NYE, NBR, NY) - op_lo(YA + 1, NBR, NY);
+        constexpr unsigned kLgkmM = waitcnt_lgkm(2 * MB);
+        constexpr unsigned kLgkmE = waitcnt_lgkm(NRE);
+        auto mfma = [&](int i, int j) __attribute__((always_inline)) {
+            if constexpr (first)
+                MfmaFp8x16<FMT>::first(acc[i][j], fb[s][j], fa[i]);
+            else
+                MfmaFp8x16<FMT>::acc(acc[i][j], fb[s][j], fa[i]);
+        };
+        // rows 0 .. MB-1: the A loads of K-step t+1; A fragments 2 .. MB+1
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int x = i * FN + j;
+                mfma(i, j);
+#pragma unroll
+                for (int o = op_lo(x, A_LOADS, NX); o < op_lo(x + 1, A_LOADS, NX); ++o)
+                    load_a(s ^ 1, (t + 1) * BK, o);
+                if (j == FN / 2) read_a(s, i + 2);
+            }
+        // barrier M: the B loads of K-step t+1 have landed (only the A loads
+        // above are still in flight)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(A_LOADS));
+        __builtin_amdgcn_s_waitcnt(kLgkmM);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        // rows MB .. FM-1: the B loads of K-step t+2, the B fragments of
+        // K-step t+1, A fragments MB+2 .. FM-1; barrier E before row FM-1,
+        // whose reads are A fragments 0, 1 of K-step t+1
+#pragma unroll
+        for (int i = MB; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int y = (i - MB) * FN + j;
+                if (y == NYE) {
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NBE));
+                    __builtin_amdgcn_s_waitcnt(kLgkmE);
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                }
+                mfma(i, j);
+#pragma unroll
+                for (int o = op_lo(y, B_LOADS, NY); o < op_lo(y + 1, B_LOADS, NY); ++o)
+                    load_b(s, (t + 2) * BK, o);
+                // the B fragments of K-step t+1, a transpose read or two
+                // per MFMA
+#pragma unroll
+                for (int r = op_lo(y, NBR, NY); r < op_lo(y + 1, NBR, NY); ++r) read_b(s ^ 1, s ^ 1, r / 4, r % 4);
+                if (j == FN / 2 && i + 2 < FM) read_a(s, i + 2);
+                if (i == FM - 1 && j == 0) read_a(s ^ 1, 0);
+                if (i == FM - 1 && j == FN / 2) read_a(s ^ 1, 1);
+            }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    const int nk = cdiv_i(cdiv_i(K, BK), 2) * 2;
+    kstep(S0{}, 0, std::true_type{});
+    kstep(S1{}, 1, std::false_type{});
+    for (int t = 2; t < nk; t += 2) {
+        kstep(S0{}, t, std::false_type{});
+        kstep(S1{}, t + 1, std::false_type{});
+    }
+
+    // ---- epilogue: the last row of tiles was written by the most recent
+    // MFMAs; each wavefront stages its block through a slot or stage of its
+    // own
+    static_assert(FN == 8, "the wait below lists the last row's tiles");
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]),
+                   "+a"(acc[FM - 1][4]), "+a"(acc[FM - 1][5]), "+a"(acc[FM - 1][6]), "+a"(acc[FM - 1][7]));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    constexpr int CW = A_BYTES < WM * WN * 2 ? A_BYTES : WM * WN * 2;
+    lds_byte* cw = wave < 2 ? a_slot(wave) : b_stage(wave - 2);
+    store_c_block<__bf16, WM, WN, CW>(acc, cw, lane, m0 + wm * WM, n0 + wn * WN, M, N, C);
+    clock_sample(clk, 1);
+}
+
 template <int FMT>
 hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
 {
@@ -725,6 +1002,18 @@ hipError_t launch_fmt(const Config& cfg, const LaunchArgs& a)
     const unsigned char* B = static_cast<const unsigned char*>(a.B);
     __bf16* C = static_cast<__bf16*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
+    if (cfg.sched == 3) {   // 128-deep K-steps on 16 x 16 x 128 MFMAs: 256 x 256 or 192 x 256, one pass only
+        if (a.splits > 1 || cfg.bn != 256 || cfg.bk != 128) return hipErrorInvalidValue;
+        if (cfg.bm == 256)
+            hipLaunchKernelGGL((gemm_fp8_k128_kernel<FMT, 256, 256>), grid, block, 0, a.stream, A, B, C, a.M, a.N,
+                               a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else if (cfg.bm == 192)
+            hipLaunchKernelGGL((gemm_fp8_k128_kernel<FMT, 192, 256>), grid, block, 0, a.stream, A, B, C, a.M, a.N,
+                               a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (cfg.sched == 2) {   // A staged two K-steps at a time: 256 x 256 or 192 x 256, one pass only
         if (a.splits > 1 || cfg.bn != 256 || cfg.bk != 64) return hipErrorInvalidValue;
         if (cfg.bm == 256)

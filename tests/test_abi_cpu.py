@@ -426,9 +426,9 @@ def test_8bit_tile_size_follows_the_tile_count():
         assert name(A, Bb, Cb, M, N, K, 4).startswith("fp8_256x256"), (M, N, K)
     # a partial last wave of 256 x 256 tiles that 192 x 256 tiles fill: 3072^2, 6144^2
     for n in (3072, 6144):
-        assert name(A, Bb, Cb, n, n, n, 3) == "fp8_192x256x64_apair", n
+        assert name(A, Bb, Cb, n, n, n, 3) == "fp8_192x256x128_k128", n
     # A direct to LDS except for a partial single wave of 256 x 256 tiles
-    assert name(A, Bb, Cb, 4096, 4096, 4096, 3) == "fp8_256x256x64_apair"
+    assert name(A, Bb, Cb, 4096, 4096, 4096, 3) == "fp8_256x256x128_k128"
     assert name(A, Bb, Cb, 2048, 2048, 2048, 3) == "fp8_128x128x64_adma"
     # the batch counts: 16 products of 1024^2 are 256 tiles of 256 x 256
     cid = dg.gemm_select_config_batched(A, Bb, Cb, 16, 1024, 1024, 1024, 1024 * 1024, 1024 * 1024,
@@ -550,7 +550,7 @@ def test_short_k_selects_128x128_tiles_with_a_through_registers():
     assert (info["bm"], info["bn"], info["bk"], info["dtype_mask"], info["threads"]) == (128, 128, 128, 6, 256)
     # from K = 264 on, the tile-count rules again
     assert name(A, Bb, Cb, 8192, 8192, 264, 2) == "mfma16x16_256x256x32_apair"
-    assert name(A, Bb, Cb, 8192, 8192, 512, 3) == "fp8_256x256x64_apair"
+    assert name(A, Bb, Cb, 8192, 8192, 512, 3) == "fp8_256x256x128_k128"
     # few rows keep the few-row kernels, few columns the vector kernel
     assert name(A, Bb, Cb, 16, 4096, 128, 2).startswith("fewrow")
     assert name(A, Bb, Cb, 16, 4096, 128, 3).startswith("fewrow8")

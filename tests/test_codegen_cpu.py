@@ -523,3 +523,106 @@ def test_pair_kernel_accumulators_stay_in_place_without_scratch(pair_kernels):
         last = max(i for i, x in enumerate(text) if x.startswith("v_mfma"))
         assert not [x for x in text[first:last]
                     if x.startswith(("v_accvgpr_write", "v_accvgpr_mov", "v_accvgpr_read"))], name
+
+
+# ---- the 8-bit kernel with 128-deep K-steps on 16x16x128 MFMAs (two A slots
+# and two B stages; barrier M after rows 0 .. MB-1 of tiles, barrier E before
+# the last row)
+
+K128_PAT = r"gemm_fp8_k128_kernelILi\d+ELi(\d+)ELi(\d+)E"
+
+
+@pytest.fixture(scope="module")
+def k128_kernels(tmp_path_factory):
+    if not os.path.exists(HIPCC) and not shutil.which("hipcc"):
+        pytest.skip("hipcc not available")
+    from dense_gemm_run_amd import build as lib_build
+    flags = [f for f in lib_build.COMMON if f not in ("-fPIC",)]
+    out = tmp_path_factory.mktemp("asm_k128") / "fp8.s"
+    r = subprocess.run([HIPCC, *flags, "--cuda-device-only", "-S", os.path.join(CSRC, "gemm_fp8.hip"), "-o", str(out)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lines = out.read_text().split("\n")
+    found, scratch = {}, {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^(_Z\S*" + K128_PAT + r"\S*):", l)
+        if m:
+            end = next(j for j in range(i, len(lines)) if lines[j].startswith(".Lfunc_end"))
+            found[m.group(1)] = (int(m.group(2)), int(m.group(3)), lines[i:end])
+    for i, l in enumerate(lines):
+        m = re.match(r"^\s*\.amdhsa_kernel (\S+)", l)
+        if m and m.group(1) in found:
+            for l2 in lines[i:i + 80]:
+                m2 = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", l2)
+                if m2:
+                    scratch[m.group(1)] = int(m2.group(1))
+                    break
+    assert len(found) == 4, sorted(found)   # {E4M3, E5M2} x {256 x 256, 192 x 256}
+    return found, scratch
+
+
+def _k128_schedule(bm, bn):
+    """Loads and waits of one K-step: per wavefront A_LOADS = bm/32 A loads
+    (bm rows of 128 bytes) before barrier M, B_LOADS = bn/32 B loads (128
+    rows of bn bytes) spread evenly over the NY MFMAs after it, NBE of them
+    before barrier E; M waits for all but the A loads and all but the 2*MB
+    A-fragment reads of rows 0 .. MB-1; E for all but NBE loads and all but
+    the NRE transpose reads issued after the last A-fragment read."""
+    fm, fn = bm // 32, bn // 32
+    mb = fm // 2 - 1
+    ny, nye = (fm - mb) * fn, (fm - 1 - mb) * fn
+    op_lo = lambda pos, n, span: (pos * n + span - 1) // span
+    a_loads, b_loads = bm // 32, bn // 32
+    nbe = op_lo(nye, b_loads, ny)
+    ya = (fm - 3 - mb) * fn + fn // 2
+    nre = op_lo(nye, 4 * fn, ny) - op_lo(ya + 1, 4 * fn, ny)
+    return a_loads, b_loads, nbe, 2 * mb, nre
+
+
+def test_k128_kernel_loads_and_counted_waits(k128_kernels):
+    found, _ = k128_kernels
+    for name, (bm, bn, body) in found.items():
+        a_loads, b_loads, nbe, lgkm_m, lgkm_e = _k128_schedule(bm, bn)
+        ev = events(body)
+        bars = [i for i, e in enumerate(ev) if e == "B"]
+        # prologue, 2 barriers in each of 2 peeled and 2 looped K-steps, epilogue
+        assert len(bars) == 10, (name, len(bars))
+        pro = [e for e in ev[:bars[0]] if e in ("g", "L")]
+        assert pro == ["L"] * (a_loads + 2 * b_loads), (name, pro)
+        assert [e[1] for e in ev[:bars[0]] if isinstance(e, tuple)][-1] == b_loads, name
+        for k in range(4):
+            m_seg = ev[bars[2 * k] + 1:bars[2 * k + 1]]
+            e_seg = ev[bars[2 * k + 1] + 1:bars[2 * k + 2]]
+            carried = 0 if k == 0 else b_loads - nbe   # B loads after the previous barrier E
+            assert [e for e in m_seg if e in ("g", "L")] == ["L"] * (carried + a_loads), (name, k)
+            assert [e[1] for e in m_seg if isinstance(e, tuple)][-1] == a_loads, (name, k)
+            assert [e for e in e_seg if e in ("g", "L")] == ["L"] * nbe, (name, k)
+            assert [e[1] for e in e_seg if isinstance(e, tuple)][-1] == nbe, (name, k)
+        text = [x.strip() for x in body]
+        bar_lines = [i for i, x in enumerate(text) if x.startswith("s_barrier")]
+        lgkm = []
+        for i in bar_lines[1:-1]:
+            w = next(text[j] for j in range(i - 1, 0, -1) if text[j].startswith("s_waitcnt"))
+            m = re.search(r"lgkmcnt\((\d+)\)", w)
+            lgkm.append(int(m.group(1)) if m else 15)
+        assert lgkm == [lgkm_m, min(lgkm_e, 15)] * 4, (name, lgkm)
+
+
+def test_k128_kernel_accumulators_stay_in_place_without_scratch(k128_kernels):
+    found, scratch = k128_kernels
+    for name, (bm, bn, body) in found.items():
+        assert scratch[name] == 0, (name, scratch[name])
+        text = [x.strip() for x in body]
+        mfma = [x for x in text if x.startswith("v_mfma")]
+        per_step = (bm // 32) * (bn // 32)
+        assert mfma and all(x.startswith("v_mfma_f32_16x16x128_f8f6f4") for x in mfma), name
+        assert len(mfma) == 4 * per_step, (name, len(mfma))
+        ops_of = lambda x: [o.strip().split()[0] for o in x.split(None, 1)[1].split(",")]
+        assert sum(1 for x in mfma if ops_of(x)[3] == "0") == per_step, name
+        for x in mfma:
+            ops = ops_of(x)
+            assert ops[3] in (ops[0], "0"), x
+        first = next(i for i, x in enumerate(text) if x.startswith("v_mfma"))
+        last = max(i for i, x in enumerate(text) if x.startswith("v_mfma"))
+        assert not [x for x in text[first:last]
+                    if x.startswith(("v_accvgpr_write", "v_accvgpr_mov", "v_accvgpr_read"))], name

@@ -32,7 +32,7 @@ def note(msg):
 def splits_k(name):
     """Whether a tile configuration has a split form: all with A through
     registers, and the 128 x 128 and 64 x 128 ones with A direct to LDS."""
-    if name.endswith("_apair"):   # A staged in K-step pairs: one pass only
+    if name.endswith(("_apair", "_k128")):   # one pass only
         return False
     return not name.endswith("_adma") or "_128x128x" in name or "_64x128x" in name
 
