@@ -745,7 +745,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_pair_kernel(const unsigned ch
 // 128-deep K-steps on 16 x 16 x 128 MFMAs (256 x 256 and 192 x 256 tiles,
 // one product per workgroup, no split).  Each wavefront owns WM x 128 of the
 // tile as (WM/16) x 8 tiles of 16 x 16; one K-step is (WM/16) x 8 MFMAs,
-// issued row of tiles by row of tiles.
+// issued row of tiles by row of tiles.  Half the accumulator data per FLOP
+// of the 32 x 32 x 64 form lets the board hold a higher clock under its
+// power limit (E4M3 4096^3 on MI355X: 2.0-2.1 against 1.85 GHz), which
+// outweighs the lower share of cycles it keeps the MFMA pipe busy: 2-5 %
+// less time than the A-pair kernel above on 3072^3 .. 8192^3.
 //  * LDS: two A slots of [BM][128 B] (128-byte rows, pieces XOR-ed by
 //    (row/2)%8) and two B stages of [128][BN] (256-byte rows, piece p of row
 //    k at p ^ (2*(k%8) + (k/32)%2)); K-step t in slot and stage t%2.
@@ -754,7 +758,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_pair_kernel(const unsigned ch
 //    ahead of their MFMAs; the transpose reads of the next K-step's B
 //    fragments are spread one or two per MFMA.
 //  * K-step t: rows 0 .. MB-1 issue the A loads of K-step t+1 (into the
-//    other slot, free since the end of K-step t-1); barrier M(t) once the B
+//    other slot, free since barrier E(t-1)); barrier M(t) once the B
 //    loads of K-step t+1 have landed; rows MB .. FM-1 issue the B loads of
 //    K-step t+2 (into this K-step's stage, whose fragments were read before
 //    M(t)) and read the B fragments of K-step t+1; barrier E(t) after row
