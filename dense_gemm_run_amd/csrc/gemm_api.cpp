@@ -340,9 +340,13 @@ int select(const Problem& p)
         // 287.5-288.3 against 297.1-297.2; on 192 x 256 tiles 3072^3
         // 25.7-25.9 against 26.8-26.9, 6144^3 159.3-159.9 against
         // 167.0-168.0.  The A-pair kernel itself beat the one-K-step ring (32,
-        // 39) by 1.6-2.4 % on the same shapes.
+        // 39) by 1.6-2.4 % on the same shapes.  Config 65 also takes 128-255
+        // tiles (a partial single wave) where 192 x 256 tiles do not fit
+        // better, in place of the 256 x 256 tile with A through registers
+        // (13): 2048 x 6144 x 4096 40.2 against 43.9 us, 1024 x 14336 x 4096
+        // 45.5 against 49.5-50.4, 1024 x 10240 x 4096 38.3 against 40.5.
         if (t256 >= 128 && ((t192 + 255) / 256) * 80 < ((t256 + 255) / 256) * 95) return 66;
-        return t256 >= 256 ? 65 : t256 >= 128 ? 13 : t64 <= 256 ? 38 : 33;
+        return t256 >= 128 ? 65 : t64 <= 256 ? 38 : 33;
     }
     if (p.N <= 4 && accepts(kTable[10], p)) {
         // Timed on bf16 shapes with M 2K-28K, K 2K-14K, N 1-4.  A K-slice

@@ -427,8 +427,11 @@ def test_8bit_tile_size_follows_the_tile_count():
     # a partial last wave of 256 x 256 tiles that 192 x 256 tiles fill: 3072^2, 6144^2
     for n in (3072, 6144):
         assert name(A, Bb, Cb, n, n, n, 3) == "fp8_192x256x128_k128", n
-    # A direct to LDS except for a partial single wave of 256 x 256 tiles
+    # the 128-deep kernel from 128 tiles of 256 x 256 on (a partial single wave included,
+    # where 192 x 256 tiles do not fill it better)
     assert name(A, Bb, Cb, 4096, 4096, 4096, 3) == "fp8_256x256x128_k128"
+    for M, N, K in [(2048, 6144, 4096), (1024, 14336, 4096)]:
+        assert name(A, Bb, Cb, M, N, K, 3) == "fp8_256x256x128_k128", (M, N, K)
     assert name(A, Bb, Cb, 2048, 2048, 2048, 3) == "fp8_128x128x64_adma"
     # the batch counts: 16 products of 1024^2 are 256 tiles of 256 x 256
     cid = dg.gemm_select_config_batched(A, Bb, Cb, 16, 1024, 1024, 1024, 1024 * 1024, 1024 * 1024,
