@@ -141,6 +141,7 @@ const Entry kTable[] = {
     {{64, 192, 256, 64, 4, 256, 0x18, 1, 1, "fp8_192x256x64_apair", 2}, kFp8},
     {{65, 256, 256, 128, 4, 256, 0x18, 1, 1, "fp8_256x256x128_k128", 3}, kFp8},
     {{66, 192, 256, 128, 4, 256, 0x18, 1, 1, "fp8_192x256x128_k128", 3}, kFp8},
+    {{67, 128, 128, 32, 4, 256, 0x6, 1, 1, "mfma16x16_128x128x32_apair", 2}, kMfma16x16},
 };
 constexpr int kTableSize = sizeof(kTable) / sizeof(kTable[0]);
 
@@ -441,7 +442,16 @@ int select(const Problem& p)
     const int64_t t64 = ((p.M + 63) / 64) * ((p.N + 127) / 128) * p.batch;
     if (p.M <= 128 && t64 <= 256) return 37;
     const int64_t t256 = ((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
-    if (t256 < 128) return t64 <= 256 ? 37 : 30;
+    // 128 x 128 tiles: A staged two K-steps at a time (67) beyond one wave
+    // of them, the one-K-step ring (30) within it.  Median of five
+    // 200-launch blocks, same box, alternating, 67 against 30: bf16
+    // 2304^2 x 4096 (324 tiles) 46.9 against 60.2 us, 2560^2 x 2048 28.1
+    // against 33.3, 3072 x 2048^2 27.4 against 32.3, 2816^2 x 1024 17.2-17.7
+    // against 19.3-19.4; at 196-256 tiles 67 is 2-6 % slower (2048^3 19.9
+    // against 19.3-19.4, 1792^3 17.3 against 16.3, 1024 x 4096^2 35.9-36.1
+    // against 34.5-34.6).
+    const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    if (t256 < 128) return t64 <= 256 ? 37 : t128 > 256 ? 67 : 30;
     // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4
     // of a 256 x 256 tile's work at ~94 % of its rate, so a wave of them costs
     // ~0.8 of a wave of 256 x 256 tiles; it wins where 256 x 256 leaves a

@@ -751,10 +751,14 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma16x16_pair_kernel(
     // ---- epilogue: as in the kernel above (the last row of tiles was
     // written by the most recent MFMAs; each wavefront stages its block
     // through one B stage of its own)
-    static_assert(FN == 8, "the wait below lists the last row's tiles");
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]),
-                   "+a"(acc[FM - 1][4]), "+a"(acc[FM - 1][5]), "+a"(acc[FM - 1][6]), "+a"(acc[FM - 1][7]));
+    static_assert(FN == 8 || FN == 4, "the wait below lists the last row's tiles");
+    if constexpr (FN == 8)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]),
+                       "+a"(acc[FM - 1][4]), "+a"(acc[FM - 1][5]), "+a"(acc[FM - 1][6]), "+a"(acc[FM - 1][7]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[FM - 1][0]), "+a"(acc[FM - 1][1]), "+a"(acc[FM - 1][2]), "+a"(acc[FM - 1][3]));
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     constexpr int RP_MAX = B_BYTES / (WN * 2);
@@ -772,9 +776,14 @@ hipError_t launch_t(const Config& cfg, const LaunchArgs& a)
     const T* B = static_cast<const T*>(a.B);
     T* C = static_cast<T*>(a.C);
     if (cfg.threads != 256) return hipErrorInvalidValue;
-    if (cfg.sched == 2) {   // A staged two K-steps at a time: 256 x 256 or 192 x 256, one pass only
-        if (a.splits > 1 || cfg.bn != 256 || cfg.bk != 32) return hipErrorInvalidValue;
-        if (cfg.bm == 256)
+    if (cfg.sched == 2) {   // A staged two K-steps at a time: 256 x 256, 192 x 256 or 128 x 128, one pass only
+        if (a.splits > 1 || cfg.bk != 32) return hipErrorInvalidValue;
+        if (cfg.bm == 128 && cfg.bn == 128)
+            hipLaunchKernelGGL((gemm_mfma16x16_pair_kernel<T, 128, 128>), grid, block, 0, a.stream, A, B, C, a.M,
+                               a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
+        else if (cfg.bn != 256)
+            return hipErrorInvalidValue;
+        else if (cfg.bm == 256)
             hipLaunchKernelGGL((gemm_mfma16x16_pair_kernel<T, 256, 256>), grid, block, 0, a.stream, A, B, C, a.M,
                                a.N, a.K, cfg.group_m, cfg.xcd_remap, a.batch, a.clk);
         else if (cfg.bm == 192)

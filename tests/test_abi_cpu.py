@@ -570,6 +570,9 @@ def test_wide_few_rows_select_64x128_tiles_while_they_fit_one_wave():
     # 448 tiles of 64 x 128: back to 128 x 128; up to 32 rows of a wide B the
     # 64 x 128 tiles from K = 1024, the strip kernel below
     assert name(A, Bb, Cb, 128, 28672, 4096, 2) == "mfma16x16_128x128x32_adma"
+    # beyond one wave of 128 x 128 tiles: A staged two K-steps at a time
+    for M, N, K in [(2560, 2560, 2048), (2304, 2304, 4096), (2816, 2816, 1024)]:
+        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_128x128x32_apair", (M, N, K)
     assert name(A, Bb, Cb, 32, 14336, 4096, 2) == "mfma16x16_64x128x32_adma"
     assert name(A, Bb, Cb, 32, 14336, 512, 2).startswith("skinny")
 

@@ -472,8 +472,9 @@ def pair_kernels(tmp_path_factory):
                     if m2:
                         scratch[m.group(1)] = int(m2.group(1))
                         break
-        # 16-bit: {f16, bf16} x {256 x 256, 192 x 256}; 8-bit: {E4M3, E5M2} x the same
-        assert len(here) == 4, (fam, sorted(here))
+        # 16-bit: {f16, bf16} x {256 x 256, 192 x 256, 128 x 128}; 8-bit: {E4M3, E5M2} x
+        # {256 x 256, 192 x 256}
+        assert len(here) == (6 if fam == "mfma16x16" else 4), (fam, sorted(here))
         found.update(here)
     return found, scratch
 
