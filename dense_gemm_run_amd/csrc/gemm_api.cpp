@@ -452,6 +452,14 @@ int select(const Problem& p)
     // against 34.5-34.6).
     const int64_t t128 = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
     if (t256 < 128) return t64 <= 256 ? 37 : t128 > 256 ? 67 : 30;
+    // A partial single wave of 256 x 256 tiles whose 128 x 128 tiles fill at
+    // most the two workgroups a CU holds of them (t128 <= 512): 67 over the
+    // 192 x 256 tile (62), sustained, alternating: bf16 2048 x 4096^2 59.3
+    // against 61.0-61.2 us, 1024 x 8192 x 4096 58.9-59.2 against 62.6-62.8,
+    // 2048 x 4096 x 14336 200.4-201.0 against 202.1-202.6, fp16 4096 x 2048 x
+    // 8192 120.4-120.7 against 125.0-125.4 (3072^3, 576 tiles: 62.6 against
+    // 48.2-48.7, so not beyond 512).
+    if (t256 < 256 && t128 <= 512) return 67;
     // Tiles run in waves of one per CU (256 CUs).  A 192 x 256 tile holds 3/4
     // of a 256 x 256 tile's work at ~94 % of its rate, so a wave of them costs
     // ~0.8 of a wave of 256 x 256 tiles; it wins where 256 x 256 leaves a

@@ -573,6 +573,9 @@ def test_wide_few_rows_select_64x128_tiles_while_they_fit_one_wave():
     # beyond one wave of 128 x 128 tiles: A staged two K-steps at a time
     for M, N, K in [(2560, 2560, 2048), (2304, 2304, 4096), (2816, 2816, 1024)]:
         assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_128x128x32_apair", (M, N, K)
+    # a partial single wave of 256 x 256 tiles that at most 512 tiles of 128 x 128 cover
+    for M, N, K in [(2048, 4096, 4096), (1024, 8192, 4096), (4096, 2048, 8192)]:
+        assert name(A, Bb, Cb, M, N, K, 2) == "mfma16x16_128x128x32_apair", (M, N, K)
     assert name(A, Bb, Cb, 32, 14336, 4096, 2) == "mfma16x16_64x128x32_adma"
     assert name(A, Bb, Cb, 32, 14336, 512, 2).startswith("skinny")
 
